@@ -1,0 +1,213 @@
+"""Compressed-layer byte format: writer and reader (oracle).
+
+[P1 §3.1]: offline, a layer is cut into GEMM-aligned tiles, all tiles share
+one compact codebook, each tile is coded independently (R lane sub-streams)
+and a light index records each tile's start offset, so any tile can be
+decoded on its own.  The byte layout below is this project's reading (the
+pages give none); all integers are little-endian.
+
+header (128 bytes)
+   0 magic  b"DGT1"              4 u16 version = 1     6 u16 header bytes = 128
+   8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split)
+  12 u32 flags = 0              16 u32 N     20 u32 K
+  24 u32 tile_n  28 u32 tile_k  32 u32 lanes R  36 u32 prob_bits n
+  40 u32 alphabet (16 for int4, else 256)       44 u32 tiles
+  48 u64 table_off   56 u64 index_off   64 u64 ktab_off   72 u64 streams_off
+  80 u64 raw_off (0 when the format stores no raw bytes)   88 u64 total bytes
+  96 u32 max tile stream length in 4-byte units
+ 100 u32 kmax (payload-step cap, 16)    104..127 zero
+table   u16 f[alphabet]                                   (16-byte aligned)
+index   u32 off[tiles + 1], 4-byte units from streams_off, off[0] = 0 (aligned)
+ktab    u8 k[tiles]: payload steps of each tile (see ``oracle.rans``) (aligned)
+streams tile t at streams_off + 4*off[t]: R u32 states (lane order) then the
+        u16 words in decoder order, then one zero u16 if the count is odd
+raw     (bf16 split only, 16-byte aligned) T low bytes per tile, tiles in id
+        order, each tile in the lane-major raw order of ``oracle.order``
+total = end of raw (bf16 split) or end of streams.
+
+Symbols: int8 code & 0xFF; int4 code; e4m3 byte; bf16 bits >> 8 (sign and
+top seven exponent bits) with the low byte (exponent LSB + mantissa) raw.
+"""
+
+import struct
+
+import numpy as np
+
+from . import entropy, freq, order, rans
+
+MAGIC = b"DGT1"
+VERSION = 1
+HEADER_BYTES = 128
+FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16 = 1, 2, 3, 4
+_HDR = struct.Struct("<4sHHIIIIIIIIII QQQQQQ II 24x")
+assert _HDR.size == HEADER_BYTES
+
+
+def _align(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def alphabet_of(fmt: int) -> int:
+    if fmt == FMT_INT4:
+        return 16
+    if fmt in (FMT_INT8, FMT_FP8, FMT_BF16):
+        return 256
+    raise ValueError("unknown format")
+
+
+def symbolise(fmt: int, w):
+    """Return (symbols uint8 [N,K], raw low bytes uint8 [N,K] or None)."""
+    w = np.asarray(w)
+    if fmt == FMT_INT8:
+        return w.astype(np.int8).view(np.uint8), None
+    if fmt == FMT_INT4:
+        if w.min() < 0 or w.max() > 15:
+            raise ValueError("int4 codes must be in [0, 15]")
+        return w.astype(np.uint8), None
+    if fmt == FMT_FP8:
+        return w.astype(np.uint8), None
+    if fmt == FMT_BF16:
+        b = w.astype(np.uint16)
+        return (b >> 8).astype(np.uint8), (b & 0xFF).astype(np.uint8)
+    raise ValueError("unknown format")
+
+
+def compress_layer(fmt: int, w, tile_n: int, tile_k: int, lanes: int,
+                   prob_bits: int = 12) -> bytes:
+    w = np.asarray(w)
+    n, k = w.shape
+    order.check_geometry(n, k, tile_n, tile_k, lanes)
+    sym, raw = symbolise(fmt, w)
+    alpha = alphabet_of(fmt)
+    counts = entropy.histogram(sym, alpha)
+    f = freq.quantize_freqs(counts, prob_bits)
+    tsym = order.gather_tiles(sym, tile_n, tile_k, lanes)
+    states, words, ks = rans.encode_tiles(tsym, f, lanes, prob_bits, rans.KMAX)
+    tiles = tsym.shape[0]
+    T = tile_n * tile_k
+
+    chunks, off = [], [0]
+    for t in range(tiles):
+        wd = words[t]
+        if wd.size % 2:
+            wd = np.concatenate([wd, np.zeros(1, np.uint16)])
+        c = states[t].astype("<u4").tobytes() + wd.astype("<u2").tobytes()
+        chunks.append(c)
+        off.append(off[-1] + len(c) // 4)
+    table_off = HEADER_BYTES
+    index_off = _align(table_off + 2 * alpha, 16)
+    ktab_off = _align(index_off + 4 * (tiles + 1), 16)
+    streams_off = _align(ktab_off + tiles, 16)
+    streams_end = streams_off + 4 * off[-1]
+    if raw is not None:
+        raw_off = _align(streams_end, 16)
+        total = raw_off + tiles * T
+    else:
+        raw_off, total = 0, streams_end
+    max_len = max(off[t + 1] - off[t] for t in range(tiles))
+    hdr = _HDR.pack(MAGIC, VERSION, HEADER_BYTES, fmt, 0, n, k, tile_n, tile_k,
+                    lanes, prob_bits, alpha, tiles, table_off, index_off,
+                    ktab_off, streams_off, raw_off, total, max_len, rans.KMAX)
+    buf = bytearray(total)
+    buf[0:HEADER_BYTES] = hdr
+    buf[table_off:table_off + 2 * alpha] = f.astype("<u2").tobytes()
+    buf[index_off:index_off + 4 * (tiles + 1)] = np.asarray(off, "<u4").tobytes()
+    buf[ktab_off:ktab_off + tiles] = ks.astype(np.uint8).tobytes()
+    buf[streams_off:streams_end] = b"".join(chunks)
+    if raw is not None:
+        rtiles = order.gather_tiles(raw, tile_n, tile_k, lanes, raw=True)
+        buf[raw_off:total] = rtiles.astype(np.uint8).tobytes()
+    return bytes(buf)
+
+
+def parse(blob) -> dict:
+    """Header fields plus table, index; validates what a reader must trust."""
+    b = bytes(blob) if not isinstance(blob, (bytes, bytearray)) else blob
+    if len(b) < HEADER_BYTES:
+        raise ValueError("blob shorter than header")
+    v = _HDR.unpack_from(b, 0)
+    keys = ["magic", "version", "header_bytes", "fmt", "flags", "n", "k",
+            "tile_n", "tile_k", "lanes", "prob_bits", "alphabet", "tiles",
+            "table_off", "index_off", "ktab_off", "streams_off", "raw_off", "total",
+            "max_tile_words4", "kmax"]
+    h = dict(zip(keys, v))
+    if h["magic"] != MAGIC or h["version"] != VERSION or h["header_bytes"] != HEADER_BYTES:
+        raise ValueError("bad magic / version")
+    if h["total"] != len(b):
+        raise ValueError("size mismatch")
+    order.check_geometry(h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"])
+    if h["alphabet"] != alphabet_of(h["fmt"]):
+        raise ValueError("bad alphabet")
+    nt = (h["n"] // h["tile_n"]) * (h["k"] // h["tile_k"])
+    if h["tiles"] != nt:
+        raise ValueError("bad tile count")
+    a, t = h["alphabet"], h["tiles"]
+    h["freq"] = np.frombuffer(b, "<u2", a, h["table_off"]).astype(np.int64)
+    if h["freq"].sum() != (1 << h["prob_bits"]):
+        raise ValueError("frequencies do not sum to 2**prob_bits")
+    h["index"] = np.frombuffer(b, "<u4", t + 1, h["index_off"]).astype(np.int64)
+    if h["index"][0] != 0 or (np.diff(h["index"]) < h["lanes"]).any():
+        raise ValueError("index not monotone")
+    end = h["streams_off"] + 4 * int(h["index"][-1])
+    if end > len(b) or (h["raw_off"] and h["raw_off"] < end):
+        raise ValueError("streams overrun")
+    if int(np.diff(h["index"]).max()) != h["max_tile_words4"]:
+        raise ValueError("bad max tile length")
+    h["ks"] = np.frombuffer(b, np.uint8, t, h["ktab_off"]).astype(np.int64)
+    S = h["tile_n"] * h["tile_k"] // h["lanes"]
+    if h["kmax"] > 255 or (h["ks"] > min(h["kmax"], S)).any():
+        raise ValueError("bad payload step count")
+    return h
+
+
+def tile_stream(blob, h: dict, t: int):
+    """(states [R] uint32, words uint16 incl. possible pad) of tile t."""
+    start = h["streams_off"] + 4 * int(h["index"][t])
+    end = h["streams_off"] + 4 * int(h["index"][t + 1])
+    R = h["lanes"]
+    states = np.frombuffer(blob, "<u4", R, start).astype(np.uint32)
+    words = np.frombuffer(blob, "<u2", (end - start - 4 * R) // 2, start + 4 * R)
+    return states, words
+
+
+def decode_symbols(blob, tiles=None) -> np.ndarray:
+    """Decoded symbols [len(tiles), T] in j order (all tiles by default)."""
+    h = parse(blob)
+    ids = range(h["tiles"]) if tiles is None else list(tiles)
+    R = h["lanes"]
+    S = h["tile_n"] * h["tile_k"] // R
+    st, ws = [], []
+    for t in ids:
+        s, w = tile_stream(blob, h, t)
+        st.append(s)
+        ws.append(w)
+    # a stream holds R states and 2*(len4 - R) word slots; the coder uses
+    # all of them, or all but a final zero pad word
+    ks = h["ks"][np.asarray(list(ids), dtype=np.int64)]
+    syms, used = rans.decode_tiles(np.asarray(st), ws, h["freq"], R, S, ks,
+                                   h["prob_bits"], check=False, return_consumed=True)
+    for i, w in enumerate(ws):
+        if not (used[i] == len(w) or (used[i] == len(w) - 1 and w[-1] == 0)):
+            raise rans.IntegrityError("stream length mismatch")
+    return syms
+
+
+def decompress_layer(blob) -> np.ndarray:
+    """Rebuild the original codes: int8 -> int8, int4/fp8 -> uint8, bf16 -> uint16."""
+    h = parse(blob)
+    syms = decode_symbols(blob)
+    n, k, tn, tk, R = h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"]
+    sym = order.scatter_tiles(syms.astype(np.uint8), n, k, tn, tk, R)
+    fmt = h["fmt"]
+    if fmt == FMT_INT8:
+        return sym.view(np.int8)
+    if fmt in (FMT_INT4, FMT_FP8):
+        return sym
+    T = tn * tk
+    raw = np.frombuffer(blob, np.uint8, h["tiles"] * T, h["raw_off"]).reshape(h["tiles"], T)
+    lo = order.scatter_tiles(raw, n, k, tn, tk, R, raw=True)
+    return (sym.astype(np.uint16) << 8) | lo.astype(np.uint16)
+
+
+def bits_per_weight(blob, n: int, k: int) -> float:
+    return 8.0 * len(blob) / (n * k)

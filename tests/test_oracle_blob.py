@@ -1,0 +1,103 @@
+"""Pins for oracle.blob: lossless round trip (the plain definition of the
+decoded weights), header layout, size bounds and corruption detection."""
+
+import struct
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import blob, entropy, rans
+
+CASES = [
+    (blob.FMT_INT8, 128, 64, 128, 32, 32),
+    (blob.FMT_INT8, 64, 32, 32, 16, 32),
+    (blob.FMT_INT4, 256, 256, 128, 64, 64),
+    (blob.FMT_FP8, 256, 128, 256, 64, 64),
+    (blob.FMT_BF16, 256, 128, 128, 64, 64),
+    (blob.FMT_BF16, 32, 16, 16, 8, 16),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R", CASES)
+def test_round_trip_is_lossless(fmt, n, k, tn, tk, R):
+    d = workloads.random_small(fmt, n, k, seed=n + k + fmt)
+    b = blob.compress_layer(fmt, d["codes"], tn, tk, R)
+    out = blob.decompress_layer(b)
+    assert out.dtype == np.asarray(d["codes"]).dtype
+    assert np.array_equal(out, d["codes"])
+
+
+def test_header_layout_and_alignment():
+    d = workloads.random_small(blob.FMT_BF16, 256, 128, seed=3)
+    b = blob.compress_layer(blob.FMT_BF16, d["codes"], 128, 64, 64)
+    assert b[:4] == b"DGT1"
+    ver, hb = struct.unpack_from("<HH", b, 4)
+    assert (ver, hb) == (1, 128)
+    fields = struct.unpack_from("<10I", b, 8)
+    assert fields == (4, 0, 256, 128, 128, 64, 64, 12, 256, 4)
+    h = blob.parse(b)
+    for key in ("table_off", "index_off", "ktab_off", "streams_off", "raw_off"):
+        assert h[key] % 16 == 0
+    assert h["table_off"] == 128
+    assert h["index_off"] == 128 + 512
+    assert h["ktab_off"] == 128 + 512 + 16 * ((4 * 5 + 15) // 16)
+    assert h["total"] == len(b) == h["raw_off"] + 4 * 128 * 64
+    assert h["kmax"] == rans.KMAX
+    # every tile's low bytes sit in the raw section, lane-major
+    raw0 = np.frombuffer(b, np.uint8, 8, h["raw_off"])
+    codes = np.asarray(d["codes"])
+    assert list(raw0) == [int(codes[0, e]) & 0xFF for e in range(8)]
+
+
+def test_bits_per_weight_bounds_on_small_configs():
+    for name in ("int8_1024", "int4_4096"):
+        d = workloads.make(name)
+        wl = d["workload"]
+        b = blob.compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+        sym, _ = blob.symbolise(wl.fmt, d["codes"])
+        h = entropy.empirical_entropy(sym, blob.alphabet_of(wl.fmt))
+        bpw = blob.bits_per_weight(b, wl.n, wl.k)
+        assert bpw >= h               # Gibbs: a static code cannot beat H_emp
+        assert bpw <= h + 0.15        # per-lane state flush dominates the excess
+
+
+def test_int8_config_entropy_is_about_5_bits():
+    d = workloads.make("int8_1024")
+    sym, _ = blob.symbolise(blob.FMT_INT8, d["codes"])
+    h = entropy.empirical_entropy(sym, 256)
+    assert 4.95 < h < 5.15  # the workload says "H ~ 5 bits"; 0.5*log2(2 pi e 64) = 5.047
+
+
+def test_corruption_is_detected():
+    d = workloads.random_small(blob.FMT_INT8, 128, 64, seed=5)
+    b = bytearray(blob.compress_layer(blob.FMT_INT8, d["codes"], 128, 32, 32))
+    h = blob.parse(bytes(b))
+    # flip a byte inside the first tile's word stream
+    pos = h["streams_off"] + 4 * 32 + 10
+    b2 = bytearray(b)
+    b2[pos] ^= 0x5A
+    with pytest.raises((rans.IntegrityError, ValueError)):
+        out = blob.decompress_layer(bytes(b2))
+        assert not np.array_equal(out, d["codes"])
+        raise rans.IntegrityError("decoded differently")
+    # truncation, bad magic, swapped index entries
+    with pytest.raises(ValueError):
+        blob.parse(bytes(b[:-1]))
+    b3 = bytearray(b)
+    b3[0] = ord("X")
+    with pytest.raises(ValueError):
+        blob.parse(bytes(b3))
+    b4 = bytearray(b)
+    io = h["index_off"]
+    b4[io + 4:io + 8], b4[io + 8:io + 12] = b[io + 8:io + 12], b[io + 4:io + 8]
+    with pytest.raises((ValueError, rans.IntegrityError)):
+        blob.decompress_layer(bytes(b4))
+
+
+def test_decode_subset_of_tiles():
+    d = workloads.random_small(blob.FMT_FP8, 512, 128, seed=8)
+    b = blob.compress_layer(blob.FMT_FP8, d["codes"], 256, 64, 64)
+    full = blob.decode_symbols(b)
+    part = blob.decode_symbols(b, [3, 1])
+    assert np.array_equal(part, full[[3, 1]])

@@ -1,0 +1,138 @@
+"""Pins for oracle.numerics (against torch's CPU casts, exhaustively where the
+input space allows) and oracle.gemm (explicit sums, exact rational arithmetic)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm, numerics
+
+
+def test_bf16_rne_matches_torch_over_all_bf16_neighbourhoods():
+    hi = np.arange(65536, dtype=np.uint32)
+    for lo in (0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000):
+        u = (hi << 16) | lo
+        f = u.view(np.float32)
+        ours = numerics.f32_to_bf16_bits(f)
+        ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        finite = np.isfinite(f)
+        assert np.array_equal(ours[finite], ref[finite])
+        nan = np.isnan(f)
+        assert np.isnan(numerics.bf16_bits_to_f64(ours[nan])).all()
+
+
+def test_bf16_to_f64_is_exact():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    ours = numerics.bf16_bits_to_f64(bits)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]) and np.isnan(ours[~ok]).all()
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    ours = numerics.e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(0)
+    vals = numerics.e4m3_to_f64(np.arange(0, 0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([vals, mids, -mids, mids * (1 + 1e-7), mids * (1 - 1e-7),
+                        rng.uniform(-464, 464, 20000), rng.normal(0, 1, 20000),
+                        np.array([0.0, -0.0, 464.0, -464.0, 1e-12])])
+    x32 = x.astype(np.float32)
+    ours = numerics.f64_to_e4m3(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_encode_saturates_and_nan():
+    out = numerics.f64_to_e4m3(np.array([465.0, 1e9, -1e9, np.inf, -np.inf, np.nan]))
+    assert list(out) == [0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x7F]
+
+
+def test_int4_dequant_matches_torch():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, (64, 256)).astype(np.uint8)
+    sc = torch.from_numpy(rng.normal(0.01, 0.002, (64, 2)).astype(np.float32)).to(torch.bfloat16)
+    sbits = sc.view(torch.int16).numpy().view(np.uint16)
+    ours = numerics.int4_dequant_bf16_bits(q, sbits)
+    ref = ((torch.from_numpy(q.astype(np.float32)) - 8.0)
+           * sc.float().repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    assert np.array_equal(ours, ref.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_fp8_activation_quant_properties():
+    rng = np.random.default_rng(2)
+    x = torch.from_numpy(rng.normal(0, 1, (8, 512)).astype(np.float32)).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    xq, sx = numerics.fp8_quantize_activations(bits)
+    xv = x.double().numpy()
+    amax = np.abs(xv).max()
+    assert sx == pytest.approx(amax / 448, rel=2 ** -23)
+    # the largest element maps to +-448
+    i = np.unravel_index(np.abs(xv).argmax(), xv.shape)
+    assert numerics.e4m3_to_f64(xq[i]) == pytest.approx(448.0 * np.sign(xv[i]))
+    # dequantised values are within half an e4m3 ulp (relative 2^-4) or the subnormal step
+    back = numerics.e4m3_to_f64(xq) * sx
+    err = np.abs(back - xv)
+    assert (err <= np.maximum(np.abs(xv) * 2.0 ** -4, sx * 2.0 ** -10) * 1.0001).all()
+    z, s0 = numerics.fp8_quantize_activations(np.zeros((2, 4), np.uint16))
+    assert (z == 0).all() and s0 == 1.0
+
+
+# ------------------------------------------------------------------ gemm
+def test_gemm_matches_explicit_sums():
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(5, 37))
+    w = rng.normal(size=(11, 37))
+    assert np.allclose(gemm.gemm_fp64(x, w), gemm.gemm_loop(x, w), rtol=1e-13, atol=1e-13)
+
+
+def test_gemm_exact_against_fractions():
+    rng = np.random.default_rng(4)
+    xb = numerics.f32_to_bf16_bits(rng.normal(size=(3, 8)).astype(np.float32))
+    wb = numerics.f32_to_bf16_bits(rng.normal(size=(4, 8)).astype(np.float32))
+    x = numerics.bf16_bits_to_f64(xb)
+    w = numerics.bf16_bits_to_f64(wb)
+    y = gemm.gemm_fp64(x, w)
+    for i in range(3):
+        for j in range(4):
+            exact = sum(Fraction(float(x[i, t])) * Fraction(float(w[j, t])) for t in range(8))
+            assert abs(Fraction(float(y[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+def test_gemm_transpose_orientation():
+    # Y = X W^T: W rows are output features
+    x = np.array([[1.0, 2.0, 3.0]])
+    w = np.array([[1.0, 0.0, 0.0], [0.0, 0.0, 1.0]])
+    assert gemm.gemm_fp64(x, w).tolist() == [[1.0, 3.0]]
+
+
+def test_weight_values_per_format():
+    codes8 = np.array([[-127, -1, 0, 5]], dtype=np.int8)
+    assert gemm.weight_values(gemm.FMT_INT8, codes8).tolist() == [[-127, -1, 0, 5]]
+    b = np.array([[0x3F80, 0xBF80, 0x4040]], dtype=np.uint16)
+    assert gemm.weight_values(gemm.FMT_BF16, b).tolist() == [[1.0, -1.0, 3.0]]
+    f8 = np.array([[0x38, 0xB8, 0x7E]], dtype=np.uint8)
+    assert gemm.weight_values(gemm.FMT_FP8, f8).tolist() == [[1.0, -1.0, 448.0]]
+    q = np.full((1, 128), 10, dtype=np.uint8)
+    s = np.array([[0x3F00]], dtype=np.uint16)  # 0.5
+    assert (gemm.weight_values(gemm.FMT_INT4, q, s) == 1.0).all()
+
+
+def test_reference_output_fp8_exact_case():
+    # X already on the e4m3 grid with amax 448 -> sx = 1, and W scale 0.5
+    x = np.array([[448.0, -1.0, 0.5, 0.0]], dtype=np.float32)
+    xb = numerics.f32_to_bf16_bits(x)
+    wq = numerics.f64_to_e4m3(np.array([[1.0, 2.0, 4.0, 8.0], [-1.0, 0.0, 0.0, 448.0]]))
+    y = gemm.reference_output(gemm.FMT_FP8, wq, xb, w_scale=0.5)
+    assert y.tolist() == [[0.5 * (448 - 2 + 2), 0.5 * (-448)]]

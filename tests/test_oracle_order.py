@@ -1,0 +1,71 @@
+"""Pins for oracle.order: bijections and hand-checked positions."""
+
+import numpy as np
+import pytest
+
+from oracle import order
+
+GEOMS = [(16, 8, 16), (16, 32, 64), (128, 32, 32), (128, 64, 64), (256, 64, 64),
+         (32, 16, 32), (48, 24, 16)]
+
+
+@pytest.mark.parametrize("tn,tk,R", GEOMS)
+def test_positions_are_bijections(tn, tk, R):
+    for fn in (order.tile_positions, order.raw_positions):
+        r, c = fn(tn, tk, R)
+        assert r.min() == 0 and r.max() == tn - 1 and c.min() == 0 and c.max() == tk - 1
+        lin = r * tk + c
+        assert np.array_equal(np.sort(lin), np.arange(tn * tk))
+
+
+def test_hand_checked_positions_r64():
+    r, c = order.tile_positions(32, 64, 64)
+    # j = step*64 + lane; lane p -> row p%16, column group p//16 (8 columns each)
+    assert (r[0], c[0]) == (0, 0)
+    assert (r[1], c[1]) == (1, 0)
+    assert (r[16], c[16]) == (0, 8)
+    assert (r[63], c[63]) == (15, 24 + 0)
+    assert (r[64], c[64]) == (0, 1)          # step 1 = element 1 of lane 0
+    assert (r[7 * 64 + 63], c[7 * 64 + 63]) == (15, 31)
+    assert (r[8 * 64], c[8 * 64]) == (16, 0)  # fragment 1 = second row band
+    assert (r[16 * 64], c[16 * 64]) == (0, 32)  # fragment 2 = next column block
+
+
+def test_hand_checked_positions_r32():
+    r, c = order.tile_positions(128, 32, 32)
+    assert (r[31], c[31]) == (15, 8)   # lane 31: row 15, column group 1
+    assert (r[32], c[32]) == (0, 1)    # step 1
+    assert (r[8 * 32], c[8 * 32]) == (16, 0)
+    assert (r[8 * 8 * 32], c[8 * 8 * 32]) == (0, 16)  # after 8 row bands: column block 1
+
+
+@pytest.mark.parametrize("tn,tk,R", GEOMS)
+def test_raw_order_is_lane_major_symbol_order(tn, tk, R):
+    """raw index q = g*8R + p*8 + e holds the element of symbol j = (8g+e)*R + p."""
+    rs, cs = order.tile_positions(tn, tk, R)
+    rr, cr = order.raw_positions(tn, tk, R)
+    T = tn * tk
+    q = np.arange(T)
+    g, p, e = q // (8 * R), (q % (8 * R)) // 8, q % 8
+    j = (8 * g + e) * R + p
+    assert np.array_equal(rr, rs[j]) and np.array_equal(cr, cs[j])
+
+
+def test_gather_scatter_inverse():
+    rng = np.random.default_rng(0)
+    w = rng.integers(0, 256, (256, 192)).astype(np.uint8)
+    for R, tn, tk in [(64, 128, 64), (32, 128, 32), (16, 16, 8)]:
+        for raw in (False, True):
+            t = order.gather_tiles(w, tn, tk, R, raw=raw)
+            assert t.shape == ((256 // tn) * (192 // tk), tn * tk)
+            assert np.array_equal(order.scatter_tiles(t, 256, 192, tn, tk, R, raw=raw), w)
+    # tile id t = bn*(K/Tk) + bk, and the first symbol of a tile is its corner
+    t = order.gather_tiles(w, 128, 64, 64)
+    assert t[1, 0] == w[0, 64] and t[3, 0] == w[128, 0]
+
+
+def test_geometry_errors():
+    for args in [(100, 64, 128, 64, 64), (128, 64, 128, 64, 48), (128, 64, 120, 64, 64),
+                 (128, 48, 128, 48, 64)]:
+        with pytest.raises(ValueError):
+            order.check_geometry(*args)
