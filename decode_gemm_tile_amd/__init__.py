@@ -1,0 +1,217 @@
+"""Python binding of libdgt (ctypes): argument marshalling only.
+
+Every step of the decode and the GEMM runs in the HIP library; PyTorch only
+provides device memory and the current HIP stream.  Function names follow the
+C ABI in include/dgt.h one to one.  There is no CPU fallback: when libdgt.so
+is missing or no GPU is present the device entry points raise.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdgt.so")
+
+DGT_FMT_INT8, DGT_FMT_INT4, DGT_FMT_FP8_E4M3, DGT_FMT_BF16_SPLIT = 1, 2, 3, 4
+STATUS = {0: "DGT_OK", -1: "DGT_E_ARG", -2: "DGT_E_SHAPE", -3: "DGT_E_ALPHABET",
+          -4: "DGT_E_BUFSIZE", -5: "DGT_E_FORMAT", -6: "DGT_E_CORRUPT", -7: "DGT_E_HIP",
+          -8: "DGT_E_UNSUPPORTED"}
+EXPORTS = ["dgt_version", "dgt_status_string", "dgt_compress_bound", "dgt_compress_layer",
+           "dgt_layer_info", "dgt_decode_tiles", "dgt_gemm_workspace",
+           "dgt_fused_decode_gemm", "dgt_dense_workspace", "dgt_dense_gemm"]
+
+
+class DgtError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, STATUS.get(code, "?"), code))
+        self.code = code
+
+
+class dgt_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("fmt", "n", "k", "tile_n", "tile_k", "lanes", "prob_bits", "flags")]
+
+
+class dgt_info(ctypes.Structure):
+    _fields_ = ([(n, ctypes.c_uint32) for n in
+                 ("fmt", "n", "k", "tile_n", "tile_k", "lanes", "prob_bits", "alphabet",
+                  "tiles", "max_tile_words4", "kmax", "flags")] +
+                [(n, ctypes.c_uint64) for n in
+                 ("table_off", "index_off", "ktab_off", "streams_off", "raw_off",
+                  "total_bytes", "stream_bytes")] +
+                [("bits_per_weight", ctypes.c_double)])
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load the in-tree libdgt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libdgt.so not built: run python -m decode_gemm_tile_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u32, sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_size_t
+        L.dgt_version.restype = ctypes.c_int
+        L.dgt_status_string.restype = ctypes.c_char_p
+        L.dgt_status_string.argtypes = [ctypes.c_int]
+        L.dgt_compress_bound.restype = sz
+        L.dgt_compress_bound.argtypes = [ctypes.POINTER(dgt_params)]
+        L.dgt_compress_layer.restype = ctypes.c_int
+        L.dgt_compress_layer.argtypes = [ctypes.POINTER(dgt_params), vp, vp, sz,
+                                         ctypes.POINTER(sz)]
+        L.dgt_layer_info.restype = ctypes.c_int
+        L.dgt_layer_info.argtypes = [vp, sz, ctypes.POINTER(dgt_info)]
+        L.dgt_decode_tiles.restype = ctypes.c_int
+        L.dgt_decode_tiles.argtypes = [vp, ctypes.POINTER(dgt_info), vp, u32, vp, vp, vp]
+        L.dgt_gemm_workspace.restype = sz
+        L.dgt_gemm_workspace.argtypes = [ctypes.POINTER(dgt_info), u32]
+        L.dgt_fused_decode_gemm.restype = ctypes.c_int
+        L.dgt_fused_decode_gemm.argtypes = [vp, ctypes.POINTER(dgt_info), vp, u32, vp,
+                                            ctypes.c_float, vp, vp, sz, vp, vp]
+        L.dgt_dense_workspace.restype = sz
+        L.dgt_dense_workspace.argtypes = [u32, u32, u32, u32, u32]
+        L.dgt_dense_gemm.restype = ctypes.c_int
+        L.dgt_dense_gemm.argtypes = [u32, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp,
+                                     vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise DgtError(code, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- host side
+def dgt_version() -> int:
+    return lib().dgt_version()
+
+
+def dgt_status_string(code: int) -> str:
+    return lib().dgt_status_string(code).decode()
+
+
+def dgt_compress_bound(fmt, n, k, tile_n, tile_k, lanes, prob_bits=12) -> int:
+    p = dgt_params(fmt, n, k, tile_n, tile_k, lanes, prob_bits, 0)
+    return lib().dgt_compress_bound(ctypes.byref(p))
+
+
+def dgt_compress_layer(fmt, w, tile_n, tile_k, lanes, prob_bits=12) -> bytes:
+    """Offline encoder.  w: [N, K] numpy array (int8 / uint8 codes, or uint16
+    bf16 bit patterns for the bf16 split)."""
+    w = np.ascontiguousarray(w)
+    n, k = w.shape
+    p = dgt_params(fmt, n, k, tile_n, tile_k, lanes, prob_bits, 0)
+    cap = lib().dgt_compress_bound(ctypes.byref(p))
+    if cap == 0:
+        _check(-2, "dgt_compress_bound")
+    out = np.empty(cap, dtype=np.uint8)
+    size = ctypes.c_size_t(0)
+    _check(lib().dgt_compress_layer(ctypes.byref(p), w.ctypes.data_as(ctypes.c_void_p),
+                                    out.ctypes.data_as(ctypes.c_void_p), cap,
+                                    ctypes.byref(size)), "dgt_compress_layer")
+    return out[: size.value].tobytes()
+
+
+def dgt_layer_info(blob: bytes) -> dgt_info:
+    info = dgt_info()
+    buf = np.frombuffer(blob, dtype=np.uint8)
+    _check(lib().dgt_layer_info(buf.ctypes.data_as(ctypes.c_void_p), len(blob),
+                                ctypes.byref(info)), "dgt_layer_info")
+    return info
+
+
+# --------------------------------------------------------------- device side
+class DeviceLayer:
+    """A blob resident in HBM plus its parsed header."""
+
+    def __init__(self, blob: bytes, device="cuda"):
+        import torch
+        self.info = dgt_layer_info(blob)
+        host = torch.frombuffer(bytearray(blob), dtype=torch.uint8)
+        self.blob = host.to(device)
+        if self.blob.data_ptr() % 16:
+            raise RuntimeError("device blob is not 16-byte aligned")
+        self.nbytes = len(blob)
+
+
+def dgt_decode_tiles(layer: DeviceLayer, tile_ids=None, out=None, status=None, stream=None):
+    """Decode tiles into W layout [N, K] (uint8 codes, or int16 bf16 bits)."""
+    import torch
+    inf = layer.info
+    dev = layer.blob.device
+    if out is None:
+        dt = torch.int16 if inf.fmt == DGT_FMT_BF16_SPLIT else torch.uint8
+        out = torch.zeros((inf.n, inf.k), dtype=dt, device=dev)
+    ids = None
+    n_ids = 0
+    if tile_ids is not None:
+        ids = torch.as_tensor(tile_ids, dtype=torch.int32).to(dev)
+        n_ids = ids.numel()
+    _check(lib().dgt_decode_tiles(_ptr(layer.blob), ctypes.byref(inf), _ptr(ids), n_ids,
+                                  _ptr(out), _ptr(status), _stream(stream)),
+           "dgt_decode_tiles")
+    return out
+
+
+def dgt_gemm_workspace(layer: DeviceLayer, m: int) -> int:
+    return lib().dgt_gemm_workspace(ctypes.byref(layer.info), m)
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def dgt_fused_decode_gemm(layer: DeviceLayer, x, scales=None, w_scale=1.0, y=None, ws=None,
+                          status=None, stream=None):
+    """Y[m, n] = sum_k X[m, k] W[n, k] with W decoded on chip; x: bf16 [M, K]."""
+    import torch
+    inf = layer.info
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, inf.n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(dgt_gemm_workspace(layer, m), x.device)
+    _check(lib().dgt_fused_decode_gemm(_ptr(layer.blob), ctypes.byref(inf), _ptr(x), m,
+                                       _ptr(scales), float(w_scale), _ptr(y), _ptr(ws),
+                                       ws.numel(), _ptr(status), _stream(stream)),
+           "dgt_fused_decode_gemm")
+    return y
+
+
+def dgt_dense_workspace(fmt, n, k, tile_n, m) -> int:
+    return lib().dgt_dense_workspace(fmt, n, k, tile_n, m)
+
+
+def dgt_dense_gemm(fmt, w, x, tile_n=128, scales=None, w_scale=1.0, y=None, ws=None,
+                   stream=None):
+    """Uncompressed baseline; w: device [N, K] (uint8 codes or bf16 bits)."""
+    import torch
+    n, k = w.shape
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(dgt_dense_workspace(fmt, n, k, tile_n, m), x.device)
+    _check(lib().dgt_dense_gemm(fmt, n, k, tile_n, _ptr(w), _ptr(x), m, _ptr(scales),
+                                float(w_scale), _ptr(y), _ptr(ws), ws.numel(),
+                                _stream(stream)), "dgt_dense_gemm")
+    return y

@@ -1,0 +1,391 @@
+// C-ABI entry points of libdgt's device side, the fp8 activation-quantisation
+// kernels and the static launch planner.
+//
+// Planner (the static tile schedule of "arXiv'26 | 无损压缩逼近 Shannon 极限" §3.1,
+// fixed at launch, no run-time bookkeeping): Y is cut into strips of tile_n
+// columns; the k-tiles of a strip are dealt to waves in order (ILP chains per
+// wave), consecutive waves share a workgroup, and a strip spans `gps`
+// workgroups whose partials meet in the workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "../../include/dgt.h"
+#include "dgt_format.h"
+#include "dgt_launch.h"
+
+namespace dgt {
+namespace dev {
+
+// ---------------------------------------------------- fp8 activation quant
+// Per-tensor e4m3 quantisation of X (bf16): amax, inv = fl32(448 / amax),
+// sx = fl32(amax / 448), xq = e4m3_rne_satfinite(fl32(x * inv)).
+struct QuantArgs {
+  const uint16_t* x;
+  uint8_t* xq;
+  uint32_t* amax_bits;   // workspace: running max of |x| as fp32 bits
+  uint32_t* done;        // workspace: finished-block counter
+  float* sx;             // workspace: activation scale
+  uint32_t count;
+};
+
+__global__ __launch_bounds__(256) void k_amax(QuantArgs q) {
+  uint32_t mx = 0;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < q.count; i += gridDim.x * blockDim.x)
+    mx = max(mx, ((uint32_t)q.x[i] << 16) & 0x7FFFFFFFu);
+  for (int d = 32; d > 0; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, d, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(q.amax_bits, mx);
+}
+
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  // round to nearest even, saturate finite values to 448, NaN -> 0x7F
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7FFFFFFFu;
+  if (au > 0x7F800000u) return 0x7Fu;
+  const float a = __uint_as_float(au);
+  if (a >= 448.f) return sign | 0x7Eu;
+  uint32_t mag;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
+    const float q = a * 512.f;                   // exact scaling
+    mag = (uint32_t)__builtin_rintf(q);          // ties to even, 0..8
+  } else {
+    const uint32_t exp = (au >> 23) - 127 + 7;   // 1..15
+    const uint32_t man = au & 0x7FFFFFu;
+    const uint32_t keep = man >> 20, rest = man & 0xFFFFFu;
+    uint32_t m3 = keep;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) m3 += 1;
+    mag = (exp << 3) + m3;                       // carry propagates into the exponent
+  }
+  return sign | mag;
+}
+
+__global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
+  const float amax = __uint_as_float(*q.amax_bits);
+  float inv = 1.f, sx = 1.f;
+  const bool zero = !(amax > 0.f) || amax > 3.4e38f;
+  if (!zero) {
+    inv = (float)(448.0 / (double)amax);
+    sx = (float)((double)amax / 448.0);
+  }
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < q.count; i += gridDim.x * blockDim.x) {
+    const float v = __uint_as_float((uint32_t)q.x[i] << 16);
+    q.xq[i] = zero ? 0 : (uint8_t)f32_to_e4m3(v * inv);
+  }
+  __shared__ bool last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(q.done, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (last && threadIdx.x == 0) {
+    *q.sx = sx;
+    *q.amax_bits = 0u;  // ready for the next call
+    *q.done = 0u;
+  }
+}
+
+
+}  // namespace dev
+}  // namespace dgt
+
+// =================================================================== host side
+namespace {
+
+using namespace dgt::dev;
+
+bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
+  if (!d_blob || !in) return false;
+  const uint8_t* b = static_cast<const uint8_t*>(d_blob);
+  L->table = reinterpret_cast<const uint16_t*>(b + in->table_off);
+  L->index = reinterpret_cast<const uint32_t*>(b + in->index_off);
+  L->ktab = b + in->ktab_off;
+  L->streams = reinterpret_cast<const uint32_t*>(b + in->streams_off);
+  L->raw = in->raw_off ? b + in->raw_off : nullptr;
+  L->n = in->n;
+  L->k = in->k;
+  L->tile_n = in->tile_n;
+  L->tile_k = in->tile_k;
+  L->lanes = in->lanes;
+  L->alphabet = in->alphabet;
+  L->tiles = in->tiles;
+  L->kt = in->k / in->tile_k;
+  L->steps = in->tile_n * in->tile_k / in->lanes;
+  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
+  L->region_words = (words + 7) & ~7u;
+  return true;
+}
+
+int device_supported(const dgt_info* in) {
+  if (!in) return DGT_E_ARG;
+  if (in->prob_bits != 12) return DGT_E_UNSUPPORTED;
+  if (in->lanes != 32 && in->lanes != 64) return DGT_E_UNSUPPORTED;
+  return DGT_OK;
+}
+
+struct FusedPlan {
+  uint32_t mt, ilp, waves, tpw, gps, strips, red_cols, lds, m_chunk;
+  size_t part_off, part_bytes, quant_off, ws_bytes;
+};
+
+bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
+  const uint32_t R = in->lanes, tpc = 64 / R;
+  const uint32_t kt = in->k / in->tile_k;
+  // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
+  p->m_chunk = std::min<uint32_t>(m, in->tile_n == 256 ? 16 : 64);
+  p->mt = p->m_chunk <= 16 ? 1 : 4;
+  p->strips = in->n / in->tile_n;
+  const uint32_t chains_total = in->tiles / tpc;
+  p->ilp = (kt % (2 * tpc) == 0 && chains_total >= 1024 * 6) ? 2 : 1;
+  if (kt % (p->ilp * tpc)) return false;
+  p->tpw = p->ilp * tpc;
+  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
+  const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
+  const uint32_t waves_per_strip = kt / p->tpw;
+  p->waves = 8;
+  auto lds_for = [&](uint32_t w) { return kLutBytes + kCumBytes + w * p->ilp * tpc * region_bytes; };
+  while (p->waves > 4 && lds_for(p->waves) > kMaxLds) p->waves /= 2;
+  // small layers: fewer waves per workgroup spread the strip over more CUs
+  if (p->waves == 8 && (uint64_t)p->strips * ((waves_per_strip + 7) / 8) < 512) p->waves = 4;
+  if (lds_for(p->waves) > kMaxLds) return false;
+  p->gps = (waves_per_strip + p->waves - 1) / p->waves;
+  p->lds = lds_for(p->waves);
+  uint32_t rc = in->tile_n;
+  while (rc > 16 && (uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) rc /= 2;
+  if ((uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) {
+    p->lds = p->waves * p->m_chunk * rc * 4;
+    if (p->lds > kMaxLds) return false;
+  }
+  p->red_cols = rc;
+  size_t off = dgt::align_up((size_t)p->strips * 4, 256);
+  p->part_off = off;
+  p->part_bytes = p->gps > 1 ? (size_t)p->strips * p->gps * p->m_chunk * in->tile_n * 4 : 0;
+  off = dgt::align_up(off + p->part_bytes, 256);
+  p->quant_off = off;
+  if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k, 256) + 256;
+  p->ws_bytes = off;
+  return true;
+}
+
+int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t st,
+                 uint8_t** xq, float** sx) {
+  QuantArgs q;
+  q.x = d_x;
+  q.xq = ws_q + 256;
+  q.amax_bits = reinterpret_cast<uint32_t*>(ws_q);
+  q.done = reinterpret_cast<uint32_t*>(ws_q + 4);
+  q.sx = reinterpret_cast<float*>(ws_q + 8);
+  q.count = count;
+  const uint32_t blocks = std::max<uint32_t>(1, std::min<uint32_t>(1024, (count + 2047) / 2048));
+  hipLaunchKernelGGL(k_amax, dim3(blocks), dim3(256), 0, st, q);
+  if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
+  hipLaunchKernelGGL(k_quant, dim3(blocks), dim3(256), 0, st, q);
+  if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
+  *xq = q.xq;
+  *sx = q.sx;
+  return DGT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
+  if (!info || m == 0) return 0;
+  FusedPlan p;
+  if (!plan_fused(info, m, &p)) return 0;
+  return p.ws_bytes;
+}
+
+int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
+                          uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
+                          void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
+  if (!d_blob || !info || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
+  if (((uintptr_t)d_blob & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
+    return DGT_E_ARG;
+  int rc = device_supported(info);
+  if (rc) return rc;
+  if (info->fmt == DGT_FMT_INT4 && (!d_scales || info->k % 128)) return DGT_E_ARG;
+  const uint32_t fn = info->tile_n / 16;
+  if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
+  if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
+  FusedPlan p;
+  if (!plan_fused(info, m, &p)) return DGT_E_UNSUPPORTED;
+  if (ws_bytes < p.ws_bytes) return DGT_E_BUFSIZE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Layer L;
+  layer_from_info(d_blob, info, &L);
+  uint8_t* ws = static_cast<uint8_t*>(d_ws);
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
+  uint32_t xrow = info->k * 2;
+  const float* sxp = nullptr;
+  if (info->fmt == DGT_FMT_FP8_E4M3) {
+    uint8_t* xq = nullptr;
+    float* sx = nullptr;
+    rc = launch_quant(d_x, m * info->k, ws + p.quant_off, st, &xq, &sx);
+    if (rc) return rc;
+    xsrc = xq;
+    xrow = info->k;
+    sxp = sx;
+  }
+  for (uint32_t m0 = 0; m0 < m; m0 += p.m_chunk) {
+    GemmArgs a;
+    a.L = L;
+    a.x = xsrc + (size_t)m0 * xrow;
+    a.scales = d_scales;
+    a.xscale = sxp;
+    a.w_scale = w_scale;
+    a.y = d_y + (size_t)m0 * info->n;
+    a.part = reinterpret_cast<float*>(ws + p.part_off);
+    a.counters = reinterpret_cast<uint32_t*>(ws);
+    a.status = d_status;
+    a.m = std::min<uint32_t>(p.m_chunk, m - m0);
+    a.x_row_bytes = xrow;
+    a.y_row = info->n;
+    a.waves = p.waves;
+    a.tpw = p.tpw;
+    a.gps = p.gps;
+    a.red_cols = p.red_cols;
+    const uint32_t grid = p.strips * p.gps, threads = 64 * p.waves;
+    switch (info->fmt) {
+      case DGT_FMT_INT8:
+        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_INT4:
+        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_FP8_E4M3:
+        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_BF16_SPLIT:
+        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        break;
+      default:
+        rc = DGT_E_ARG;
+    }
+    if (rc) return rc;
+  }
+  return DGT_OK;
+}
+
+int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d_tile_ids,
+                     uint32_t n_ids, void* d_out, int32_t* d_status, void* stream) {
+  if (!d_blob || !info || !d_out) return DGT_E_ARG;
+  if ((uintptr_t)d_blob & 15) return DGT_E_ARG;
+  int rc = device_supported(info);
+  if (rc) return rc;
+  if (!d_tile_ids) n_ids = info->tiles;
+  if (n_ids == 0) return DGT_OK;
+  DecodeArgs a;
+  layer_from_info(d_blob, info, &a.L);
+  a.ids = d_tile_ids;
+  a.n_ids = n_ids;
+  a.out = static_cast<uint8_t*>(d_out);
+  a.status = d_status;
+  const uint32_t R = info->lanes, tpc = 64 / R;
+  const uint32_t ilp = n_ids / tpc >= 1024 * 6 ? 2 : 1;
+  uint32_t waves = 8;
+  const uint32_t region_bytes = a.L.region_words * 2;
+  auto lds_for = [&](uint32_t w) { return kLutBytes + kCumBytes + w * ilp * tpc * region_bytes; };
+  while (waves > 4 && lds_for(waves) > kMaxLds) waves /= 2;
+  if (lds_for(waves) > kMaxLds) return DGT_E_UNSUPPORTED;
+  a.waves = waves;
+  const uint32_t per_wg = waves * ilp * tpc;
+  const uint32_t grid = (n_ids + per_wg - 1) / per_wg;
+  const uint32_t lds = lds_for(waves);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+switch (info->fmt) {
+    case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, grid, 64 * waves, lds, st);
+    default: break;
+  }
+  return DGT_E_UNSUPPORTED;
+}
+
+size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, uint32_t m) {
+  if (m == 0 || (tile_n != 128 && tile_n != 256) || n % tile_n || k % 64) return 0;
+  const uint32_t strips = n / tile_n, kt = k / 64, tpw = 2, waves = 8;
+  const uint32_t gps = (kt / tpw + waves - 1) / waves;
+  const uint32_t mc = std::min<uint32_t>(m, tile_n == 256 ? 16 : 64);
+  size_t off = dgt::align_up((size_t)strips * 4, 256);
+  if (gps > 1) off += (size_t)strips * gps * mc * tile_n * 4;
+  off = dgt::align_up(off, 256);
+  if (fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * k, 256) + 256;
+  return off;
+}
+
+int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const void* d_w,
+                   const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
+                   float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!d_w || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
+  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_SPLIT) return DGT_E_ARG;
+  if ((tile_n != 128 && tile_n != 256) || n % tile_n || k % 64 || (k / 64) % 2)
+    return DGT_E_SHAPE;
+  if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;
+  if (((uintptr_t)d_w & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
+    return DGT_E_ARG;
+  const size_t need = dgt_dense_workspace(fmt, n, k, tile_n, m);
+  if (ws_bytes < need) return DGT_E_BUFSIZE;
+  const uint32_t strips = n / tile_n, kt = k / 64, tpw = 2, waves = 8;
+  const uint32_t gps = (kt / tpw + waves - 1) / waves;
+  const uint32_t mc = std::min<uint32_t>(m, tile_n == 256 ? 16 : 64), mt = mc <= 16 ? 1 : 4;
+  uint8_t* ws = static_cast<uint8_t*>(d_ws);
+  size_t part_off = dgt::align_up((size_t)strips * 4, 256);
+  size_t quant_off = dgt::align_up(part_off + (gps > 1 ? (size_t)strips * gps * mc * tile_n * 4 : 0), 256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
+  uint32_t xrow = k * 2;
+  const float* sxp = nullptr;
+  if (fmt == DGT_FMT_FP8_E4M3) {
+    uint8_t* xq = nullptr;
+    float* sx = nullptr;
+    int rc = launch_quant(d_x, m * k, ws + quant_off, st, &xq, &sx);
+    if (rc) return rc;
+    xsrc = xq;
+    xrow = k;
+    sxp = sx;
+  }
+  const uint32_t lds = 64 * 1024;
+  for (uint32_t m0 = 0; m0 < m; m0 += mc) {
+    DenseArgs d;
+    GemmArgs& a = d.g;
+    a.L = Layer{};
+    a.x = xsrc + (size_t)m0 * xrow;
+    a.scales = d_scales;
+    a.xscale = sxp;
+    a.w_scale = w_scale;
+    a.y = d_y + (size_t)m0 * n;
+    a.part = reinterpret_cast<float*>(ws + part_off);
+    a.counters = reinterpret_cast<uint32_t*>(ws);
+    a.status = nullptr;
+    a.m = std::min<uint32_t>(mc, m - m0);
+    a.x_row_bytes = xrow;
+    a.y_row = n;
+    a.waves = waves;
+    a.tpw = tpw;
+    a.gps = gps;
+    uint32_t rc_cols = tile_n;
+    while (rc_cols > 16 && (uint64_t)waves * a.m * rc_cols * 4 > lds) rc_cols /= 2;
+    a.red_cols = rc_cols;
+    d.w = static_cast<const uint8_t*>(d_w);
+    d.n = n;
+    d.k = k;
+    d.kt = kt;
+    const uint32_t grid = strips * gps;
+int rc = DGT_E_UNSUPPORTED;
+    const uint32_t fnv = tile_n / 16;
+    switch (fmt) {
+      case DGT_FMT_INT8: rc = launch_dense<INT8>(d, fnv, mt, grid, 64 * waves, lds, st); break;
+      case DGT_FMT_INT4: rc = launch_dense<INT4>(d, fnv, mt, grid, 64 * waves, lds, st); break;
+      case DGT_FMT_FP8_E4M3: rc = launch_dense<FP8>(d, fnv, mt, grid, 64 * waves, lds, st); break;
+      case DGT_FMT_BF16_SPLIT: rc = launch_dense<BF16>(d, fnv, mt, grid, 64 * waves, lds, st); break;
+      default: break;
+    }
+    if (rc) return rc;
+    return DGT_E_UNSUPPORTED;
+  }
+  return DGT_OK;
+}
+
+}  // extern "C"

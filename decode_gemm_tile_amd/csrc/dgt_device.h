@@ -1,0 +1,191 @@
+// Device building blocks of libdgt for gfx950 (CDNA4, wave64).
+//
+// Method: the page "arXiv'26 | 无损压缩逼近 Shannon 极限：你的 LLM 权重里一半以上的
+// bit 是白存的" §3.1 -- every tile stream is split into R rANS lane sub-streams,
+// one state per lane of the wavefront; decoded tiles go straight to on-chip
+// storage and into the matrix multiply, never to global memory; decoding of the
+// next tile overlaps the product of the current one.
+//
+// MI355X mapping used here:
+//   * one wave64 holds the R lane states of one tile (R = 64) or of two tiles
+//     (R = 32, lanes 0-31 and 32-63);
+//   * the per-layer decode table lives in LDS: 4096 slots x 8 bytes
+//     {f | symbol << 24, slot - c_s}, so one ds_read_b64 gives everything a
+//     step needs and the state update is a single v_mad_u32_u24;
+//   * renormalisation words are read from the tile's stream staged in LDS; the
+//     lanes that need a word get consecutive words through a wave ballot and
+//     mbcnt prefix count, in increasing lane order;
+//   * the tile-local symbol order equals the 16x16x32 MFMA B-operand register
+//     layout (lane p: row p % 16, k = 8 * (p / 16) + e), so after 8 steps a lane
+//     holds exactly its B operand: decoded values go register -> matrix core.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgt {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kL = 1u << 16;
+constexpr uint32_t kSlots = 4096;      // 2^prob_bits, prob_bits = 12 on the device
+constexpr uint32_t kLutBytes = kSlots * 8;
+constexpr uint32_t kCumBytes = 1040;   // (256 + 1) u32, padded
+constexpr uint32_t kSlackWords = 64;   // u16 words of slack after each staged stream
+
+enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4 };
+
+// Everything a kernel needs to know about a layer (passed by value).
+struct Layer {
+  const uint16_t* table;    // f[alphabet]
+  const uint32_t* index;    // off[tiles + 1], 4-byte units
+  const uint8_t* ktab;      // k[tiles]
+  const uint32_t* streams;  // streams section
+  const uint8_t* raw;       // raw low bytes (BF16 split) or null
+  uint32_t n, k, tile_n, tile_k, lanes, alphabet, tiles, kt, steps;
+  uint32_t region_words;    // u16 capacity of one staged-stream region (even)
+};
+
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Build the slot table in LDS from the shared frequency table: every slot r
+// maps to the symbol s with c_s <= r < c_s + f_s.  Caller synchronises.
+__device__ inline void build_lut(const uint16_t* table, uint32_t alphabet, u32x2* lut,
+                                 uint32_t* cum) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t lane = t & 63, wave = t >> 6;
+  // inclusive scan of f over <= 256 symbols: wave scans plus wave totals
+  uint32_t v = (t < alphabet) ? (uint32_t)table[t] : 0u;
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (t < 256) cum[1 + t] = v;
+  if (t == 0) cum[0] = 0;
+  __syncthreads();
+  if (t < 256 && wave > 0) {
+    uint32_t add = 0;
+    for (uint32_t w = 0; w < wave; ++w) add += cum[1 + w * 64 + 63];
+    v += add;
+  }
+  __syncthreads();
+  if (t < 256) cum[1 + t] = v;
+  __syncthreads();
+  for (uint32_t r = t; r < kSlots; r += blockDim.x) {
+    uint32_t lo = 0, hi = alphabet;  // cum[lo] <= r < cum[hi]
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (cum[mid] <= r) lo = mid; else hi = mid;
+    }
+    const uint32_t f = cum[lo + 1] - cum[lo];
+    u32x2 e;
+    e.x = f | (lo << 24);
+    e.y = r - cum[lo];
+    lut[r] = e;
+  }
+}
+
+// R lane states of one chain: one tile (R = 64) or two tiles (R = 32).
+// Fields marked "uniform" hold the same value on every lane.
+struct Chain {
+  uint32_t x;      // lane state
+  uint32_t lim;    // first payload step of the lane's tile (steps - k)
+  uint32_t p0;     // uniform: next word of tile A (u16 index into the LDS word array)
+  uint32_t p1;     // uniform: next word of tile B (R = 32)
+  uint32_t e0;     // uniform: end of tile A's staged words
+  uint32_t e1;     // uniform: end of tile B's staged words
+  uint32_t s0;     // uniform: start of tile A's words
+  uint32_t s1;     // uniform: start of tile B's words
+  uint32_t ovf;    // uniform: bit 0 / bit 1 -> tile A / B read past its stream
+};
+
+// One rANS decode step on every lane of a chain; returns the LUT word whose top
+// byte is the decoded symbol.  CAREFUL handles the switch to the payload state
+// (x -= L at step == lim) and suppresses renormalisation from then on.
+template <int R, bool CAREFUL>
+__device__ __forceinline__ uint32_t step(Chain& c, const u32x2* __restrict__ lut,
+                                         const uint16_t* __restrict__ words, uint32_t s,
+                                         bool upper_half) {
+  uint32_t x = c.x;
+  if (CAREFUL) x = (s == c.lim) ? x - kL : x;
+  const u32x2 e = lut[x & (kSlots - 1)];
+  uint32_t xn = (e.x & 0xFFFFFFu) * (x >> 12) + e.y;  // v_mad_u32_u24
+  bool need = xn < kL;
+  if (CAREFUL) need = need && (s < c.lim);
+  const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+  const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+  uint32_t idx;
+  if (R == 64) {
+    idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, c.p0));
+    uint32_t np = c.p0 + (uint32_t)__builtin_popcountll(m);
+    if (np > c.e0) { c.ovf |= 1u; np = c.e0; }
+    c.p0 = np;
+  } else {
+    const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
+    const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
+    const uint32_t base = upper_half ? c.p1 - pl : c.p0;
+    idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, base));
+    uint32_t n0 = c.p0 + pl, n1 = c.p1 + ph;
+    if (n0 > c.e0) { c.ovf |= 1u; n0 = c.e0; }
+    if (n1 > c.e1) { c.ovf |= 2u; n1 = c.e1; }
+    c.p0 = n0;
+    c.p1 = n1;
+  }
+  if (need) xn = (xn << 16) | (uint32_t)words[idx];
+  c.x = xn;
+  return e.x;
+}
+
+// Integrity flags of the chain's tile(s) after the last step, per lane's tile:
+// 1 = a lane did not return to its initial value, 2 = words consumed != stream,
+// 4 = read past the stream.
+template <int R>
+__device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
+                                                bool upper_half) {
+  const uint32_t want = (c.lim == steps) ? kL : 0u;
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(c.x != want);
+  uint32_t f = 0;
+  if (R == 64) {
+    if (bad) f |= 1u;
+    const uint32_t used = c.p0 - c.s0, avail = c.e0 - c.s0;
+    if (!(used == avail || used + 1 == avail)) f |= 2u;
+    if (c.ovf & 1u) f |= 4u;
+  } else {
+    const uint32_t half_bad = upper_half ? (uint32_t)(bad >> 32) : (uint32_t)bad;
+    if (half_bad) f |= 1u;
+    const uint32_t p = upper_half ? c.p1 : c.p0, st = upper_half ? c.s1 : c.s0,
+                   en = upper_half ? c.e1 : c.e0;
+    const uint32_t used = p - st, avail = en - st;
+    if (!(used == avail || used + 1 == avail)) f |= 2u;
+    if (c.ovf & (upper_half ? 2u : 1u)) f |= 4u;
+  }
+  return f;
+}
+
+// Stage tile t's word stream into LDS words[start ..) using the lanes of one
+// half (R = 32) or the whole wave (R = 64); load the lane states.  Returns the
+// number of staged u16 words (including a possible pad word).
+__device__ __forceinline__ uint32_t stage_tile(const Layer& L, uint32_t t, uint16_t* words,
+                                               uint32_t start, uint32_t sub_lane,
+                                               uint32_t sub_size) {
+  const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
+  const uint32_t words4 = o1 - o0 - L.lanes;
+  const uint32_t* src = L.streams + o0 + L.lanes;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(words + start);
+  for (uint32_t i = sub_lane; i < words4; i += sub_size) dst[i] = src[i];
+  return 2 * words4;
+}
+
+}  // namespace dev
+}  // namespace dgt

@@ -1,0 +1,91 @@
+// Instantiates the kernels of one weight format (compiled once per format with
+// -DDGT_FMT=<dgt_format>) so the formats build in parallel.
+#include "../../include/dgt.h"
+#include "dgt_launch.h"
+
+#ifndef DGT_FMT
+#error "DGT_FMT must be defined"
+#endif
+
+namespace dgt {
+namespace dev {
+namespace {
+
+template <typename K>
+bool set_lds(K kernel, uint32_t bytes) {
+  if (bytes <= 64 * 1024) return true;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
+         hipSuccess;
+}
+
+template <int R, int FN, int MT, int ILP>
+int fused_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
+  auto k = k_fused<DGT_FMT, R, FN, MT, ILP>;
+  if (!set_lds(k, lds)) return DGT_E_HIP;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);
+  return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
+}
+
+template <int R, int FN>
+int fused_r(const GemmArgs& a, uint32_t mt, uint32_t ilp, uint32_t grid, uint32_t threads,
+            uint32_t lds, hipStream_t st) {
+  if (mt == 1 && ilp == 1) return fused_t<R, FN, 1, 1>(a, grid, threads, lds, st);
+  if (mt == 1 && ilp == 2) return fused_t<R, FN, 1, 2>(a, grid, threads, lds, st);
+  if constexpr (FN <= 8) {
+    if (mt == 4 && ilp == 1) return fused_t<R, FN, 4, 1>(a, grid, threads, lds, st);
+    if (mt == 4 && ilp == 2) return fused_t<R, FN, 4, 2>(a, grid, threads, lds, st);
+  }
+  return DGT_E_UNSUPPORTED;
+}
+
+}  // namespace
+
+template <>
+int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt,
+                          uint32_t ilp, uint32_t grid, uint32_t threads, uint32_t lds,
+                          hipStream_t st) {
+  if (lanes == 64 && fn == 8) return fused_r<64, 8>(a, mt, ilp, grid, threads, lds, st);
+  if (lanes == 64 && fn == 16) return fused_r<64, 16>(a, mt, ilp, grid, threads, lds, st);
+  if (lanes == 32 && fn == 8) return fused_r<32, 8>(a, mt, ilp, grid, threads, lds, st);
+  if (lanes == 32 && fn == 16) return fused_r<32, 16>(a, mt, ilp, grid, threads, lds, st);
+  return DGT_E_UNSUPPORTED;
+}
+
+template <>
+int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, uint32_t grid,
+                           uint32_t threads, uint32_t lds, hipStream_t st) {
+#define DGT_DECODE_CASE(RR, II)                                                \
+  if (lanes == RR && ilp == II) {                                              \
+    auto k = k_decode<DGT_FMT, RR, II>;                                        \
+    if (!set_lds(k, lds)) return DGT_E_HIP;                                    \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);              \
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;               \
+  }
+  DGT_DECODE_CASE(64, 1)
+  DGT_DECODE_CASE(64, 2)
+  DGT_DECODE_CASE(32, 1)
+  DGT_DECODE_CASE(32, 2)
+#undef DGT_DECODE_CASE
+  return DGT_E_UNSUPPORTED;
+}
+
+template <>
+int launch_dense<DGT_FMT>(const DenseArgs& d, uint32_t fn, uint32_t mt, uint32_t grid,
+                          uint32_t threads, uint32_t lds, hipStream_t st) {
+#define DGT_DENSE_CASE(FNV, MTV)                                                        \
+  if (fn == FNV && mt == MTV) {                                                         \
+    auto k = k_dense<DGT_FMT, FNV, MTV>;                                                \
+    if (!set_lds(k, lds)) return DGT_E_HIP;                                             \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, d);                       \
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                        \
+  }
+  DGT_DENSE_CASE(8, 1)
+  DGT_DENSE_CASE(8, 4)
+  DGT_DENSE_CASE(16, 1)
+#undef DGT_DENSE_CASE
+  return DGT_E_UNSUPPORTED;
+}
+
+}  // namespace dev
+}  // namespace dgt

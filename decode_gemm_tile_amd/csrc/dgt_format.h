@@ -1,0 +1,56 @@
+// Internal constants and helpers of the compressed-layer format (library side).
+//
+// The format follows the execution model of the page "arXiv'26 | 无损压缩逼近
+// Shannon 极限" §3.1 (tiles in the GEMM's geometry, one shared frequency
+// table per layer, a per-tile offset index, R rANS lane states per tile); the
+// byte layout itself is documented in include/dgt.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dgt {
+
+constexpr uint32_t kMagic = 0x31544744u;  // "DGT1" little-endian
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kHeaderBytes = 128;
+constexpr uint32_t kStateL = 1u << 16;     // normalised states live in [L, 2^32)
+constexpr uint32_t kKmax = 16;             // payload-step cap per tile
+constexpr uint32_t kGroup = 128;           // INT4 scale group along K
+
+// Byte offsets of header fields.
+struct HeaderLayout {
+  static constexpr size_t magic = 0, version = 4, header_bytes = 6, fmt = 8, flags = 12,
+                          n = 16, k = 20, tile_n = 24, tile_k = 28, lanes = 32,
+                          prob_bits = 36, alphabet = 40, tiles = 44, table_off = 48,
+                          index_off = 56, ktab_off = 64, streams_off = 72, raw_off = 80,
+                          total = 88, max_tile_words4 = 96, kmax = 100;
+};
+
+inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : 256u; }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Tile-local position of symbol j = s*R + p (s = 8g + e; g = fk*Fn + fn).
+inline void symbol_position(uint32_t j, uint32_t tile_n, uint32_t lanes, uint32_t* row,
+                            uint32_t* col) {
+  const uint32_t s = j / lanes, p = j % lanes;
+  const uint32_t g = s >> 3, e = s & 7;
+  const uint32_t fn_count = tile_n / 16;
+  const uint32_t fk = g / fn_count, fn = g % fn_count;
+  *row = fn * 16 + (p & 15);
+  *col = fk * (lanes / 2) + (p >> 4) * 8 + e;
+}
+
+// Tile-local position of raw byte q = g*8R + p*8 + e (lane-major).
+inline void raw_position(uint32_t q, uint32_t tile_n, uint32_t lanes, uint32_t* row,
+                         uint32_t* col) {
+  const uint32_t g = q / (8 * lanes), rem = q % (8 * lanes);
+  const uint32_t p = rem >> 3, e = rem & 7;
+  const uint32_t fn_count = tile_n / 16;
+  const uint32_t fk = g / fn_count, fn = g % fn_count;
+  *row = fn * 16 + (p & 15);
+  *col = fk * (lanes / 2) + (p >> 4) * 8 + e;
+}
+
+}  // namespace dgt

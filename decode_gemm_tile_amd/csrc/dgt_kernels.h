@@ -1,0 +1,506 @@
+// HIP kernel templates of libdgt for gfx950 (instantiated per format in dgt_fmt.hip).
+//
+// The fused path follows the run-time stage of "arXiv'26 | 无损压缩逼近
+// Shannon 极限" §3.1: tiles are decoded on chip and handed straight to the
+// matrix multiply; the decompressed layer is never written to HBM.  §2.2
+// (layer-level decompress-to-global then GEMM) is kept only as the
+// dgt_decode_tiles + dgt_dense_gemm comparison path.
+//
+// Work decomposition (static schedule, fixed at launch): the output is cut into
+// strips of tile_n columns of Y (one tile row band of W).  A strip's k-tiles are
+// split over waves: each wave decodes ILP chains (ILP independent rANS chains
+// interleaved step by step, so one wave keeps several LDS round trips in
+// flight) and accumulates its partial Y[M, tile_n] in registers.  The waves of
+// a workgroup cover consecutive k-tiles of one strip and reduce their partials
+// through LDS in a fixed order; when a strip needs several workgroups, each
+// writes its partial to the workspace and the last one to arrive (atomic
+// counter per strip) sums them in workgroup order and writes Y.  Results are
+// therefore deterministic run to run.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "dgt_device.h"
+
+namespace dgt {
+namespace dev {
+
+// ------------------------------------------------------------ kernel params
+struct GemmArgs {
+  Layer L;
+  const uint8_t* x;          // bf16 bits [M, K] (or e4m3 bytes [M, K] for FP8)
+  const uint16_t* scales;    // INT4: bf16 bits [N, K/128]
+  const float* xscale;       // FP8: device sx (per-tensor activation scale)
+  float w_scale;             // FP8 weight scale
+  float* y;                  // fp32 [M, N]
+  float* part;               // workspace partials [strips][gps][M][tile_n]
+  uint32_t* counters;        // workspace counters [strips]
+  int32_t* status;           // per-tile status or null
+  uint32_t m;                // rows of X / Y in this launch (<= 16 * MT)
+  uint32_t x_row_bytes;      // row stride of x in bytes
+  uint32_t y_row;            // row stride of y in floats (= N)
+  uint32_t waves;            // waves per workgroup
+  uint32_t tpw;              // k-tiles per wave
+  uint32_t gps;              // workgroups per strip
+  uint32_t red_cols;         // tile_n columns reduced per LDS pass
+};
+
+template <int FMT>
+struct OperandTraits;
+template <>
+struct OperandTraits<INT8> { static constexpr int xbytes = 2; };
+template <>
+struct OperandTraits<INT4> { static constexpr int xbytes = 2; };
+template <>
+struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
+template <>
+struct OperandTraits<FP8> { static constexpr int xbytes = 1; };
+
+// B operand of one fragment from 8 decoded LUT words (+ raw bytes / scales).
+struct BOp {
+  u32x4 v;  // bf16 path: 8 bf16; fp8 path: v.x, v.y hold 8 bytes
+};
+
+__device__ __forceinline__ uint32_t pack_hi_bytes(uint32_t e1, uint32_t e0) {
+  return __builtin_amdgcn_perm(e1, e0, 0x0c0c0703u);  // [s0, s1, 0, 0]
+}
+
+template <int FMT>
+__device__ __forceinline__ BOp make_b(const uint32_t (&e)[8], u32x2 raw, float sc, float nsc8) {
+  BOp b;
+  if constexpr (FMT == BF16) {
+    const uint32_t p01 = pack_hi_bytes(e[1], e[0]);
+    const uint32_t p23 = pack_hi_bytes(e[3], e[2]);
+    const uint32_t p45 = pack_hi_bytes(e[5], e[4]);
+    const uint32_t p67 = pack_hi_bytes(e[7], e[6]);
+    b.v.x = __builtin_amdgcn_perm(p01, raw.x, 0x05010400u);
+    b.v.y = __builtin_amdgcn_perm(p23, raw.x, 0x05030402u);
+    b.v.z = __builtin_amdgcn_perm(p45, raw.y, 0x05010400u);
+    b.v.w = __builtin_amdgcn_perm(p67, raw.y, 0x05030402u);
+  } else if constexpr (FMT == INT8) {
+    uint32_t f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __float_as_uint((float)((int32_t)e[i] >> 24));
+    b.v.x = __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
+    b.v.y = __builtin_amdgcn_perm(f[3], f[2], 0x07060302u);
+    b.v.z = __builtin_amdgcn_perm(f[5], f[4], 0x07060302u);
+    b.v.w = __builtin_amdgcn_perm(f[7], f[6], 0x07060302u);
+  } else if constexpr (FMT == INT4) {
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx2 w;
+      w.x = __builtin_fmaf((float)(e[2 * i] >> 24), sc, nsc8);
+      w.y = __builtin_fmaf((float)(e[2 * i + 1] >> 24), sc, nsc8);
+      const bf16x2 h = __builtin_convertvector(w, bf16x2);
+      o[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
+  } else {  // FP8: bytes
+    b.v.x = pack_hi_bytes(e[1], e[0]) | (pack_hi_bytes(e[3], e[2]) << 16);
+    b.v.y = pack_hi_bytes(e[5], e[4]) | (pack_hi_bytes(e[7], e[6]) << 16);
+    b.v.z = 0; b.v.w = 0;
+  }
+  return b;
+}
+
+template <int FMT>
+__device__ __forceinline__ floatx4 mfma(const u32x4& a, const BOp& b, floatx4 acc) {
+  if constexpr (FMT == FP8) {
+    const long av = (long)(((uint64_t)a.y << 32) | a.x);
+    const long bv = (long)(((uint64_t)b.v.y << 32) | b.v.x);
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, acc, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b.v), acc, 0,
+                                                   0, 0);
+  }
+}
+
+// A operand (X) for lane l: row m, 8 consecutive k starting at k0.
+template <int FMT>
+__device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t k0) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (m < a.m) {
+    const uint8_t* p = a.x + (size_t)m * a.x_row_bytes + (size_t)k0 * OperandTraits<FMT>::xbytes;
+    if constexpr (FMT == FP8) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      r.x = v.x; r.y = v.y;
+    } else {
+      r = *reinterpret_cast<const u32x4*>(p);
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- reduction
+// Sum the per-wave partials acc[FN][MT] of a workgroup in wave order through
+// LDS, then either write Y (one workgroup per strip) or a workspace partial
+// with the last-arriving workgroup summing all partials in workgroup order.
+template <int FN, int MT>
+__device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
+                                                 float* red, uint32_t strip, uint32_t gslot,
+                                                 float out_scale) {
+  const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t M = a.m, TN = FN * 16, W = a.waves, RC = a.red_cols;
+  const uint32_t n0 = strip * TN;
+  __syncthreads();  // LUT / staged streams are no longer needed
+  for (uint32_t c0 = 0; c0 < TN; c0 += RC) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const uint32_t col = fn * 16 + (lane & 15);
+      if (col >= c0 && col < c0 + RC) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t m = mt * 16 + 4 * (lane >> 4) + i;
+            if (m < M) red[((size_t)wave * M + m) * RC + (col - c0)] = acc[fn][mt][i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (uint32_t idx = t; idx < M * RC; idx += blockDim.x) {
+      float s = 0.f;
+      for (uint32_t w = 0; w < W; ++w) s += red[(size_t)w * M * RC + idx];
+      const uint32_t m = idx / RC, col = c0 + idx % RC;
+      if (a.gps == 1) {
+        a.y[(size_t)m * a.y_row + n0 + col] = s * out_scale;
+      } else {
+        a.part[(((size_t)strip * a.gps + gslot) * M + m) * TN + col] = s;
+      }
+    }
+    __syncthreads();
+  }
+  if (a.gps == 1) return;
+  __shared__ uint32_t last_flag;
+  __threadfence();
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t old = atomicAdd(&a.counters[strip], 1u);
+    last_flag = (old == a.gps - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (uint32_t idx = t; idx < M * TN; idx += blockDim.x) {
+    const uint32_t m = idx / TN, col = idx % TN;
+    float s = 0.f;
+    for (uint32_t g = 0; g < a.gps; ++g)
+      s += a.part[(((size_t)strip * a.gps + g) * M + m) * TN + col];
+    a.y[(size_t)m * a.y_row + n0 + col] = s * out_scale;
+  }
+  if (t == 0) a.counters[strip] = 0u;
+}
+
+// --------------------------------------------------------------- fused GEMM
+// FN = tile_n / 16 row bands per tile, MT = 16-row blocks of X, ILP = chains
+// per wave.  LDS: LUT | cumulative table | staged stream regions.
+template <int FMT, int R, int FN, int MT, int ILP>
+__global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  u32x2* lut = reinterpret_cast<u32x2*>(smem);
+  uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
+  const Layer& L = a.L;
+  constexpr uint32_t TPC = 64 / R;  // tiles per chain
+  constexpr uint32_t FW = R / 2;    // fragment width (columns)
+
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const uint32_t strip = blockIdx.x / a.gps, gslot = blockIdx.x % a.gps;
+  const uint32_t kt_first = uniform((gslot * a.waves + wave) * a.tpw);
+  const bool active = kt_first < L.kt;
+  const bool upper = lane >= 32;
+  const uint32_t half_lane = lane & 31;
+
+  build_lut(L.table, L.alphabet, lut, cum);
+
+  Chain ch[ILP];
+  uint32_t tile_lane[ILP];
+  uint32_t k0_lane[ILP];
+  const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t ta = strip * L.kt + kt_first + c * TPC;
+      const uint32_t tb = (R == 32) ? ta + 1 : ta;
+      const uint32_t ra = region0 + c * TPC * L.region_words;
+      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
+      uint32_t na, nb;
+      if (R == 64) {
+        na = stage_tile(L, ta, words, ra, lane, 64);
+        nb = na;
+      } else {
+        const uint32_t mine = stage_tile(L, upper ? tb : ta, words, upper ? rb : ra,
+                                         half_lane, 32);
+        na = uniform(mine);
+        nb = (uint32_t)__builtin_amdgcn_readlane((int)mine, 32);
+      }
+      const uint32_t t_l = upper && R == 32 ? tb : ta;
+      tile_lane[c] = t_l;
+      ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
+      ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
+      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
+      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
+      ch[c].ovf = 0;
+      const uint32_t kt_l = kt_first + c * TPC + ((R == 32 && upper) ? 1u : 0u);
+      k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
+    }
+  }
+  __syncthreads();
+
+  floatx4 acc[FN][MT];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (active) {
+    uint32_t lim_min = ch[0].lim;
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      lim_min = min(lim_min, uniform(ch[c].lim));
+      if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
+    }
+    const uint32_t FK = L.tile_k / FW;
+    const uint32_t kgroups = L.k / 128;
+    for (uint32_t fk = 0; fk < FK; ++fk) {
+      u32x4 A[ILP][MT];
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint32_t g = fk * FN + fn;
+        const uint32_t s0 = g * 8;
+        u32x2 raw[ILP];
+        float sc[ILP], nsc8[ILP];
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) {
+          raw[c] = u32x2{0u, 0u};
+          sc[c] = 0.f; nsc8[c] = 0.f;
+          if constexpr (FMT == BF16) {
+            const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
+                                (size_t)g * 8 * R + (lane % R) * 8;
+            raw[c] = *reinterpret_cast<const u32x2*>(rp);
+          }
+          if constexpr (FMT == INT4) {
+            const uint32_t row = strip * L.tile_n + fn * 16 + (lane & 15);
+            const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fk * FW) / 128];
+            sc[c] = __uint_as_float((uint32_t)sb << 16);
+            nsc8[c] = -8.f * sc[c];
+          }
+        }
+        uint32_t e[ILP][8];
+        // payload steps (at most the last 16) fall in the last two fragments
+        if (fn < FN - 2 || s0 + 7 < lim_min) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int c = 0; c < ILP; ++c)
+              e[c][i] = step<R, false>(ch[c], lut, words, s0 + i, upper);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int c = 0; c < ILP; ++c)
+              e[c][i] = step<R, true>(ch[c], lut, words, s0 + i, upper);
+        }
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) {
+          const BOp b = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = mfma<FMT>(A[c][mt], b, acc[fn][mt]);
+        }
+      }
+    }
+    if (a.status) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
+        if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+      }
+    }
+  }
+  float out_scale = 1.f;
+  if constexpr (FMT == FP8) out_scale = a.xscale[0] * a.w_scale;
+  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), strip, gslot, out_scale);
+}
+
+// --------------------------------------------------------------- decode only
+struct DecodeArgs {
+  Layer L;
+  const uint32_t* ids;  // tile ids or null (all)
+  uint32_t n_ids;
+  uint8_t* out;         // [N, K] of u8 or u16
+  int32_t* status;
+  uint32_t waves;
+};
+
+template <int FMT, int R, int ILP>
+__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  u32x2* lut = reinterpret_cast<u32x2*>(smem);
+  uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
+  const Layer& L = a.L;
+  constexpr uint32_t TPC = 64 / R;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const bool upper = lane >= 32;
+  const uint32_t half_lane = lane & 31;
+  const uint32_t first = uniform((blockIdx.x * a.waves + wave) * ILP * TPC);
+  const bool active = first < a.n_ids;
+
+  build_lut(L.table, L.alphabet, lut, cum);
+  Chain ch[ILP];
+  uint32_t tile_lane[ILP];
+  const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      // slots past the end repeat the last id (same tile decoded twice, same output)
+      uint32_t ia = min(first + c * TPC, a.n_ids - 1);
+      uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
+      const uint32_t ta = a.ids ? a.ids[ia] : ia;
+      const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
+      const uint32_t ra = region0 + c * TPC * L.region_words;
+      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
+      uint32_t na, nb;
+      if (R == 64) {
+        na = stage_tile(L, ta, words, ra, lane, 64);
+        nb = na;
+      } else {
+        const uint32_t mine = stage_tile(L, upper ? tb : ta, words, upper ? rb : ra,
+                                         half_lane, 32);
+        na = uniform(mine);
+        nb = (uint32_t)__builtin_amdgcn_readlane((int)mine, 32);
+      }
+      const uint32_t t_l = upper && R == 32 ? tb : ta;
+      tile_lane[c] = t_l;
+      ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
+      ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
+      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
+      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
+      ch[c].ovf = 0;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  uint32_t lim_min = L.steps;
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    lim_min = min(lim_min, uniform(ch[c].lim));
+    if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
+  }
+  const uint32_t FN = L.tile_n / 16;
+  const uint32_t G = L.steps / 8;
+  const uint32_t p = lane % R;
+  for (uint32_t g = 0; g < G; ++g) {
+    const uint32_t s0 = g * 8;
+    uint32_t e[ILP][8];
+    if (s0 + 7 < lim_min) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) e[c][i] = step<R, false>(ch[c], lut, words, s0 + i, upper);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) e[c][i] = step<R, true>(ch[c], lut, words, s0 + i, upper);
+    }
+    const uint32_t fk = g / FN, fn = g % FN;
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t t = tile_lane[c];
+      const uint32_t row = (t / L.kt) * L.tile_n + fn * 16 + (p & 15);
+      const uint32_t col = (t % L.kt) * L.tile_k + fk * (R / 2) + 8 * (p >> 4);
+      if constexpr (FMT == BF16) {
+        const uint8_t* rp = L.raw + (size_t)t * L.tile_n * L.tile_k + (size_t)g * 8 * R + p * 8;
+        const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);
+        const BOp b = make_b<BF16>(e[c], raw, 0.f, 0.f);
+        *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
+      } else {
+        u32x2 v;
+        v.x = pack_hi_bytes(e[c][1], e[c][0]) | (pack_hi_bytes(e[c][3], e[c][2]) << 16);
+        v.y = pack_hi_bytes(e[c][5], e[c][4]) | (pack_hi_bytes(e[c][7], e[c][6]) << 16);
+        *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
+      }
+    }
+  }
+  if (a.status) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
+      if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+    }
+  }
+}
+
+// -------------------------------------------------------------- dense GEMM
+// Same strip / wave decomposition and reduction as k_fused, W read from HBM
+// in the layout dgt_decode_tiles writes (row-major [N, K] elements).
+struct DenseArgs {
+  GemmArgs g;
+  const uint8_t* w;
+  uint32_t n, k, kt;   // kt: 64-column k-tiles per strip
+};
+
+template <int FMT, int FN, int MT>
+__global__ __launch_bounds__(512) void k_dense(DenseArgs d) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const GemmArgs& a = d.g;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const uint32_t strip = blockIdx.x / a.gps, gslot = blockIdx.x % a.gps;
+  const uint32_t kt_first = uniform((gslot * a.waves + wave) * a.tpw);
+  floatx4 acc[FN][MT];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t kgroups = d.k / 128;
+  for (uint32_t kt = kt_first; kt < min(kt_first + a.tpw, d.kt); ++kt) {
+#pragma unroll
+    for (uint32_t fk = 0; fk < 2; ++fk) {
+      const uint32_t k0 = kt * 64 + fk * 32 + 8 * (lane >> 4);
+      u32x4 A[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) A[mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint32_t row = strip * FN * 16 + fn * 16 + (lane & 15);
+        BOp b;
+        if constexpr (FMT == BF16) {
+          b.v = *reinterpret_cast<const u32x4*>(d.w + ((size_t)row * d.k + k0) * 2);
+        } else {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(d.w + (size_t)row * d.k + k0);
+          uint32_t e[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = v.x << (24 - 8 * i);
+            e[4 + i] = v.y << (24 - 8 * i);
+          }
+          float sc = 0.f, nsc8 = 0.f;
+          if constexpr (FMT == INT4) {
+            sc = __uint_as_float((uint32_t)a.scales[(size_t)row * kgroups + k0 / 128] << 16);
+            nsc8 = -8.f * sc;
+          }
+          b = make_b<FMT>(e, u32x2{0u, 0u}, sc, nsc8);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = mfma<FMT>(A[mt], b, acc[fn][mt]);
+      }
+    }
+  }
+  float out_scale = 1.f;
+  if constexpr (FMT == FP8) out_scale = a.xscale[0] * a.w_scale;
+  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), strip, gslot, out_scale);
+}
+
+}  // namespace dev
+}  // namespace dgt

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Decoded weights must be bit-exact (the method is lossless: the decoded layer is
+the input itself, and the oracle's decoder gives the same symbols); GEMM
+outputs (fp32 accumulation) must be within 1e-5 relative Frobenius error of the
+fp64 oracle.  Sizes span several tiles, several workgroups per strip and
+ragged wave/workgroup tails."""
+
+import numpy as np
+import pytest
+
+import decode_gemm_tile_amd as dgt
+import workloads
+from oracle import blob as oblob
+from oracle import gemm as ogemm
+from tests.gpu_util import (codes_as_u8_or_u16, decoded_to_numpy, reference, rel_err, to_dev,
+                            x_dev)
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+F8, F4, FE, FB = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
+                  dgt.DGT_FMT_BF16_SPLIT)
+
+# (fmt, N, K, tile_n, tile_k, lanes, seed)
+CASES = [
+    (F8, 256, 512, 128, 32, 32, 1),       # 32 lanes: two tiles per wave
+    (F8, 384, 256, 128, 64, 64, 2),
+    (F4, 256, 1024, 128, 64, 64, 3),
+    (F4, 128, 384, 128, 64, 32, 4),       # ragged: 6 k-tiles
+    (FE, 512, 448, 256, 64, 64, 5),       # 7 k-tiles: odd count
+    (FE, 256, 256, 128, 32, 32, 6),
+    (FB, 384, 640, 128, 64, 64, 7),
+    (FB, 512, 192, 256, 64, 64, 8),
+    (FB, 256, 4096, 128, 64, 64, 9),      # 64 k-tiles: several workgroups per strip
+]
+
+
+def _layer(fmt, n, k, tn, tk, R, seed, m=16):
+    d = workloads.random_small(fmt, n, k, seed=seed, m=m)
+    blob = dgt.dgt_compress_layer(fmt, d["codes"], tn, tk, R)
+    return d, blob
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES)
+def test_decode_tiles_bit_exact(fmt, n, k, tn, tk, R, seed):
+    import torch
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed)
+    layer = dgt.DeviceLayer(blob)
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    out = dgt.dgt_decode_tiles(layer, status=status)
+    torch.cuda.synchronize()
+    got = decoded_to_numpy(fmt, out)
+    assert np.array_equal(got, codes_as_u8_or_u16(fmt, d["codes"]))
+    assert (status.cpu().numpy() == 0).all()
+    # the oracle's decoder agrees symbol for symbol
+    assert np.array_equal(oblob.decompress_layer(blob), d["codes"])
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES[:4] + CASES[6:7])
+def test_decode_tile_subset(fmt, n, k, tn, tk, R, seed):
+    import torch
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed)
+    layer = dgt.DeviceLayer(blob)
+    tiles = layer.info.tiles
+    ids = [tiles - 1, 0, tiles // 2] if tiles > 2 else [0]
+    out = dgt.dgt_decode_tiles(layer, tile_ids=ids)
+    torch.cuda.synchronize()
+    got = decoded_to_numpy(fmt, out)
+    want = codes_as_u8_or_u16(fmt, d["codes"])
+    kt = k // tk
+    mask = np.zeros((n, k), bool)
+    for t in ids:
+        r0, c0 = (t // kt) * tn, (t % kt) * tk
+        mask[r0:r0 + tn, c0:c0 + tk] = True
+    assert np.array_equal(got[mask], want[mask])
+    assert (got[~mask] == 0).all()
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES)
+@pytest.mark.parametrize("m", [1, 5, 16, 33, 64, 100])
+def test_fused_gemm_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
+    import torch
+    if fmt == F4 and k % 128:
+        pytest.skip("int4 needs K % 128 == 0 for its scale groups")
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"],
+                                  status=status)
+    torch.cuda.synchronize()
+    ref = reference(fmt, d, d["x"])
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+    assert (status.cpu().numpy() == 0).all()
+
+
+def test_fused_gemm_repeatable_and_workspace_reusable():
+    import torch
+    d, blob = _layer(FB, 256, 4096, 128, 64, 64, 21, m=16)
+    layer = dgt.DeviceLayer(blob)
+    x = x_dev(d["x"])
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, 16))
+    y1 = dgt.dgt_fused_decode_gemm(layer, x, ws=ws).clone()
+    y2 = dgt.dgt_fused_decode_gemm(layer, x, ws=ws).clone()
+    y3 = dgt.dgt_fused_decode_gemm(layer, x[:3].contiguous(), ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)               # deterministic reduction order
+    assert torch.equal(y3, y1[:3])           # row results do not depend on M
+    assert int(ws[:256].sum().item()) == 0   # strip counters returned to zero
+
+
+def test_exact_integer_case():
+    """int8 weights and integer activations in [-4, 4]: every fp32 partial sum is
+    an integer below 2^24, so the device result must equal the oracle exactly."""
+    import torch
+    rng = np.random.default_rng(3)
+    d = workloads.random_small(F8, 512, 1024, seed=31)
+    xi = rng.integers(-4, 5, (16, 1024)).astype(np.float32)
+    xb = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    blob = dgt.dgt_compress_layer(F8, d["codes"], 128, 32, 32)
+    y = dgt.dgt_fused_decode_gemm(dgt.DeviceLayer(blob), x_dev(xb))
+    torch.cuda.synchronize()
+    ref = ogemm.gemm_fp64(xi.astype(np.float64), d["codes"].astype(np.float64))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256)])
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_dense_baseline_matches_oracle(fmt, tn, m):
+    import torch
+    n, k = 512, 1024
+    d = workloads.random_small(fmt, n, k, seed=40 + fmt, m=m)
+    w = to_dev(codes_as_u8_or_u16(fmt, d["codes"]))
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    y = dgt.dgt_dense_gemm(fmt, w, x_dev(d["x"]), tile_n=tn, scales=scales,
+                           w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
+
+
+def test_corrupt_stream_sets_status_and_stays_in_bounds():
+    """Bytes flipped inside tile word streams (the index untouched): the
+    kernel's clamps keep every access in bounds and the tile status reports it."""
+    import torch
+    d, blob = _layer(F8, 256, 512, 128, 64, 64, 51)
+    info = dgt.dgt_layer_info(blob)
+    h = oblob.parse(blob)
+    b = bytearray(blob)
+    bad_tiles = [1, 5]
+    for t in bad_tiles:
+        start = info.streams_off + 4 * int(h["index"][t]) + 4 * info.lanes
+        for j in range(6):
+            b[start + 2 * j] ^= 0xA5
+    layer = dgt.DeviceLayer(bytes(b))
+    status = torch.full((info.tiles,), -1, dtype=torch.int32, device="cuda")
+    dgt.dgt_decode_tiles(layer, status=status)
+    torch.cuda.synchronize()
+    st = status.cpu().numpy()
+    assert all(st[t] != 0 for t in bad_tiles)
+    assert all(st[t] == 0 for t in range(info.tiles) if t not in bad_tiles)
+
+
+def test_argument_errors():
+    d, blob = _layer(F8, 256, 512, 128, 64, 64, 61)
+    layer = dgt.DeviceLayer(blob)
+    x = x_dev(d["x"])
+    with pytest.raises(dgt.DgtError) as e:
+        dgt.dgt_fused_decode_gemm(layer, x, ws=dgt.alloc_workspace(256)[:0])
+    assert e.value.code in (-1, -4)
+    import torch
+    big = torch.zeros((257, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dgt.DgtError) as e:
+        dgt.dgt_fused_decode_gemm(layer, big)
+    assert e.value.code == -1

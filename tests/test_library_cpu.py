@@ -1,0 +1,121 @@
+"""Host-side checks of libdgt (no GPU): the C-ABI library loads and exports
+every symbol include/dgt.h declares; the C++ encoder writes byte for byte the
+blob the oracle writes; dgt_layer_info validates like the oracle's parser."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_gemm_tile_amd as dgt
+import workloads
+from oracle import blob as oblob
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "dgt.h")).read()
+    return sorted(set(re.findall(r"\b(dgt_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dgt.lib()
+    declared = _header_symbols()
+    assert set(declared) == set(dgt.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert dgt.dgt_version() == 1
+    assert dgt.dgt_status_string(0) == "ok"
+    assert "corrupt" in dgt.dgt_status_string(-6)
+
+
+CASES = [
+    (dgt.DGT_FMT_INT8, 256, 64, 128, 32, 32, 1),
+    (dgt.DGT_FMT_INT8, 128, 128, 128, 64, 64, 2),
+    (dgt.DGT_FMT_INT4, 256, 256, 128, 64, 64, 3),
+    (dgt.DGT_FMT_INT4, 128, 256, 128, 64, 32, 4),
+    (dgt.DGT_FMT_FP8_E4M3, 512, 128, 256, 64, 64, 5),
+    (dgt.DGT_FMT_BF16_SPLIT, 256, 128, 128, 64, 64, 6),
+    (dgt.DGT_FMT_BF16_SPLIT, 32, 16, 16, 8, 16, 7),
+    (dgt.DGT_FMT_BF16_SPLIT, 256, 64, 256, 32, 64, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES)
+def test_cpp_encoder_matches_oracle_bytes(fmt, n, k, tn, tk, R, seed):
+    d = workloads.random_small(fmt, n, k, seed=seed)
+    ours = dgt.dgt_compress_layer(fmt, d["codes"], tn, tk, R)
+    ref = oblob.compress_layer(fmt, d["codes"], tn, tk, R)
+    assert len(ours) == len(ref)
+    assert ours == ref
+    info = dgt.dgt_layer_info(ours)
+    h = oblob.parse(ref)
+    for key in ("n", "k", "tile_n", "tile_k", "lanes", "prob_bits", "alphabet", "tiles",
+                "table_off", "index_off", "ktab_off", "streams_off", "raw_off", "kmax",
+                "max_tile_words4"):
+        assert getattr(info, key) == h[key], key
+    assert info.total_bytes == len(ref)
+    assert info.bits_per_weight == pytest.approx(8 * len(ref) / (n * k))
+
+
+def test_cpp_encoder_matches_oracle_on_small_workloads():
+    for name in ("int8_1024", "int4_4096"):
+        d = workloads.make(name)
+        wl = d["workload"]
+        ours = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+        ref = oblob.compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+        assert ours == ref, name
+
+
+def test_cpp_encoder_special_tables():
+    # constant layer (one symbol: f = 4096), two-symbol layer with f = 1
+    for codes in (np.full((128, 64), 3, np.uint8),
+                  np.where(np.arange(128 * 64).reshape(128, 64) == 77, 1, 0).astype(np.uint8)):
+        ours = dgt.dgt_compress_layer(dgt.DGT_FMT_INT4, codes, 128, 64, 64)
+        ref = oblob.compress_layer(oblob.FMT_INT4, codes, 128, 64, 64)
+        assert ours == ref
+        assert np.array_equal(oblob.decompress_layer(ours), codes)
+
+
+def test_compress_errors():
+    w = np.zeros((100, 64), np.uint8)
+    with pytest.raises(dgt.DgtError) as e:
+        dgt.dgt_compress_layer(dgt.DGT_FMT_INT8, w, 128, 64, 64)
+    assert e.value.code == -2
+    bad = np.full((128, 64), 16, np.uint8)
+    with pytest.raises(dgt.DgtError) as e:
+        dgt.dgt_compress_layer(dgt.DGT_FMT_INT4, bad, 128, 64, 64)
+    assert e.value.code == -3
+    assert dgt.dgt_compress_bound(9, 128, 64, 128, 64, 64) == 0
+    assert dgt.dgt_compress_bound(1, 128, 64, 128, 64, 48) == 0
+
+
+def test_layer_info_rejects_corruption():
+    d = workloads.random_small(dgt.DGT_FMT_INT8, 256, 64, seed=11)
+    b = bytearray(dgt.dgt_compress_layer(dgt.DGT_FMT_INT8, d["codes"], 128, 32, 32))
+    info = dgt.dgt_layer_info(bytes(b))
+    cases = []
+    c = bytearray(b); c[0] ^= 1; cases.append((c, -5))                       # magic
+    c = bytearray(b); cases.append((c[:-4], -6))                            # truncated
+    c = bytearray(b); c[info.table_off] ^= 1; cases.append((c, -6))         # table sum
+    c = bytearray(b); io = info.index_off
+    c[io + 4:io + 8] = (0).to_bytes(4, "little"); cases.append((c, -6))     # index order
+    c = bytearray(b); c[info.ktab_off] = 200; cases.append((c, -6))         # ktab range
+    c = bytearray(b); c[8] = 7; cases.append((c, -5))                       # format id
+    for blob, code in cases:
+        with pytest.raises(dgt.DgtError) as e:
+            dgt.dgt_layer_info(bytes(blob))
+        assert e.value.code == code
+
+
+def test_device_calls_need_a_gpu_or_fail_loudly():
+    """Without a GPU the device entry points must error, never fall back to CPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    d = workloads.random_small(dgt.DGT_FMT_INT8, 128, 64, seed=12)
+    b = dgt.dgt_compress_layer(dgt.DGT_FMT_INT8, d["codes"], 128, 32, 32)
+    with pytest.raises(Exception):
+        dgt.DeviceLayer(b, "cuda")
