@@ -22,7 +22,7 @@ namespace dev {
 // sx = fl32(amax / 448), xq = e4m3_rne_satfinite(fl32(x * inv)).
 struct QuantArgs {
   const uint16_t* x;
-  uint8_t* xq;
+  uint16_t* xq;          // bf16 bits of the e4m3 value (exact: e4m3 is a subset of bf16)
   uint32_t* amax_bits;   // workspace: running max of |x| as fp32 bits
   uint32_t* done;        // workspace: finished-block counter
   float* sx;             // workspace: activation scale
@@ -60,6 +60,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | mag;
 }
 
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, man = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (man << 20))  // 2^(e-7) * 1.m
+                      : (float)man * 0.001953125f;                       // m * 2^-9
+  const uint32_t bits = __float_as_uint(mag) | ((c & 0x80u) << 24);
+  return (uint16_t)(bits >> 16);
+}
+
 __global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
   const float amax = __uint_as_float(*q.amax_bits);
   float inv = 1.f, sx = 1.f;
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
   }
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < q.count; i += gridDim.x * blockDim.x) {
     const float v = __uint_as_float((uint32_t)q.x[i] << 16);
-    q.xq[i] = zero ? 0 : (uint8_t)f32_to_e4m3(v * inv);
+    q.xq[i] = zero ? (uint16_t)0 : e4m3_to_bf16(f32_to_e4m3(v * inv));
   }
   __shared__ bool last;
   __threadfence();
@@ -161,16 +169,16 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->part_bytes = p->gps > 1 ? (size_t)p->strips * p->gps * p->m_chunk * in->tile_n * 4 : 0;
   off = dgt::align_up(off + p->part_bytes, 256);
   p->quant_off = off;
-  if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k, 256) + 256;
+  if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
   p->ws_bytes = off;
   return true;
 }
 
 int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t st,
-                 uint8_t** xq, float** sx) {
+                 uint16_t** xq, float** sx) {
   QuantArgs q;
   q.x = d_x;
-  q.xq = ws_q + 256;
+  q.xq = reinterpret_cast<uint16_t*>(ws_q + 256);
   q.amax_bits = reinterpret_cast<uint32_t*>(ws_q);
   q.done = reinterpret_cast<uint32_t*>(ws_q + 4);
   q.sx = reinterpret_cast<float*>(ws_q + 8);
@@ -219,12 +227,11 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
   uint32_t xrow = info->k * 2;
   const float* sxp = nullptr;
   if (info->fmt == DGT_FMT_FP8_E4M3) {
-    uint8_t* xq = nullptr;
+    uint16_t* xq = nullptr;
     float* sx = nullptr;
     rc = launch_quant(d_x, m * info->k, ws + p.quant_off, st, &xq, &sx);
     if (rc) return rc;
-    xsrc = xq;
-    xrow = info->k;
+    xsrc = reinterpret_cast<const uint8_t*>(xq);
     sxp = sx;
   }
   for (uint32_t m0 = 0; m0 < m; m0 += p.m_chunk) {
@@ -311,7 +318,7 @@ size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n
   size_t off = dgt::align_up((size_t)strips * 4, 256);
   if (gps > 1) off += (size_t)strips * gps * mc * tile_n * 4;
   off = dgt::align_up(off, 256);
-  if (fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * k, 256) + 256;
+  if (fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * k * 2, 256) + 256;
   return off;
 }
 
@@ -338,12 +345,11 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
   uint32_t xrow = k * 2;
   const float* sxp = nullptr;
   if (fmt == DGT_FMT_FP8_E4M3) {
-    uint8_t* xq = nullptr;
+    uint16_t* xq = nullptr;
     float* sx = nullptr;
     int rc = launch_quant(d_x, m * k, ws + quant_off, st, &xq, &sx);
     if (rc) return rc;
-    xsrc = xq;
-    xrow = k;
+    xsrc = reinterpret_cast<const uint8_t*>(xq);
     sxp = sx;
   }
   const uint32_t lds = 64 * 1024;
@@ -373,7 +379,7 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     d.k = k;
     d.kt = kt;
     const uint32_t grid = strips * gps;
-int rc = DGT_E_UNSUPPORTED;
+    int rc = DGT_E_UNSUPPORTED;
     const uint32_t fnv = tile_n / 16;
     switch (fmt) {
       case DGT_FMT_INT8: rc = launch_dense<INT8>(d, fnv, mt, grid, 64 * waves, lds, st); break;
@@ -383,7 +389,6 @@ int rc = DGT_E_UNSUPPORTED;
       default: break;
     }
     if (rc) return rc;
-    return DGT_E_UNSUPPORTED;
   }
   return DGT_OK;
 }

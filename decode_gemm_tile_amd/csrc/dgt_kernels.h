@@ -27,7 +27,7 @@ namespace dev {
 // ------------------------------------------------------------ kernel params
 struct GemmArgs {
   Layer L;
-  const uint8_t* x;          // bf16 bits [M, K] (or e4m3 bytes [M, K] for FP8)
+  const uint8_t* x;          // bf16 bits [M, K] (FP8: the quantised X as exact bf16)
   const uint16_t* scales;    // INT4: bf16 bits [N, K/128]
   const float* xscale;       // FP8: device sx (per-tensor activation scale)
   float w_scale;             // FP8 weight scale
@@ -53,7 +53,7 @@ struct OperandTraits<INT4> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
 template <>
-struct OperandTraits<FP8> { static constexpr int xbytes = 1; };
+struct OperandTraits<FP8> { static constexpr int xbytes = 2; };  // e4m3 widened to bf16
 
 // B operand of one fragment from 8 decoded LUT words (+ raw bytes / scales).
 struct BOp {
@@ -95,25 +95,27 @@ __device__ __forceinline__ BOp make_b(const uint32_t (&e)[8], u32x2 raw, float s
       o[i] = __builtin_bit_cast(uint32_t, h);
     }
     b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
-  } else {  // FP8: bytes
-    b.v.x = pack_hi_bytes(e[1], e[0]) | (pack_hi_bytes(e[3], e[2]) << 16);
-    b.v.y = pack_hi_bytes(e[5], e[4]) | (pack_hi_bytes(e[7], e[6]) << 16);
-    b.v.z = 0; b.v.w = 0;
+  } else {  // FP8: e4m3 bytes widened exactly to bf16 (e4m3 is a subset of bf16)
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pair = __builtin_amdgcn_perm(e[2 * i + 1], e[2 * i], 0x07030c0cu);
+      const floatx2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)pair, true);
+      o[i] = __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+    }
+    b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
   }
   return b;
 }
 
+// All formats multiply on the bf16 matrix cores with fp32 accumulation.  The
+// fp8 x fp8 matrix instructions sum each 32-term dot product with only about
+// 16 bits relative to the sum of |products|, short of a 1e-5 output bound, so
+// e4m3 operands are widened (exactly) to bf16 instead.
 template <int FMT>
 __device__ __forceinline__ floatx4 mfma(const u32x4& a, const BOp& b, floatx4 acc) {
-  if constexpr (FMT == FP8) {
-    const long av = (long)(((uint64_t)a.y << 32) | a.x);
-    const long bv = (long)(((uint64_t)b.v.y << 32) | b.v.x);
-    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, acc, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b.v), acc, 0,
-                                                   0, 0);
-  }
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
 }
 
 // A operand (X) for lane l: row m, 8 consecutive k starting at k0.
@@ -122,12 +124,7 @@ __device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t 
   u32x4 r = {0u, 0u, 0u, 0u};
   if (m < a.m) {
     const uint8_t* p = a.x + (size_t)m * a.x_row_bytes + (size_t)k0 * OperandTraits<FMT>::xbytes;
-    if constexpr (FMT == FP8) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-      r.x = v.x; r.y = v.y;
-    } else {
-      r = *reinterpret_cast<const u32x4*>(p);
-    }
+    r = *reinterpret_cast<const u32x4*>(p);
   }
   return r;
 }
