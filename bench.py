@@ -1,0 +1,250 @@
+"""Benchmark of the fused rANS-decode GEMM on one MI355X.
+
+One step = one pass of the hot path over one batch: dgt_fused_decode_gemm on a
+resident compressed layer (LUT prologue, tile fetch, on-chip rANS decode,
+matrix-core product, split-K reduction and epilogue), here on the Llama-3-8B
+MLP projection shape W 14336x4096 stored as bf16 with its high byte coded
+(workload "bf16_mlp"), X of M = 1 row.  Several copies of the blob rotate so
+the 256 MB last-level cache cannot hold the working set.
+
+Prints ONE JSON line: metric, value (decoded-weight GB/s at M = 1), roofline of
+the fused kernel (HBM bytes it must read / kernel time), the CPU oracle timed on
+the host cores, and secondary figures (bits/weight, TFLOP/s at M = 256, the
+uncompressed baseline).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+ROTATE_BYTES = 512 << 20     # working set above the 256 MB last-level cache
+METRIC = "fused rANS-decode GEMM decoded-weight GB/s at M=1; TFLOP/s at M=256; bits/wt"
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="bf16_mlp")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="time only the M=1 fused kernel (for profiler runs)")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run one plain device copy of 512 MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: profile figures are valid only for this code."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "decode_gemm_tile_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_prefix: str, workload: str, per_launch_ref: float):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source hash:\s*`?([0-9a-f]{16})", text)
+    m_val = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def cpu_baseline(d, wl, blob):
+    """The CPU oracle (decode of the compressed layer + fp64 GEMV), timed on the
+    host on a bounded sample of the layer: every tile of the first strips."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import blob as oblob
+    from oracle import gemm as ogemm
+    from oracle import numerics
+    h = oblob.parse(blob)
+    kt = wl.k // wl.tile_k
+    strips = wl.n // wl.tile_n
+    tiles = list(range(strips * kt))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        syms = oblob.decode_symbols(blob, tiles)
+        raw = np.frombuffer(blob, np.uint8, len(tiles) * wl.tile_n * wl.tile_k,
+                            h["raw_off"]).reshape(len(tiles), -1)
+        from oracle import order
+        rows = strips * wl.tile_n
+        hi = order.scatter_tiles(syms.astype(np.uint8), rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes)
+        lo = order.scatter_tiles(raw, rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes, raw=True)
+        w = (hi.astype(np.uint16) << 8) | lo
+        y = ogemm.gemm_fp64(numerics.bf16_bits_to_f64(d["x"][:1]), numerics.bf16_bits_to_f64(w))
+        dt = time.perf_counter() - t0
+    assert np.array_equal(w, d["codes"][:rows])
+    weights = rows * wl.k
+    return {"value": round(weights * 2 / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of %d tiles (rows 0..%d, all K), decode + fp64 GEMV, %.1f s, "
+                      "1 thread (numpy, BLAS limited to 1)" % (len(tiles), wl.n // wl.tile_n * kt,
+                                                               rows - 1, dt),
+            "seconds": round(dt, 3), "checksum": float(np.abs(y).sum())}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
+              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_gemm_tile_amd as dgt
+    import workloads
+    from oracle import entropy as oentropy
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    wl = workloads.WORKLOADS[args.workload]
+    d = workloads.make(args.workload)
+    t0 = time.perf_counter()
+    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    encode_s = time.perf_counter() - t0
+    info = dgt.dgt_layer_info(blob)
+    sym = (np.asarray(d["codes"]) >> 8).astype(np.uint8) if wl.fmt == 4 else None
+    h_hi = oentropy.empirical_entropy(sym, 256) if sym is not None else None
+
+    copies = max(2, math.ceil(ROTATE_BYTES / len(blob)))
+    layers = [dgt.DeviceLayer(blob, dev) for _ in range(copies)]
+    xall = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    scales = (torch.from_numpy(d["scales"].view(np.int16)).to(dev)
+              if d["scales"] is not None else None)
+
+    # ---- headline: fused kernel at M = 1
+    m = 1
+    x1 = xall[:m].contiguous()
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layers[0], m), dev)
+    y = torch.empty((m, wl.n), dtype=torch.float32, device=dev)
+
+    def fused(i, x=x1, y=y, ws=ws):
+        dgt.dgt_fused_decode_gemm(layers[i % copies], x, scales=scales, w_scale=d["w_scale"],
+                                  y=y, ws=ws, stream=stream)
+
+    ms = timed(fused, args.steps, args.warmup, stream)
+    nk = wl.n * wl.k
+    decoded_bytes = nk * 2
+    value = decoded_bytes / (ms * 1e-3) / 1e9
+    alg_bytes = len(blob) + m * wl.k * 2 + m * wl.n * 4
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("k_fused", args.workload, alg_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: W %dx%d bf16 N(0,0.02) byte split, tiles %dx%d, R=%d, M=%d"
+                               % (args.workload, wl.n, wl.k, wl.tile_n, wl.tile_k, wl.lanes, m),
+                   "m": m, "n": wl.n, "k": wl.k, "blob_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes": alg_bytes,
+                     "source_hash": source_hash()},
+    }
+
+    secondary = {"bits_per_weight": round(info.bits_per_weight, 4),
+                 "compressed_bytes": len(blob), "encode_seconds": round(encode_s, 3)}
+    if h_hi is not None:
+        secondary["entropy_hi_byte_bits"] = round(h_hi, 4)
+        secondary["bits_over_entropy"] = round(info.bits_per_weight - (h_hi + 8.0), 4)
+    if not args.no_secondary:
+        # fused at M = 256 (TFLOP/s) and the uncompressed baseline at M = 1 and 256
+        m2 = 256
+        x2 = xall[:m2].contiguous()
+        ws2 = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layers[0], m2), dev)
+        y2 = torch.empty((m2, wl.n), dtype=torch.float32, device=dev)
+        ms2 = timed(lambda i: dgt.dgt_fused_decode_gemm(layers[i % copies], x2, scales=scales,
+                                                        w_scale=d["w_scale"], y=y2, ws=ws2,
+                                                        stream=stream),
+                    max(5, args.steps // 10), 3, stream)
+        flops = 2.0 * m2 * nk
+        secondary["fused_m256_ms"] = round(ms2, 4)
+        secondary["fused_m256_tflops"] = round(flops / (ms2 * 1e-3) / 1e12, 3)
+        secondary["fused_m256_mfma_frac"] = round(flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        wraw = torch.from_numpy(np.asarray(d["codes"]).view(np.int16)).to(dev)
+        dcopies = max(2, math.ceil(ROTATE_BYTES / (nk * 2)))
+        wd = [wraw.clone() for _ in range(dcopies)]
+        del wraw
+        for mm in (1, 256):
+            xm = xall[:mm].contiguous()
+            wsd = dgt.alloc_workspace(dgt.dgt_dense_workspace(wl.fmt, wl.n, wl.k, wl.tile_n, mm), dev)
+            yd = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
+            msd = timed(lambda i: dgt.dgt_dense_gemm(wl.fmt, wd[i % dcopies], xm,
+                                                     tile_n=wl.tile_n, scales=scales,
+                                                     w_scale=d["w_scale"], y=yd, ws=wsd,
+                                                     stream=stream),
+                        max(5, args.steps // 10), 3, stream)
+            secondary["dense_m%d_ms" % mm] = round(msd, 4)
+            if mm == 1:
+                secondary["dense_m1_weight_gbs"] = round(nk * 2 / (msd * 1e-3) / 1e9, 3)
+                secondary["fused_speedup_vs_dense_m1"] = round(msd / ms, 3)
+            else:
+                secondary["dense_m256_tflops"] = round(2.0 * mm * nk / (msd * 1e-3) / 1e12, 3)
+        del wd
+    result["secondary"] = secondary
+
+    if args.copy_calib:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = a.numel()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, wl, blob)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

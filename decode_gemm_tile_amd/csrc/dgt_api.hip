@@ -3,9 +3,11 @@
 //
 // Planner (the static tile schedule of "arXiv'26 | 无损压缩逼近 Shannon 极限" §3.1,
 // fixed at launch, no run-time bookkeeping): Y is cut into strips of tile_n
-// columns; the k-tiles of a strip are dealt to waves in order (ILP chains per
-// wave), consecutive waves share a workgroup, and a strip spans `gps`
-// workgroups whose partials meet in the workspace.
+// columns; a unit is ILP chains of consecutive k-tiles of one strip; units are
+// numbered strip-major and dealt to workgroups in equal contiguous runs of W
+// (one wave per unit), W chosen so the layer fills the CUs in as few rounds as
+// registers and LDS allow.  Strips shared by several workgroups meet in the
+// workspace (per-strip slots and counters).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -69,7 +71,8 @@ __device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
 }
 
 __global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
-  const float amax = __uint_as_float(*q.amax_bits);
+  const float amax = __uint_as_float(
+      __hip_atomic_load(q.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   float inv = 1.f, sx = 1.f;
   const bool zero = !(amax > 0.f) || amax > 3.4e38f;
   if (!zero) {
@@ -81,14 +84,16 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
     q.xq[i] = zero ? (uint16_t)0 : e4m3_to_bf16(f32_to_e4m3(v * inv));
   }
   __shared__ bool last;
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(q.done, 1u) == gridDim.x - 1;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(q.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x - 1;
   __syncthreads();
   if (last && threadIdx.x == 0) {
-    *q.sx = sx;
-    *q.amax_bits = 0u;  // ready for the next call
-    *q.done = 0u;
+    // every block has read amax by now; reset it for the next call
+    __hip_atomic_store(q.sx, sx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q.amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -131,9 +136,19 @@ int device_supported(const dgt_info* in) {
 }
 
 struct FusedPlan {
-  uint32_t mt, ilp, waves, tpw, gps, strips, red_cols, lds, m_chunk;
+  uint32_t mt, ilp, waves, threads, tpw, ups, units, wgs, slots, strips, red_cols, lds, m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
 };
+
+constexpr uint32_t kCUs = 256;
+
+// Units per workgroup so that the layer fills the CUs in as few rounds as the
+// wave cap allows; a workgroup never spans more than two strips (W <= ups).
+uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
+  uint32_t w = (units + kCUs - 1) / kCUs;
+  w = std::min(std::max(w, 1u), cap);
+  return std::min(w, ups);
+}
 
 bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   const uint32_t R = in->lanes, tpc = 64 / R;
@@ -143,20 +158,24 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->mt = p->m_chunk <= 16 ? 1 : 4;
   p->strips = in->n / in->tile_n;
   const uint32_t chains_total = in->tiles / tpc;
-  p->ilp = (kt % (2 * tpc) == 0 && chains_total >= 1024 * 6) ? 2 : 1;
+  p->ilp = (kt % (2 * tpc) == 0 && chains_total >= kCUs * 4 * 5) ? 2 : 1;
   if (kt % (p->ilp * tpc)) return false;
   p->tpw = p->ilp * tpc;
+  p->ups = kt / p->tpw;
+  p->units = p->strips * p->ups;
   const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
   const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
-  const uint32_t waves_per_strip = kt / p->tpw;
-  p->waves = 8;
-  auto lds_for = [&](uint32_t w) { return kLutBytes + kCumBytes + w * p->ilp * tpc * region_bytes; };
-  while (p->waves > 4 && lds_for(p->waves) > kMaxLds) p->waves /= 2;
-  // small layers: fewer waves per workgroup spread the strip over more CUs
-  if (p->waves == 8 && (uint64_t)p->strips * ((waves_per_strip + 7) / 8) < 512) p->waves = 4;
-  if (lds_for(p->waves) > kMaxLds) return false;
-  p->gps = (waves_per_strip + p->waves - 1) / p->waves;
-  p->lds = lds_for(p->waves);
+  const uint32_t per_wave = p->ilp * tpc * region_bytes;
+  if (kLutBytes + kCumBytes + per_wave > kMaxLds) return false;
+  const uint32_t lds_cap = (kMaxLds - kLutBytes - kCumBytes) / per_wave;
+  const uint32_t fn = in->tile_n / 16;
+  const uint32_t reg_cap =
+      fused_max_threads(R, fn == 8 ? 8 : 16, p->mt, p->ilp) / 64;  // VGPR budget per lane
+  p->waves = pick_waves(p->units, p->ups, std::min(lds_cap, reg_cap));
+  p->threads = 64 * std::max(p->waves, 4u);       // the LUT build uses >= 4 waves
+  p->wgs = (p->units + p->waves - 1) / p->waves;
+  p->slots = (p->ups + p->waves - 1) / p->waves + 1;
+  p->lds = kLutBytes + kCumBytes + (p->threads / 64) * per_wave;
   uint32_t rc = in->tile_n;
   while (rc > 16 && (uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) rc /= 2;
   if ((uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) {
@@ -166,7 +185,7 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->red_cols = rc;
   size_t off = dgt::align_up((size_t)p->strips * 4, 256);
   p->part_off = off;
-  p->part_bytes = p->gps > 1 ? (size_t)p->strips * p->gps * p->m_chunk * in->tile_n * 4 : 0;
+  p->part_bytes = (size_t)p->strips * p->slots * p->m_chunk * in->tile_n * 4;
   off = dgt::align_up(off + p->part_bytes, 256);
   p->quant_off = off;
   if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
@@ -225,7 +244,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
   uint8_t* ws = static_cast<uint8_t*>(d_ws);
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
   uint32_t xrow = info->k * 2;
-  const float* sxp = nullptr;
+  float* sxp = nullptr;
   if (info->fmt == DGT_FMT_FP8_E4M3) {
     uint16_t* xq = nullptr;
     float* sx = nullptr;
@@ -250,9 +269,11 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     a.y_row = info->n;
     a.waves = p.waves;
     a.tpw = p.tpw;
-    a.gps = p.gps;
+    a.units = p.units;
+    a.ups = p.ups;
+    a.slots = p.slots;
     a.red_cols = p.red_cols;
-    const uint32_t grid = p.strips * p.gps, threads = 64 * p.waves;
+    const uint32_t grid = p.wgs, threads = p.threads;
     switch (info->fmt) {
       case DGT_FMT_INT8:
         rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
@@ -310,16 +331,37 @@ switch (info->fmt) {
   return DGT_E_UNSUPPORTED;
 }
 
-size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, uint32_t m) {
-  if (m == 0 || (tile_n != 128 && tile_n != 256) || n % tile_n || k % 64) return 0;
-  const uint32_t strips = n / tile_n, kt = k / 64, tpw = 2, waves = 8;
-  const uint32_t gps = (kt / tpw + waves - 1) / waves;
-  const uint32_t mc = std::min<uint32_t>(m, tile_n == 256 ? 16 : 64);
-  size_t off = dgt::align_up((size_t)strips * 4, 256);
-  if (gps > 1) off += (size_t)strips * gps * mc * tile_n * 4;
+namespace {
+struct DensePlan {
+  uint32_t strips, kt, tpw, ups, units, waves, wgs, slots, mc, mt;
+  size_t part_off, quant_off, ws_bytes;
+};
+bool plan_dense(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, uint32_t m, DensePlan* p) {
+  if (m == 0 || (tile_n != 128 && tile_n != 256) || n % tile_n || k % 128) return false;
+  p->strips = n / tile_n;
+  p->kt = k / 64;
+  p->tpw = 2;
+  p->ups = p->kt / p->tpw;
+  p->units = p->strips * p->ups;
+  p->mc = std::min<uint32_t>(m, tile_n == 256 ? 16 : 64);
+  p->mt = p->mc <= 16 ? 1 : 4;
+  p->waves = pick_waves(p->units, p->ups, dense_max_threads(tile_n / 16, p->mt) / 64);
+  p->wgs = (p->units + p->waves - 1) / p->waves;
+  p->slots = (p->ups + p->waves - 1) / p->waves + 1;
+  size_t off = dgt::align_up((size_t)p->strips * 4, 256);
+  p->part_off = off;
+  off += (size_t)p->strips * p->slots * p->mc * tile_n * 4;
   off = dgt::align_up(off, 256);
+  p->quant_off = off;
   if (fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * k * 2, 256) + 256;
-  return off;
+  p->ws_bytes = off;
+  return true;
+}
+}  // namespace
+
+size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, uint32_t m) {
+  DensePlan p;
+  return plan_dense(fmt, n, k, tile_n, m, &p) ? p.ws_bytes : 0;
 }
 
 int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const void* d_w,
@@ -332,18 +374,16 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
   if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;
   if (((uintptr_t)d_w & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
     return DGT_E_ARG;
-  const size_t need = dgt_dense_workspace(fmt, n, k, tile_n, m);
-  if (ws_bytes < need) return DGT_E_BUFSIZE;
-  const uint32_t strips = n / tile_n, kt = k / 64, tpw = 2, waves = 8;
-  const uint32_t gps = (kt / tpw + waves - 1) / waves;
-  const uint32_t mc = std::min<uint32_t>(m, tile_n == 256 ? 16 : 64), mt = mc <= 16 ? 1 : 4;
+  DensePlan p;
+  if (!plan_dense(fmt, n, k, tile_n, m, &p)) return DGT_E_SHAPE;
+  if (ws_bytes < p.ws_bytes) return DGT_E_BUFSIZE;
+  const uint32_t mc = p.mc, mt = p.mt, waves = p.waves;
   uint8_t* ws = static_cast<uint8_t*>(d_ws);
-  size_t part_off = dgt::align_up((size_t)strips * 4, 256);
-  size_t quant_off = dgt::align_up(part_off + (gps > 1 ? (size_t)strips * gps * mc * tile_n * 4 : 0), 256);
+  const size_t part_off = p.part_off, quant_off = p.quant_off;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
   uint32_t xrow = k * 2;
-  const float* sxp = nullptr;
+  float* sxp = nullptr;
   if (fmt == DGT_FMT_FP8_E4M3) {
     uint16_t* xq = nullptr;
     float* sx = nullptr;
@@ -369,23 +409,27 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     a.x_row_bytes = xrow;
     a.y_row = n;
     a.waves = waves;
-    a.tpw = tpw;
-    a.gps = gps;
+    a.tpw = p.tpw;
+    a.units = p.units;
+    a.ups = p.ups;
+    a.slots = p.slots;
     uint32_t rc_cols = tile_n;
     while (rc_cols > 16 && (uint64_t)waves * a.m * rc_cols * 4 > lds) rc_cols /= 2;
     a.red_cols = rc_cols;
     d.w = static_cast<const uint8_t*>(d_w);
     d.n = n;
     d.k = k;
-    d.kt = kt;
-    const uint32_t grid = strips * gps;
+    d.kt = p.kt;
+    const uint32_t grid = p.wgs;
     int rc = DGT_E_UNSUPPORTED;
     const uint32_t fnv = tile_n / 16;
     switch (fmt) {
       case DGT_FMT_INT8: rc = launch_dense<INT8>(d, fnv, mt, grid, 64 * waves, lds, st); break;
       case DGT_FMT_INT4: rc = launch_dense<INT4>(d, fnv, mt, grid, 64 * waves, lds, st); break;
       case DGT_FMT_FP8_E4M3: rc = launch_dense<FP8>(d, fnv, mt, grid, 64 * waves, lds, st); break;
-      case DGT_FMT_BF16_SPLIT: rc = launch_dense<BF16>(d, fnv, mt, grid, 64 * waves, lds, st); break;
+      case DGT_FMT_BF16_SPLIT:
+        rc = launch_dense<BF16>(d, fnv, mt, grid, 64 * waves, lds, st);
+        break;
       default: break;
     }
     if (rc) return rc;

@@ -101,75 +101,86 @@ __device__ inline void build_lut(const uint16_t* table, uint32_t alphabet, u32x2
 struct Chain {
   uint32_t x;      // lane state
   uint32_t lim;    // first payload step of the lane's tile (steps - k)
-  uint32_t p0;     // uniform: next word of tile A (u16 index into the LDS word array)
-  uint32_t p1;     // uniform: next word of tile B (R = 32)
+  uint32_t p0;     // uniform: words of tile A consumed so far + s0 (not clamped)
+  uint32_t p1;     // uniform: same for tile B (R = 32)
   uint32_t e0;     // uniform: end of tile A's staged words
   uint32_t e1;     // uniform: end of tile B's staged words
-  uint32_t s0;     // uniform: start of tile A's words
+  uint32_t s0;     // uniform: start of tile A's words (u16 index into the LDS word array)
   uint32_t s1;     // uniform: start of tile B's words
-  uint32_t ovf;    // uniform: bit 0 / bit 1 -> tile A / B read past its stream
 };
 
-// One rANS decode step on every lane of a chain; returns the LUT word whose top
-// byte is the decoded symbol.  CAREFUL handles the switch to the payload state
-// (x -= L at step == lim) and suppresses renormalisation from then on.
-template <int R, bool CAREFUL>
-__device__ __forceinline__ uint32_t step(Chain& c, const u32x2* __restrict__ lut,
+// ILP chains advance one rANS step together, in three phases so that their
+// LDS round trips overlap: (1) table reads for every chain, (2) state update,
+// wave ballot of the lanes that renormalise, word reads for every chain,
+// (3) merge.  Branch-free: every lane reads a word (in bounds: a pointer is
+// clamped to its stream end and the region has kSlackWords of slack) and
+// keeps it only if it renormalises.  The word of lane p is the next unread
+// one plus the number of renormalising lanes below p (mbcnt of the ballot).
+// CAREFUL also handles the payload switch (x -= L at step == lim, no reads
+// from then on).  Returns the table words (decoded symbol in the top byte).
+template <int R, bool CAREFUL, int ILP>
+__device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
                                          const uint16_t* __restrict__ words, uint32_t s,
-                                         bool upper_half) {
-  uint32_t x = c.x;
-  if (CAREFUL) x = (s == c.lim) ? x - kL : x;
-  const u32x2 e = lut[x & (kSlots - 1)];
-  uint32_t xn = (e.x & 0xFFFFFFu) * (x >> 12) + e.y;  // v_mad_u32_u24
-  bool need = xn < kL;
-  if (CAREFUL) need = need && (s < c.lim);
-  const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-  const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-  uint32_t idx;
-  if (R == 64) {
-    idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, c.p0));
-    uint32_t np = c.p0 + (uint32_t)__builtin_popcountll(m);
-    if (np > c.e0) { c.ovf |= 1u; np = c.e0; }
-    c.p0 = np;
-  } else {
-    const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
-    const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
-    const uint32_t base = upper_half ? c.p1 - pl : c.p0;
-    idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, base));
-    uint32_t n0 = c.p0 + pl, n1 = c.p1 + ph;
-    if (n0 > c.e0) { c.ovf |= 1u; n0 = c.e0; }
-    if (n1 > c.e1) { c.ovf |= 2u; n1 = c.e1; }
-    c.p0 = n0;
-    c.p1 = n1;
+                                         bool upper_half, uint32_t (&sym)[ILP]) {
+  uint32_t x[ILP];
+  u32x2 e[ILP];
+#pragma unroll
+  for (int i = 0; i < ILP; ++i) {
+    x[i] = c[i].x;
+    if (CAREFUL) x[i] = (s == c[i].lim) ? x[i] - kL : x[i];
+    e[i] = lut[x[i] & (kSlots - 1)];
   }
-  if (need) xn = (xn << 16) | (uint32_t)words[idx];
-  c.x = xn;
-  return e.x;
+  uint32_t xn[ILP], w[ILP];
+  bool need[ILP];
+#pragma unroll
+  for (int i = 0; i < ILP; ++i) {
+    xn[i] = (e[i].x & 0xFFFFFFu) * (x[i] >> 12) + e[i].y;  // v_mad_u32_u24
+    need[i] = xn[i] < kL;
+    if (CAREFUL) need[i] = need[i] && (s < c[i].lim);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(need[i]);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+    uint32_t idx;
+    if (R == 64) {
+      idx = rank + min(c[i].p0, c[i].e0);
+      c[i].p0 += (uint32_t)__builtin_popcountll(m);
+    } else {
+      const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
+      const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
+      // upper-half lanes count the lower half's bits too: start them pl lower
+      const uint32_t b0 = min(c[i].p0, c[i].e0);
+      const uint32_t b1 = min(c[i].p1, c[i].e1) - pl;
+      idx = rank + (upper_half ? b1 : b0);
+      c[i].p0 += pl;
+      c[i].p1 += ph;
+    }
+    w[i] = words[idx];
+  }
+#pragma unroll
+  for (int i = 0; i < ILP; ++i) {
+    c[i].x = need[i] ? ((xn[i] << 16) | w[i]) : xn[i];
+    sym[i] = e[i].x;
+  }
 }
 
 // Integrity flags of the chain's tile(s) after the last step, per lane's tile:
-// 1 = a lane did not return to its initial value, 2 = words consumed != stream,
-// 4 = read past the stream.
+// 1 = a lane did not return to its initial value, 2 = words consumed != stream
+// (a pad word may remain), 4 = read past the stream.
 template <int R>
 __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
                                                 bool upper_half) {
   const uint32_t want = (c.lim == steps) ? kL : 0u;
   const uint64_t bad = __builtin_amdgcn_ballot_w64(c.x != want);
   uint32_t f = 0;
-  if (R == 64) {
-    if (bad) f |= 1u;
-    const uint32_t used = c.p0 - c.s0, avail = c.e0 - c.s0;
-    if (!(used == avail || used + 1 == avail)) f |= 2u;
-    if (c.ovf & 1u) f |= 4u;
-  } else {
-    const uint32_t half_bad = upper_half ? (uint32_t)(bad >> 32) : (uint32_t)bad;
-    if (half_bad) f |= 1u;
-    const uint32_t p = upper_half ? c.p1 : c.p0, st = upper_half ? c.s1 : c.s0,
-                   en = upper_half ? c.e1 : c.e0;
-    const uint32_t used = p - st, avail = en - st;
-    if (!(used == avail || used + 1 == avail)) f |= 2u;
-    if (c.ovf & (upper_half ? 2u : 1u)) f |= 4u;
-  }
+  const uint32_t half_bad = (R == 64) ? (bad != 0) : (upper_half ? (uint32_t)(bad >> 32)
+                                                                 : (uint32_t)bad);
+  if (half_bad) f |= 1u;
+  const uint32_t p = (R == 32 && upper_half) ? c.p1 : c.p0;
+  const uint32_t st = (R == 32 && upper_half) ? c.s1 : c.s0;
+  const uint32_t en = (R == 32 && upper_half) ? c.e1 : c.e0;
+  const uint32_t used = p - st, avail = en - st;
+  if (!(used == avail || used + 1 == avail)) f |= 2u;
+  if (used > avail) f |= 4u;
   return f;
 }
 

@@ -29,20 +29,33 @@ struct GemmArgs {
   Layer L;
   const uint8_t* x;          // bf16 bits [M, K] (FP8: the quantised X as exact bf16)
   const uint16_t* scales;    // INT4: bf16 bits [N, K/128]
-  const float* xscale;       // FP8: device sx (per-tensor activation scale)
+  float* xscale;             // FP8: device sx (per-tensor activation scale)
   float w_scale;             // FP8 weight scale
   float* y;                  // fp32 [M, N]
-  float* part;               // workspace partials [strips][gps][M][tile_n]
+  float* part;               // workspace partials [strips][slots][M][tile_n]
   uint32_t* counters;        // workspace counters [strips]
   int32_t* status;           // per-tile status or null
   uint32_t m;                // rows of X / Y in this launch (<= 16 * MT)
   uint32_t x_row_bytes;      // row stride of x in bytes
   uint32_t y_row;            // row stride of y in floats (= N)
-  uint32_t waves;            // waves per workgroup
-  uint32_t tpw;              // k-tiles per wave
-  uint32_t gps;              // workgroups per strip
+  uint32_t waves;            // waves (= units) per workgroup
+  uint32_t tpw;              // k-tiles per unit (one wave's work)
+  uint32_t units;            // total units: strips * ups
+  uint32_t ups;              // units per strip
+  uint32_t slots;            // partial slots per strip in the workspace
   uint32_t red_cols;         // tile_n columns reduced per LDS pass
 };
+
+// Static schedule: units (ILP chains of consecutive k-tiles of one strip) are
+// numbered strip-major; workgroup b takes units [b*W, b*W + W), so it covers
+// the tail of one strip and the head of the next at most (W <= ups).  The
+// workgroups touching strip s are floor(s*ups/W) .. floor(((s+1)*ups-1)/W).
+__device__ __forceinline__ uint32_t strip_first_wg(uint32_t s, uint32_t ups, uint32_t W) {
+  return (uint32_t)(((uint64_t)s * ups) / W);
+}
+__device__ __forceinline__ uint32_t strip_last_wg(uint32_t s, uint32_t ups, uint32_t W) {
+  return (uint32_t)(((uint64_t)(s + 1) * ups - 1) / W);
+}
 
 template <int FMT>
 struct OperandTraits;
@@ -130,71 +143,112 @@ __device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t 
 }
 
 // ---------------------------------------------------------------- reduction
-// Sum the per-wave partials acc[FN][MT] of a workgroup in wave order through
-// LDS, then either write Y (one workgroup per strip) or a workspace partial
-// with the last-arriving workgroup summing all partials in workgroup order.
+// Sum the per-wave partials acc[FN][MT] of a workgroup through LDS in wave
+// order, separately for the (at most two) strips the workgroup covers.  A strip
+// covered by one workgroup is written to Y directly; otherwise each workgroup
+// stores its partial in its slot and the last one to arrive (per-strip
+// counter) sums the slots in order, so results are deterministic.
 template <int FN, int MT>
 __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
-                                                 float* red, uint32_t strip, uint32_t gslot,
-                                                 float out_scale) {
+                                                 float* red, float out_scale) {
   const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint32_t M = a.m, TN = FN * 16, W = a.waves, RC = a.red_cols;
-  const uint32_t n0 = strip * TN;
+  const uint32_t wg = blockIdx.x;
+  const uint32_t u0 = wg * W, u1 = min(u0 + W, a.units);
+  const uint32_t nw = u1 - u0;                       // active waves
+  const uint32_t sA = u0 / a.ups, sB = (u1 - 1) / a.ups;
+  const uint32_t split = (sA == sB) ? nw : (sA + 1) * a.ups - u0;  // waves in strip A
+  const uint32_t nstrips = (sA == sB) ? 1u : 2u;
   __syncthreads();  // LUT / staged streams are no longer needed
   for (uint32_t c0 = 0; c0 < TN; c0 += RC) {
+    if (wave < nw) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const uint32_t col = fn * 16 + (lane & 15);
-      if (col >= c0 && col < c0 + RC) {
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint32_t col = fn * 16 + (lane & 15);
+        if (col >= c0 && col < c0 + RC) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+          for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t m = mt * 16 + 4 * (lane >> 4) + i;
-            if (m < M) red[((size_t)wave * M + m) * RC + (col - c0)] = acc[fn][mt][i];
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t m = mt * 16 + 4 * (lane >> 4) + i;
+              if (m < M) red[((size_t)wave * M + m) * RC + (col - c0)] = acc[fn][mt][i];
+            }
           }
         }
       }
     }
     __syncthreads();
     for (uint32_t idx = t; idx < M * RC; idx += blockDim.x) {
-      float s = 0.f;
-      for (uint32_t w = 0; w < W; ++w) s += red[(size_t)w * M * RC + idx];
       const uint32_t m = idx / RC, col = c0 + idx % RC;
-      if (a.gps == 1) {
-        a.y[(size_t)m * a.y_row + n0 + col] = s * out_scale;
-      } else {
-        a.part[(((size_t)strip * a.gps + gslot) * M + m) * TN + col] = s;
+      for (uint32_t k = 0; k < nstrips; ++k) {
+        const uint32_t s = k ? sB : sA;
+        const uint32_t w0 = k ? split : 0u, w1 = k ? nw : split;
+        float v = 0.f;
+        for (uint32_t w = w0; w < w1; ++w) v += red[(size_t)w * M * RC + idx];
+        const uint32_t f = strip_first_wg(s, a.ups, W), l = strip_last_wg(s, a.ups, W);
+        if (f == l) {
+          a.y[(size_t)m * a.y_row + s * TN + col] = v * out_scale;
+        } else {
+          // agent-scope store: coherent across XCDs without an L2 writeback
+          __hip_atomic_store(&a.part[(((size_t)s * a.slots + (wg - f)) * M + m) * TN + col], v,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     __syncthreads();
   }
-  if (a.gps == 1) return;
-  __shared__ uint32_t last_flag;
-  __threadfence();
+  // Hand-off to the last workgroup of a shared strip.  The partials are
+  // agent-scope atomic stores; waiting for their completion before the counter
+  // update (and reading them back with agent-scope atomic loads) orders them
+  // without the device-wide cache writeback/invalidate a full fence costs on a
+  // multi-XCD part.
+  __shared__ uint32_t last_flag[2];
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t == 0) {
-    const uint32_t old = atomicAdd(&a.counters[strip], 1u);
-    last_flag = (old == a.gps - 1) ? 1u : 0u;
+  if (t < nstrips) {
+    const uint32_t s = t ? sB : sA;
+    const uint32_t f = strip_first_wg(s, a.ups, W), l = strip_last_wg(s, a.ups, W);
+    uint32_t last = 0;
+    if (f != l) {
+      const uint32_t old = __hip_atomic_fetch_add(&a.counters[s], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      last = (old == l - f) ? 1u : 0u;
+    }
+    last_flag[t] = last;
   }
   __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  for (uint32_t idx = t; idx < M * TN; idx += blockDim.x) {
-    const uint32_t m = idx / TN, col = idx % TN;
-    float s = 0.f;
-    for (uint32_t g = 0; g < a.gps; ++g)
-      s += a.part[(((size_t)strip * a.gps + g) * M + m) * TN + col];
-    a.y[(size_t)m * a.y_row + n0 + col] = s * out_scale;
+  for (uint32_t k = 0; k < nstrips; ++k) {
+    if (!last_flag[k]) continue;
+    const uint32_t s = k ? sB : sA;
+    const uint32_t n = strip_last_wg(s, a.ups, W) - strip_first_wg(s, a.ups, W) + 1;
+    for (uint32_t idx = t; idx < M * TN; idx += blockDim.x) {
+      const uint32_t m = idx / TN, col = idx % TN;
+      float v = 0.f;
+      for (uint32_t g = 0; g < n; ++g)
+        v += __hip_atomic_load(&a.part[(((size_t)s * a.slots + g) * M + m) * TN + col],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.y[(size_t)m * a.y_row + s * TN + col] = v * out_scale;
+    }
+    if (t == 0)
+      __hip_atomic_store(&a.counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (t == 0) a.counters[strip] = 0u;
 }
 
 // --------------------------------------------------------------- fused GEMM
 // FN = tile_n / 16 row bands per tile, MT = 16-row blocks of X, ILP = chains
 // per wave.  LDS: LUT | cumulative table | staged stream regions.
+// Workgroup size cap per variant: kernels whose registers fit in 128 VGPRs run
+// up to 16 waves per workgroup; the others (more row bands or row blocks of
+// accumulators) stay at 8 waves with up to 256 VGPRs.
+__host__ __device__ constexpr uint32_t fused_max_threads(int R, int FN, int MT, int ILP) {
+  return (MT == 1 && FN <= 8 && (R == 64 || ILP == 1)) ? 1024u : 512u;
+}
+__host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
+  return (MT == 1 && FN <= 8) ? 1024u : 512u;
+}
+
 template <int FMT, int R, int FN, int MT, int ILP>
-__global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
+__global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
@@ -205,9 +259,10 @@ __global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
 
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t strip = blockIdx.x / a.gps, gslot = blockIdx.x % a.gps;
-  const uint32_t kt_first = uniform((gslot * a.waves + wave) * a.tpw);
-  const bool active = kt_first < L.kt;
+  const uint32_t unit = uniform(blockIdx.x * a.waves + wave);
+  const bool active = (wave < a.waves) && (unit < a.units);
+  const uint32_t strip = active ? unit / a.ups : 0u;
+  const uint32_t kt_first = active ? (unit % a.ups) * a.tpw : 0u;
   const bool upper = lane >= 32;
   const uint32_t half_lane = lane & 31;
 
@@ -240,7 +295,6 @@ __global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
       ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
       ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
       ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
-      ch[c].ovf = 0;
       const uint32_t kt_l = kt_first + c * TPC + ((R == 32 && upper) ? 1u : 0u);
       k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
     }
@@ -261,50 +315,86 @@ __global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
       if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
     }
     const uint32_t FK = L.tile_k / FW;
+    const uint32_t G = FK * FN;
     const uint32_t kgroups = L.k / 128;
+    // operands that come from global memory are fetched one fragment (raw
+    // bytes, scales) or one column block (X) ahead of their use
+    auto load_raw = [&](int c, uint32_t g) -> u32x2 {
+      const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
+                          (size_t)g * 8 * R + (lane % R) * 8;
+      return *reinterpret_cast<const u32x2*>(rp);
+    };
+    auto load_scale = [&](int c, uint32_t g) -> float {
+      const uint32_t fkg = g / FN, fng = g % FN;
+      const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
+      const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fkg * FW) / 128];
+      return __uint_as_float((uint32_t)sb << 16);
+    };
+    u32x2 raw_n[ILP];
+    float sc_n[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      raw_n[c] = u32x2{0u, 0u};
+      sc_n[c] = 0.f;
+      if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
+      if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
+    }
+    constexpr bool kPrefetchA = (MT == 1);
+    u32x4 A_n[ILP][MT];
+    if constexpr (kPrefetchA) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c]);
+    }
     for (uint32_t fk = 0; fk < FK; ++fk) {
       u32x4 A[ILP][MT];
 #pragma unroll
       for (int c = 0; c < ILP; ++c)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
+        for (int mt = 0; mt < MT; ++mt) {
+          if constexpr (kPrefetchA) {
+            A[c][mt] = A_n[c][mt];
+            if (fk + 1 < FK)
+              A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + (fk + 1) * FW);
+          } else {
+            A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
+          }
+        }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const uint32_t g = fk * FN + fn;
         const uint32_t s0 = g * 8;
+        const uint32_t gn = min(g + 1, G - 1);
         u32x2 raw[ILP];
         float sc[ILP], nsc8[ILP];
 #pragma unroll
         for (int c = 0; c < ILP; ++c) {
-          raw[c] = u32x2{0u, 0u};
-          sc[c] = 0.f; nsc8[c] = 0.f;
-          if constexpr (FMT == BF16) {
-            const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
-                                (size_t)g * 8 * R + (lane % R) * 8;
-            raw[c] = *reinterpret_cast<const u32x2*>(rp);
-          }
-          if constexpr (FMT == INT4) {
-            const uint32_t row = strip * L.tile_n + fn * 16 + (lane & 15);
-            const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fk * FW) / 128];
-            sc[c] = __uint_as_float((uint32_t)sb << 16);
-            nsc8[c] = -8.f * sc[c];
-          }
+          raw[c] = raw_n[c];
+          sc[c] = sc_n[c];
+          nsc8[c] = -8.f * sc[c];
+          if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
+          if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
         }
         uint32_t e[ILP][8];
         // payload steps (at most the last 16) fall in the last two fragments
         if (fn < FN - 2 || s0 + 7 < lim_min) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < 8; ++i) {
+            uint32_t sy[ILP];
+            step_all<R, false, ILP>(ch, lut, words, s0 + i, upper, sy);
 #pragma unroll
-            for (int c = 0; c < ILP; ++c)
-              e[c][i] = step<R, false>(ch[c], lut, words, s0 + i, upper);
+            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+          }
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < 8; ++i) {
+            uint32_t sy[ILP];
+            step_all<R, true, ILP>(ch, lut, words, s0 + i, upper, sy);
 #pragma unroll
-            for (int c = 0; c < ILP; ++c)
-              e[c][i] = step<R, true>(ch[c], lut, words, s0 + i, upper);
+            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+          }
         }
 #pragma unroll
         for (int c = 0; c < ILP; ++c) {
@@ -323,8 +413,9 @@ __global__ __launch_bounds__(512) void k_fused(GemmArgs a) {
     }
   }
   float out_scale = 1.f;
-  if constexpr (FMT == FP8) out_scale = a.xscale[0] * a.w_scale;
-  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), strip, gslot, out_scale);
+  if constexpr (FMT == FP8)
+    out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
+  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), out_scale);
 }
 
 // --------------------------------------------------------------- decode only
@@ -382,7 +473,6 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
       ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
       ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
-      ch[c].ovf = 0;
     }
   }
   __syncthreads();
@@ -401,14 +491,20 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     uint32_t e[ILP][8];
     if (s0 + 7 < lim_min) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        uint32_t sy[ILP];
+        step_all<R, false, ILP>(ch, lut, words, s0 + i, upper, sy);
 #pragma unroll
-        for (int c = 0; c < ILP; ++c) e[c][i] = step<R, false>(ch[c], lut, words, s0 + i, upper);
+        for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        uint32_t sy[ILP];
+        step_all<R, true, ILP>(ch, lut, words, s0 + i, upper, sy);
 #pragma unroll
-        for (int c = 0; c < ILP; ++c) e[c][i] = step<R, true>(ch[c], lut, words, s0 + i, upper);
+        for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+      }
     }
     const uint32_t fk = g / FN, fn = g % FN;
 #pragma unroll
@@ -448,13 +544,15 @@ struct DenseArgs {
 };
 
 template <int FMT, int FN, int MT>
-__global__ __launch_bounds__(512) void k_dense(DenseArgs d) {
+__global__ __launch_bounds__(dense_max_threads(FN, MT)) void k_dense(DenseArgs d) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GemmArgs& a = d.g;
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t strip = blockIdx.x / a.gps, gslot = blockIdx.x % a.gps;
-  const uint32_t kt_first = uniform((gslot * a.waves + wave) * a.tpw);
+  const uint32_t unit = uniform(blockIdx.x * a.waves + wave);
+  const bool active = unit < a.units;
+  const uint32_t strip = active ? unit / a.ups : 0u;
+  const uint32_t kt_first = active ? (unit % a.ups) * a.tpw : d.kt;
   floatx4 acc[FN][MT];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn)
@@ -495,8 +593,9 @@ __global__ __launch_bounds__(512) void k_dense(DenseArgs d) {
     }
   }
   float out_scale = 1.f;
-  if constexpr (FMT == FP8) out_scale = a.xscale[0] * a.w_scale;
-  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), strip, gslot, out_scale);
+  if constexpr (FMT == FP8)
+    out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
+  reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), out_scale);
 }
 
 }  // namespace dev
