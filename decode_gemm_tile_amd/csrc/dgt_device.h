@@ -82,17 +82,28 @@ __device__ inline void build_lut(const uint16_t* table, uint32_t alphabet, u32x2
   __syncthreads();
   if (t < 256) cum[1 + t] = v;
   __syncthreads();
-  for (uint32_t r = t; r < kSlots; r += blockDim.x) {
-    uint32_t lo = 0, hi = alphabet;  // cum[lo] <= r < cum[hi]
+  // each thread fills a contiguous run of slots: one binary search for the
+  // first slot, then a forward walk (the symbol only grows along the run)
+  const uint32_t per = (kSlots + blockDim.x - 1) / blockDim.x;
+  const uint32_t r0 = t * per, r1 = min(r0 + per, kSlots);
+  if (r0 < r1) {
+    uint32_t lo = 0, hi = alphabet;  // cum[lo] <= r0 < cum[hi]
     while (hi - lo > 1) {
       const uint32_t mid = (lo + hi) >> 1;
-      if (cum[mid] <= r) lo = mid; else hi = mid;
+      if (cum[mid] <= r0) lo = mid; else hi = mid;
     }
-    const uint32_t f = cum[lo + 1] - cum[lo];
-    u32x2 e;
-    e.x = f | (lo << 24);
-    e.y = r - cum[lo];
-    lut[r] = e;
+    uint32_t c_lo = cum[lo], c_hi = cum[lo + 1];
+    for (uint32_t r = r0; r < r1; ++r) {
+      while (c_hi <= r) {  // next symbol with a non-empty range
+        ++lo;
+        c_lo = c_hi;
+        c_hi = cum[lo + 1];
+      }
+      u32x2 e;
+      e.x = (c_hi - c_lo) | (lo << 24);
+      e.y = r - c_lo;
+      lut[r] = e;
+    }
   }
 }
 
@@ -184,18 +195,41 @@ __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
   return f;
 }
 
-// Stage tile t's word stream into LDS words[start ..) using the lanes of one
-// half (R = 32) or the whole wave (R = 64); load the lane states.  Returns the
-// number of staged u16 words (including a possible pad word).
-__device__ __forceinline__ uint32_t stage_tile(const Layer& L, uint32_t t, uint16_t* words,
-                                               uint32_t start, uint32_t sub_lane,
-                                               uint32_t sub_size) {
+// Staging of a tile's word stream into LDS in two phases, so the HBM latency
+// of the loads overlaps other prologue work: stage_issue loads up to kPre
+// dwords per lane into registers, stage_commit writes them to LDS and copies
+// whatever the registers did not cover.
+constexpr int kPre = 16;
+
+struct Staged {
+  uint32_t v[kPre];
+  const uint32_t* src;
+  uint32_t words4;
+};
+
+__device__ __forceinline__ void stage_issue(const Layer& L, uint32_t t, uint32_t sub_lane,
+                                            uint32_t sub_size, Staged& st) {
   const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
-  const uint32_t words4 = o1 - o0 - L.lanes;
-  const uint32_t* src = L.streams + o0 + L.lanes;
+  st.words4 = o1 - o0 - L.lanes;
+  st.src = L.streams + o0 + L.lanes;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const uint32_t i = sub_lane + j * sub_size;
+    st.v[j] = (i < st.words4) ? st.src[i] : 0u;
+  }
+}
+
+// Returns the number of staged u16 words (including a possible pad word).
+__device__ __forceinline__ uint32_t stage_commit(const Staged& st, uint16_t* words, uint32_t start,
+                                                 uint32_t sub_lane, uint32_t sub_size) {
   uint32_t* dst = reinterpret_cast<uint32_t*>(words + start);
-  for (uint32_t i = sub_lane; i < words4; i += sub_size) dst[i] = src[i];
-  return 2 * words4;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const uint32_t i = sub_lane + j * sub_size;
+    if (i < st.words4) dst[i] = st.v[j];
+  }
+  for (uint32_t i = sub_lane + kPre * sub_size; i < st.words4; i += sub_size) dst[i] = st.src[i];
+  return 2 * st.words4;
 }
 
 }  // namespace dev

@@ -266,37 +266,38 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
   const bool upper = lane >= 32;
   const uint32_t half_lane = lane & 31;
 
-  build_lut(L.table, L.alphabet, lut, cum);
-
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
   uint32_t k0_lane[ILP];
+  Staged stg[ILP];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  // 1) issue the stream loads, 2) build the LUT while they are in flight,
+  // 3) write the streams to LDS
   if (active) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t ta = strip * L.kt + kt_first + c * TPC;
-      const uint32_t tb = (R == 32) ? ta + 1 : ta;
-      const uint32_t ra = region0 + c * TPC * L.region_words;
-      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
-      uint32_t na, nb;
-      if (R == 64) {
-        na = stage_tile(L, ta, words, ra, lane, 64);
-        nb = na;
-      } else {
-        const uint32_t mine = stage_tile(L, upper ? tb : ta, words, upper ? rb : ra,
-                                         half_lane, 32);
-        na = uniform(mine);
-        nb = (uint32_t)__builtin_amdgcn_readlane((int)mine, 32);
-      }
-      const uint32_t t_l = upper && R == 32 ? tb : ta;
+      const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
       tile_lane[c] = t_l;
+      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
       ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
       ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
-      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
-      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
       const uint32_t kt_l = kt_first + c * TPC + ((R == 32 && upper) ? 1u : 0u);
       k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
+    }
+  }
+  build_lut(L.table, L.alphabet, lut, cum);
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t ra = region0 + c * TPC * L.region_words;
+      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
+      const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
+                                         R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
+      const uint32_t na = uniform(mine);
+      const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
+      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
+      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
     }
   }
   __syncthreads();
@@ -443,34 +444,35 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   const uint32_t first = uniform((blockIdx.x * a.waves + wave) * ILP * TPC);
   const bool active = first < a.n_ids;
 
-  build_lut(L.table, L.alphabet, lut, cum);
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
+  Staged stg[ILP];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
   if (active) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       // slots past the end repeat the last id (same tile decoded twice, same output)
-      uint32_t ia = min(first + c * TPC, a.n_ids - 1);
-      uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
+      const uint32_t ia = min(first + c * TPC, a.n_ids - 1);
+      const uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
       const uint32_t ta = a.ids ? a.ids[ia] : ia;
       const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
-      const uint32_t ra = region0 + c * TPC * L.region_words;
-      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
-      uint32_t na, nb;
-      if (R == 64) {
-        na = stage_tile(L, ta, words, ra, lane, 64);
-        nb = na;
-      } else {
-        const uint32_t mine = stage_tile(L, upper ? tb : ta, words, upper ? rb : ra,
-                                         half_lane, 32);
-        na = uniform(mine);
-        nb = (uint32_t)__builtin_amdgcn_readlane((int)mine, 32);
-      }
-      const uint32_t t_l = upper && R == 32 ? tb : ta;
+      const uint32_t t_l = (R == 32 && upper) ? tb : ta;
       tile_lane[c] = t_l;
+      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
       ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
       ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
+    }
+  }
+  build_lut(L.table, L.alphabet, lut, cum);
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t ra = region0 + c * TPC * L.region_words;
+      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
+      const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
+                                         R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
+      const uint32_t na = uniform(mine);
+      const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
       ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
       ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
     }
