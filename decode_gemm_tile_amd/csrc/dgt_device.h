@@ -61,12 +61,18 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
 
 // Build the slot table in LDS from the shared frequency table: every slot r
 // maps to the symbol s with c_s <= r < c_s + f_s.  Caller synchronises.
-__device__ inline void build_lut(const uint16_t* table, uint32_t alphabet, u32x2* lut,
+// The frequency load is split off so it can be issued before other loads
+// (the vector-memory counter retires loads in order).
+__device__ __forceinline__ uint32_t lut_load_freq(const uint16_t* table, uint32_t alphabet) {
+  return (threadIdx.x < alphabet) ? (uint32_t)table[threadIdx.x] : 0u;
+}
+
+__device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32x2* lut,
                                  uint32_t* cum) {
   const uint32_t t = threadIdx.x;
   const uint32_t lane = t & 63, wave = t >> 6;
   // inclusive scan of f over <= 256 symbols: wave scans plus wave totals
-  uint32_t v = (t < alphabet) ? (uint32_t)table[t] : 0u;
+  uint32_t v = freq_of_thread;
   for (uint32_t d = 1; d < 64; d <<= 1) {
     uint32_t o = __shfl_up(v, d, 64);
     if (lane >= d) v += o;
@@ -82,56 +88,55 @@ __device__ inline void build_lut(const uint16_t* table, uint32_t alphabet, u32x2
   __syncthreads();
   if (t < 256) cum[1 + t] = v;
   __syncthreads();
-  // each thread fills a contiguous run of slots: one binary search for the
-  // first slot, then a forward walk (the symbol only grows along the run)
+  // each thread fills a contiguous run of slots, searching for the symbol of
+  // a slot only when the slot leaves the current symbol's range
   const uint32_t per = (kSlots + blockDim.x - 1) / blockDim.x;
   const uint32_t r0 = t * per, r1 = min(r0 + per, kSlots);
-  if (r0 < r1) {
-    uint32_t lo = 0, hi = alphabet;  // cum[lo] <= r0 < cum[hi]
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (cum[mid] <= r0) lo = mid; else hi = mid;
-    }
-    uint32_t c_lo = cum[lo], c_hi = cum[lo + 1];
-    for (uint32_t r = r0; r < r1; ++r) {
-      while (c_hi <= r) {  // next symbol with a non-empty range
-        ++lo;
-        c_lo = c_hi;
-        c_hi = cum[lo + 1];
+  uint32_t s_cur = 0, c_lo = 0, c_hi = 0;  // empty range: forces the first search
+  for (uint32_t r = r0; r < r1; ++r) {
+    if (r >= c_hi) {
+      uint32_t lo = 0, hi = alphabet;  // cum[lo] <= r < cum[hi]
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (cum[mid] <= r) lo = mid; else hi = mid;
       }
-      u32x2 e;
-      e.x = (c_hi - c_lo) | (lo << 24);
-      e.y = r - c_lo;
-      lut[r] = e;
+      s_cur = lo;
+      c_lo = cum[lo];
+      c_hi = cum[lo + 1];
     }
+    u32x2 e;
+    e.x = (c_hi - c_lo) | (s_cur << 24);
+    e.y = r - c_lo;
+    lut[r] = e;
   }
 }
 
 // R lane states of one chain: one tile (R = 64) or two tiles (R = 32).
-// Fields marked "uniform" hold the same value on every lane.
+// Word positions are byte offsets into the workgroup's LDS; fields marked
+// "uniform" hold the same value on every lane.
 struct Chain {
   uint32_t x;      // lane state
   uint32_t lim;    // first payload step of the lane's tile (steps - k)
-  uint32_t p0;     // uniform: words of tile A consumed so far + s0 (not clamped)
-  uint32_t p1;     // uniform: same for tile B (R = 32)
-  uint32_t e0;     // uniform: end of tile A's staged words
+  uint32_t p0;     // uniform: next word of tile A (byte offset, not clamped)
+  uint32_t p1;     // uniform: next word of tile B (R = 32)
+  uint32_t e0;     // uniform: end of tile A's staged words (byte offset)
   uint32_t e1;     // uniform: end of tile B's staged words
-  uint32_t s0;     // uniform: start of tile A's words (u16 index into the LDS word array)
+  uint32_t s0;     // uniform: start of tile A's words (byte offset)
   uint32_t s1;     // uniform: start of tile B's words
 };
 
 // ILP chains advance one rANS step together, in three phases so that their
 // LDS round trips overlap: (1) table reads for every chain, (2) state update,
 // wave ballot of the lanes that renormalise, word reads for every chain,
-// (3) merge.  Branch-free: every lane reads a word (in bounds: a pointer is
-// clamped to its stream end and the region has kSlackWords of slack) and
-// keeps it only if it renormalises.  The word of lane p is the next unread
-// one plus the number of renormalising lanes below p (mbcnt of the ballot).
-// CAREFUL also handles the payload switch (x -= L at step == lim, no reads
-// from then on).  Returns the table words (decoded symbol in the top byte).
+// (3) merge.  Branch-free: every lane reads a word (in bounds: a pointer is clamped to its
+// stream end and the region has kSlackWords of slack); only the lanes that
+// renormalise take it.  The word of lane p is the next unread one plus the
+// number of renormalising lanes below p (mbcnt of the ballot).  CAREFUL also
+// handles the payload switch (x -= L at step == lim, no reads from then on).
+// Returns the table words (decoded symbol in the top byte).
 template <int R, bool CAREFUL, int ILP>
 __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
-                                         const uint16_t* __restrict__ words, uint32_t s,
+                                         const uint8_t* __restrict__ lds, uint32_t s,
                                          bool upper_half, uint32_t (&sym)[ILP]) {
   uint32_t x[ILP];
   u32x2 e[ILP];
@@ -151,21 +156,21 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
     const uint64_t m = __builtin_amdgcn_ballot_w64(need[i]);
     const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-    uint32_t idx;
+    uint32_t addr;
     if (R == 64) {
-      idx = rank + min(c[i].p0, c[i].e0);
-      c[i].p0 += (uint32_t)__builtin_popcountll(m);
+      addr = 2 * rank + min(c[i].p0, c[i].e0);
+      c[i].p0 += 2 * (uint32_t)__builtin_popcountll(m);
     } else {
       const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
       const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
       // upper-half lanes count the lower half's bits too: start them pl lower
       const uint32_t b0 = min(c[i].p0, c[i].e0);
-      const uint32_t b1 = min(c[i].p1, c[i].e1) - pl;
-      idx = rank + (upper_half ? b1 : b0);
-      c[i].p0 += pl;
-      c[i].p1 += ph;
+      const uint32_t b1 = min(c[i].p1, c[i].e1) - 2 * pl;
+      addr = 2 * rank + (upper_half ? b1 : b0);
+      c[i].p0 += 2 * pl;
+      c[i].p1 += 2 * ph;
     }
-    w[i] = words[idx];
+    w[i] = *reinterpret_cast<const uint16_t*>(lds + addr);
   }
 #pragma unroll
   for (int i = 0; i < ILP; ++i) {
@@ -189,7 +194,7 @@ __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
   const uint32_t p = (R == 32 && upper_half) ? c.p1 : c.p0;
   const uint32_t st = (R == 32 && upper_half) ? c.s1 : c.s0;
   const uint32_t en = (R == 32 && upper_half) ? c.e1 : c.e0;
-  const uint32_t used = p - st, avail = en - st;
+  const uint32_t used = (p - st) / 2, avail = (en - st) / 2;  // words
   if (!(used == avail || used + 1 == avail)) f |= 2u;
   if (used > avail) f |= 4u;
   return f;

@@ -202,7 +202,7 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
   // update (and reading them back with agent-scope atomic loads) orders them
   // without the device-wide cache writeback/invalidate a full fence costs on a
   // multi-XCD part.
-  __shared__ uint32_t last_flag[2];
+  uint32_t* last_flag = reinterpret_cast<uint32_t*>(red);  // reduction buffer is free now
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t < nstrips) {
@@ -271,6 +271,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
   uint32_t k0_lane[ILP];
   Staged stg[ILP];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
   // 3) write the streams to LDS
   if (active) {
@@ -286,7 +287,8 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
       k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
     }
   }
-  build_lut(L.table, L.alphabet, lut, cum);
+  build_lut(fq, L.alphabet, lut, cum);
+  __syncthreads();  // LUT complete; each wave's staged stream is private to it
   if (active) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -296,11 +298,11 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
                                          R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
       const uint32_t na = uniform(mine);
       const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
-      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
+      const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
+      ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
+      ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
     }
   }
-  __syncthreads();
 
   floatx4 acc[FN][MT];
 #pragma unroll
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             uint32_t sy[ILP];
-            step_all<R, false, ILP>(ch, lut, words, s0 + i, upper, sy);
+            step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
           }
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             uint32_t sy[ILP];
-            step_all<R, true, ILP>(ch, lut, words, s0 + i, upper, sy);
+            step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
           }
@@ -448,6 +450,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   uint32_t tile_lane[ILP];
   Staged stg[ILP];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   if (active) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -463,7 +466,8 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
     }
   }
-  build_lut(L.table, L.alphabet, lut, cum);
+  build_lut(fq, L.alphabet, lut, cum);
+  __syncthreads();  // LUT complete; each wave's staged stream is private to it
   if (active) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
@@ -473,11 +477,11 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
                                          R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
       const uint32_t na = uniform(mine);
       const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-      ch[c].p0 = ra; ch[c].s0 = ra; ch[c].e0 = ra + na;
-      ch[c].p1 = rb; ch[c].s1 = rb; ch[c].e1 = rb + nb;
+      const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
+      ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
+      ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
     }
   }
-  __syncthreads();
   if (!active) return;
   uint32_t lim_min = L.steps;
 #pragma unroll
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t sy[ILP];
-        step_all<R, false, ILP>(ch, lut, words, s0 + i, upper, sy);
+        step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
       }
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t sy[ILP];
-        step_all<R, true, ILP>(ch, lut, words, s0 + i, upper, sy);
+        step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
       }
