@@ -85,6 +85,15 @@ def _to_bf16_bits(values_f64) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def _normal_bf16_bits(rng, count: int, mean: float, sigma: float) -> np.ndarray:
+    """Same draws and casts as _to_bf16_bits(_normal(...)), chunk by chunk."""
+    out = np.empty(count, dtype=np.uint16)
+    for s in range(0, count, _CHUNK):
+        e = min(count, s + _CHUNK)
+        out[s:e] = _to_bf16_bits(rng.normal(mean, sigma, e - s))
+    return out
+
+
 def _int_codes(rng, n, k, mean, sigma, lo, hi) -> np.ndarray:
     out = np.empty(n * k, dtype=np.int16)
     for s in range(0, n * k, _CHUNK):
@@ -116,7 +125,7 @@ def make_weights(wl: Workload, rng=None):
         out["scales"] = _scales(rng, n, k // 128)
     elif wl.fmt == FMT_FP8:
         import torch
-        wb = _to_bf16_bits(_normal(rng, n * k, 0.0, wl.w_sigma)).reshape(n, k)
+        wb = _normal_bf16_bits(rng, n * k, 0.0, wl.w_sigma).reshape(n, k)
         wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).float()
         amax = wt.abs().max()
         sw = (amax / 448.0).to(torch.float32)
@@ -124,7 +133,7 @@ def make_weights(wl: Workload, rng=None):
         out["codes"] = q.view(torch.uint8).numpy().copy()
         out["w_scale"] = float(sw)
     elif wl.fmt == FMT_BF16:
-        out["codes"] = _to_bf16_bits(_normal(rng, n * k, 0.0, wl.w_sigma)).reshape(n, k)
+        out["codes"] = _normal_bf16_bits(rng, n * k, 0.0, wl.w_sigma).reshape(n, k)
     else:
         raise ValueError("unknown format")
     return out
