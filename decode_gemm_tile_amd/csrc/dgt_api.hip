@@ -138,6 +138,8 @@ int device_supported(const dgt_info* in) {
 struct FusedPlan {
   uint32_t mt, ilp, waves, threads, tpw, ups, units, wgs, slots, strips, red_cols, lds, m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
+  // large-M variant (fragments shared through LDS): used when xm != 0
+  uint32_t xm, bps, bpw, batches, xbuf_off;
 };
 
 constexpr uint32_t kCUs = 256;
@@ -150,7 +152,56 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
   return std::min(w, ups);
 }
 
+// Large M: one launch in which every tile is decoded once and shared through
+// LDS by waves that own disjoint row blocks, instead of one launch per chunk
+// of rows that each decode the whole layer.  Needs R = 64 and k-tiles per
+// strip divisible by the workgroup's wave count.
+bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
+  const uint32_t fn = in->tile_n / 16;
+  if (in->lanes != 64 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
+  if (m <= (fn == 8 ? 64u : 16u)) return false;  // one register-resident pass covers M
+  const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn);
+  if (m > nw * mtw * 16) return false;
+  const uint32_t kt = in->k / in->tile_k;
+  if (kt % nw) return false;
+  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
+  const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
+  const uint32_t xbuf_off =
+      (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nw * region_bytes + 16, 16);
+  const uint32_t lds = xbuf_off + 2 * nw * 1024;
+  if (lds > kMaxLds) return false;
+  p->xm = 1;
+  p->xbuf_off = xbuf_off;
+  p->lds = lds;
+  p->strips = in->n / in->tile_n;
+  p->bps = kt / nw;
+  p->batches = p->strips * p->bps;
+  p->bpw = (p->batches + kCUs - 1) / kCUs;  // one workgroup per CU, one round
+  p->wgs = (p->batches + p->bpw - 1) / p->bpw;
+  p->slots = (p->bps + p->bpw - 1) / p->bpw + 1;
+  p->threads = 64 * nw;
+  p->m_chunk = m;
+  p->mt = mtw;
+  p->ilp = 1;
+  p->waves = nw;
+  p->tpw = 1;
+  p->ups = p->bps;
+  p->units = p->batches;
+  p->red_cols = 0;
+  size_t off = dgt::align_up((size_t)p->strips * 4, 256);
+  p->part_off = off;
+  p->part_bytes = (size_t)p->strips * p->slots * m * in->tile_n * 4;
+  off = dgt::align_up(off + p->part_bytes, 256);
+  p->quant_off = off;
+  if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
+  p->ws_bytes = off;
+  return true;
+}
+
 bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
+  p->xm = 0;
+  if (plan_fused_xm(in, m, p)) return true;
+  p->xm = 0;
   const uint32_t R = in->lanes, tpc = 64 / R;
   const uint32_t kt = in->k / in->tile_k;
   // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
@@ -252,6 +303,39 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     if (rc) return rc;
     xsrc = reinterpret_cast<const uint8_t*>(xq);
     sxp = sx;
+  }
+  if (p.xm) {
+    XmArgs x;
+    GemmArgs& a = x.g;
+    a.L = L;
+    a.x = xsrc;
+    a.scales = d_scales;
+    a.xscale = sxp;
+    a.w_scale = w_scale;
+    a.y = d_y;
+    a.part = reinterpret_cast<float*>(ws + p.part_off);
+    a.counters = reinterpret_cast<uint32_t*>(ws);
+    a.status = d_status;
+    a.m = m;
+    a.x_row_bytes = xrow;
+    a.y_row = info->n;
+    a.waves = p.waves;
+    a.tpw = p.tpw;
+    a.units = p.units;
+    a.ups = p.ups;
+    a.slots = p.slots;
+    a.red_cols = 0;
+    x.bps = p.bps;
+    x.bpw = p.bpw;
+    x.batches = p.batches;
+    x.xbuf_off = p.xbuf_off;
+    switch (info->fmt) {
+      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, p.wgs, p.lds, st);
+      default: return DGT_E_ARG;
+    }
   }
   for (uint32_t m0 = 0; m0 < m; m0 += p.m_chunk) {
     GemmArgs a;

@@ -217,23 +217,25 @@ __device__ __forceinline__ void stage_issue(const Layer& L, uint32_t t, uint32_t
   const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
   st.words4 = o1 - o0 - L.lanes;
   st.src = L.streams + o0 + L.lanes;
+  // bound checks against the remaining count keep the per-j offsets constant
+  // (nothing lane-dependent is hoisted out of a caller's loop)
+  const int32_t rem = (int32_t)st.words4 - (int32_t)sub_lane;
+  const uint32_t* p = st.src + sub_lane;
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const uint32_t i = sub_lane + j * sub_size;
-    st.v[j] = (i < st.words4) ? st.src[i] : 0u;
-  }
+  for (int j = 0; j < kPre; ++j)
+    st.v[j] = (rem > (int32_t)(j * sub_size)) ? p[j * sub_size] : 0u;
 }
 
 // Returns the number of staged u16 words (including a possible pad word).
 __device__ __forceinline__ uint32_t stage_commit(const Staged& st, uint16_t* words, uint32_t start,
                                                  uint32_t sub_lane, uint32_t sub_size) {
-  uint32_t* dst = reinterpret_cast<uint32_t*>(words + start);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(words + start) + sub_lane;
+  const int32_t rem = (int32_t)st.words4 - (int32_t)sub_lane;
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const uint32_t i = sub_lane + j * sub_size;
-    if (i < st.words4) dst[i] = st.v[j];
-  }
-  for (uint32_t i = sub_lane + kPre * sub_size; i < st.words4; i += sub_size) dst[i] = st.src[i];
+  for (int j = 0; j < kPre; ++j)
+    if (rem > (int32_t)(j * sub_size)) dst[j * sub_size] = st.v[j];
+  const uint32_t* src = st.src + sub_lane;
+  for (int32_t i = kPre * sub_size; i < rem; i += sub_size) dst[i] = src[i];
   return 2 * st.words4;
 }
 

@@ -53,6 +53,22 @@ int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32
 }
 
 template <>
+int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t fn, uint32_t grid, uint32_t lds,
+                             hipStream_t st) {
+#define DGT_XM_CASE(FNV)                                                        \
+  if (fn == FNV) {                                                              \
+    auto k = k_fused_xm<DGT_FMT, FNV>;                                          \
+    if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(FNV)), lds, st, x);    \
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
+  }
+  DGT_XM_CASE(8)
+  DGT_XM_CASE(16)
+#undef DGT_XM_CASE
+  return DGT_E_UNSUPPORTED;
+}
+
+template <>
 int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, uint32_t grid,
                            uint32_t threads, uint32_t lds, hipStream_t st) {
 #define DGT_DECODE_CASE(RR, II)                                                \

@@ -95,6 +95,54 @@ def test_fused_gemm_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     assert (status.cpu().numpy() == 0).all()
 
 
+# Large M: every tile decoded once and its fragments shared through LDS by the
+# waves that own the row blocks (tile_n 128: 16 waves x 16 rows; tile_n 256:
+# 8 waves x 32 rows).  Shapes cover strips finished by one workgroup (direct
+# store) and by several (workspace hand-off), ragged M and idle row blocks.
+XM_CASES = [
+    (FB, 256, 1024, 128, 64, 64, 41),     # one batch per strip
+    (FB, 384, 4096, 128, 64, 64, 42),     # four workgroups per strip
+    (F8, 256, 2048, 128, 64, 64, 43),
+    (F4, 256, 2048, 128, 64, 64, 44),
+    (FE, 512, 1024, 256, 64, 64, 45),     # tile_n 256: two batches per strip
+    (FB, 512, 512, 256, 64, 64, 46),
+    (F4, 256, 1024, 256, 64, 64, 47),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", XM_CASES)
+@pytest.mark.parametrize("m", [17, 65, 100, 256])
+def test_fused_gemm_large_m_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
+    import torch
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, m))
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"],
+                                  status=status, ws=ws)
+    torch.cuda.synchronize()
+    ref = reference(fmt, d, d["x"])
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+    assert (status.cpu().numpy() == 0).all()
+    strips = n // tn
+    assert int(ws[:4 * strips].sum().item()) == 0   # strip counters returned to zero
+
+
+def test_fused_gemm_large_m_repeatable():
+    import torch
+    d, blob = _layer(FB, 384, 4096, 128, 64, 64, 48, m=256)
+    layer = dgt.DeviceLayer(blob)
+    x = x_dev(d["x"])
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, 256))
+    y1 = dgt.dgt_fused_decode_gemm(layer, x, ws=ws).clone()
+    y2 = dgt.dgt_fused_decode_gemm(layer, x, ws=ws).clone()
+    y3 = dgt.dgt_fused_decode_gemm(layer, x[:200].contiguous(), ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)               # fixed accumulation and reduction order
+    assert torch.equal(y3, y1[:200])         # row results do not depend on M in this path
+
+
 def test_fused_gemm_repeatable_and_workspace_reusable():
     import torch
     d, blob = _layer(FB, 256, 4096, 128, 64, 64, 21, m=16)
