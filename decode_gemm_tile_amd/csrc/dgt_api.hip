@@ -160,21 +160,21 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   const uint32_t fn = in->tile_n / 16;
   if (in->lanes != 64 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
   if (m <= (fn == 8 ? 64u : 16u)) return false;  // one register-resident pass covers M
-  const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn);
+  const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn), nt = xm_tiles(fn);
   if (m > nw * mtw * 16) return false;
   const uint32_t kt = in->k / in->tile_k;
-  if (kt % nw) return false;
+  if (kt % nt) return false;
   const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
   const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
   const uint32_t xbuf_off =
-      (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nw * region_bytes + 16, 16);
-  const uint32_t lds = xbuf_off + 2 * nw * 1024;
+      (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nt * region_bytes + 16, 16);
+  const uint32_t lds = xbuf_off + 2 * nt * 1024;
   if (lds > kMaxLds) return false;
   p->xm = 1;
   p->xbuf_off = xbuf_off;
   p->lds = lds;
   p->strips = in->n / in->tile_n;
-  p->bps = kt / nw;
+  p->bps = kt / nt;
   p->batches = p->strips * p->bps;
   p->bpw = (p->batches + kCUs - 1) / kCUs;  // one workgroup per CU, one round
   p->wgs = (p->batches + p->bpw - 1) / p->bpw;
@@ -190,7 +190,8 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->red_cols = 0;
   size_t off = dgt::align_up((size_t)p->strips * 4, 256);
   p->part_off = off;
-  p->part_bytes = (size_t)p->strips * p->slots * m * in->tile_n * 4;
+  // partial slots hold every row block of the workgroup (register layout)
+  p->part_bytes = (size_t)p->strips * p->slots * (nw * mtw * 16) * in->tile_n * 4;
   off = dgt::align_up(off + p->part_bytes, 256);
   p->quant_off = off;
   if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;

@@ -425,18 +425,24 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
 // When M is too large for one wave to hold every row's accumulators, decoded
 // fragments are shared through an LDS ping-pong buffer (the double-buffered
 // decode/compute overlap of [P1 §3.1]).  A workgroup of NW waves works on
-// batches of NW consecutive k-tiles of one strip, one tile per wave.  After
-// every fragment (8 steps) each wave publishes its finished 16x32 B operand
-// into buffer (g & 1); after one barrier every wave multiplies all NW
-// fragments of the batch with its own MTW 16-row blocks of X (A operands of the
-// NW k-ranges stay in registers for the FN fragments that share them), then
-// decodes the next fragment into the other buffer.  Each weight is decoded
-// once for all M <= NW * MTW * 16 rows.  A workgroup runs bpw consecutive
-// batches; each wave owns distinct rows, so accumulators go straight to Y (or
-// to the strip's workspace slot) when the strip changes, with no LDS reduction.
+// batches of NT = NW * ILP consecutive k-tiles of one strip; each wave decodes
+// ILP of them as interleaved chains.  After every fragment (8 steps) each wave
+// publishes its finished 16x32 B operands into buffer (g & 1); after one
+// barrier every wave multiplies all NT fragments of the batch with its own MTW
+// 16-row blocks of X (A operands of the NT k-ranges stay in registers for the
+// FN fragments that share them).  Each weight is decoded once for all
+// M <= NW * MTW * 16 rows.  Registers bound the shape: A takes
+// rows * NT / 4 and the accumulators rows * 2 VGPRs per wave, so a CU holds
+// 16 decode chains at most (tile_n 128: 16 waves x 16 rows, one chain each;
+// tile_n 256: 8 waves x 32 rows).  A workgroup runs bpw consecutive batches;
+// each wave owns distinct rows, so accumulators go straight to Y (or to the
+// strip's workspace slot) when the strip changes, with no LDS reduction.
+template <bool V>
+struct BoolC { static constexpr bool value = V; };
+
 struct XmArgs {
   GemmArgs g;
-  uint32_t bps;        // batches per strip (k-tiles / NW)
+  uint32_t bps;        // batches per strip (k-tiles / NT)
   uint32_t bpw;        // batches per workgroup
   uint32_t batches;    // total batches (strips * bps)
   uint32_t xbuf_off;   // byte offset of the fragment buffers in LDS (16-aligned)
@@ -444,36 +450,57 @@ struct XmArgs {
 
 __host__ __device__ constexpr int xm_waves(int FN) { return FN == 8 ? 16 : 8; }
 __host__ __device__ constexpr int xm_row_blocks(int FN) { return FN == 8 ? 1 : 2; }
+__host__ __device__ constexpr int xm_ilp(int FN) { return 1; }
+__host__ __device__ constexpr int xm_tiles(int FN) { return xm_waves(FN) * xm_ilp(FN); }
 
+// Partials of a strip shared by several workgroups are kept in the
+// accumulators' register layout (slot, wave, row block, fragment, float pair,
+// lane), so every 8-byte store and load of a wave covers 512 contiguous bytes.
+// A slot holds the full NW * MTW * 16 rows.
 template <int FN, int MTW>
 __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW],
                                          uint32_t strip, uint32_t* flag, float out_scale) {
+  constexpr int NW = xm_waves(FN);
+  constexpr uint32_t kSlotPairs = NW * MTW * FN * 2 * 64;  // float pairs per slot
   const GemmArgs& a = x.g;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t M = a.m, TN = FN * 16, wg = blockIdx.x;
   const uint32_t f = strip_first_wg(strip, x.bps, x.bpw), l = strip_last_wg(strip, x.bps, x.bpw);
+  auto store_y = [&](int fn, int mt, floatx4 v) {
+    const uint32_t col = strip * TN + fn * 16 + (lane & 15);
+    const uint32_t m0 = (wave * MTW + mt) * 16 + 4 * (lane >> 4);
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const uint32_t col = fn * 16 + (lane & 15);
+    for (int i = 0; i < 4; ++i)
+      if (m0 + i < M) a.y[(size_t)(m0 + i) * a.y_row + col] = v[i] * out_scale;
+  };
+  auto pair_ptr = [&](uint32_t slot, int fn, int mt, int h) {
+    return reinterpret_cast<uint64_t*>(a.part) + ((size_t)strip * a.slots + slot) * kSlotPairs +
+           ((((wave * MTW + mt) * FN + fn) * 2 + h) * 64 + lane);
+  };
+  if (f == l) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        store_y(fn, mt, acc[fn][mt]);
+        acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    return;
+  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
+      // agent-scope stores: coherent across XCDs without an L2 writeback
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t m = (wave * MTW + mt) * 16 + 4 * (lane >> 4) + i;
-        if (m < M) {
-          if (f == l) {
-            a.y[(size_t)m * a.y_row + strip * TN + col] = acc[fn][mt][i] * out_scale;
-          } else {
-            // agent-scope store: coherent across XCDs without an L2 writeback
-            __hip_atomic_store(&a.part[(((size_t)strip * a.slots + (wg - f)) * M + m) * TN + col],
-                               acc[fn][mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        acc[fn][mt][i] = 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const uint64_t bits = (uint64_t)__float_as_uint(acc[fn][mt][2 * h]) |
+                              ((uint64_t)__float_as_uint(acc[fn][mt][2 * h + 1]) << 32);
+        __hip_atomic_store(pair_ptr(wg - f, fn, mt, h), bits, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
+      acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-  if (f == l) return;
   // hand-off to the last workgroup of the strip, ordered as in reduce_and_store
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -487,22 +514,30 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
   __syncthreads();  // flag is rewritten by the next flush
   if (!last) return;
   const uint32_t n = l - f + 1;
-  for (uint32_t idx = threadIdx.x; idx < M * TN; idx += blockDim.x) {
-    const uint32_t m = idx / TN, col = idx % TN;
-    float v = 0.f;
-    for (uint32_t g = 0; g < n; ++g)
-      v += __hip_atomic_load(&a.part[(((size_t)strip * a.slots + g) * M + m) * TN + col],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.y[(size_t)m * a.y_row + strip * TN + col] = v * out_scale;
-  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (uint32_t g = 0; g < n; ++g) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint64_t bits =
+              __hip_atomic_load(pair_ptr(g, fn, mt, h), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[2 * h] += __uint_as_float((uint32_t)bits);
+          v[2 * h + 1] += __uint_as_float((uint32_t)(bits >> 32));
+        }
+      }
+      store_y(fn, mt, v);
+    }
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// R = 64 lanes (one tile per wave) and tile_k = 64 only.
+// R = 64 lanes (one tile per chain) and tile_k = 64 only.
 template <int FMT, int FN>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
-  constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN);
+  constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr uint32_t R = 64, FW = 32, TK = 64, FK = TK / FW, G = FK * FN;
   extern __shared__ __align__(16) uint8_t smem[];
   const GemmArgs& a = x.g;
@@ -522,103 +557,138 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   const uint32_t b0 = blockIdx.x * x.bpw, b1 = min(b0 + x.bpw, x.batches);
-  const uint32_t region = wave * L.region_words;
   floatx4 acc[FN][MTW];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (uint32_t b = b0; b < b1; ++b) {
-    const uint32_t strip = b / x.bps, kt0 = (b % x.bps) * NW;
-    const uint32_t t = strip * L.kt + kt0 + wave;
-    Chain ch[1];
-    Staged stg;
-    stage_issue(L, t, lane, 64u, stg);
-    ch[0].x = L.streams[L.index[t] + lane];
-    ch[0].lim = uniform(L.steps - (uint32_t)L.ktab[t]);
+    const uint32_t strip = b / x.bps, kt0 = (b % x.bps) * NT;
+    // chain c of this wave decodes batch tile j = c * NW + wave
+    uint32_t tj[ILP];
+    Chain ch[ILP];
+    Staged stg[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      tj[c] = strip * L.kt + kt0 + c * NW + wave;
+      stage_issue(L, tj[c], lane, 64u, stg[c]);
+      ch[c].x = L.streams[L.index[tj[c]] + lane];
+      ch[c].lim = L.steps - (uint32_t)L.ktab[tj[c]];
+    }
     if (b == b0) build_lut(fq, L.alphabet, lut, cum);
     __syncthreads();  // LUT complete; the previous batch's fragment reads are done
-    {
-      const uint32_t n = uniform(stage_commit(stg, words, region, lane, 64u));
+    uint32_t lim_min = 0xFFFFFFFFu;
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t region = (wave * ILP + c) * L.region_words;
+      const uint32_t n = uniform(stage_commit(stg[c], words, region, lane, 64u));
       const uint32_t base = kLutBytes + kCumBytes + 2 * region;
-      ch[0].p0 = base; ch[0].s0 = base; ch[0].e0 = base + 2 * n;
-      ch[0].p1 = base; ch[0].s1 = base; ch[0].e1 = base + 2 * n;
+      ch[c].p0 = base; ch[c].s0 = base; ch[c].e0 = base + 2 * n;
+      ch[c].p1 = base; ch[c].s1 = base; ch[c].e1 = base + 2 * n;
+      lim_min = min(lim_min, uniform(ch[c].lim));
     }
-    const uint32_t lim_min = ch[0].lim;
-    const uint32_t k0_lane = (kt0 + wave) * TK + 8 * (lane >> 4);
-    auto load_raw = [&](uint32_t g) -> u32x2 {
-      const uint8_t* rp = L.raw + (size_t)t * FN * 16 * TK + (size_t)g * 8 * R + lane * 8;
+    auto load_raw = [&](int c, uint32_t g) -> u32x2 {
+      const uint8_t* rp = L.raw + (size_t)tj[c] * FN * 16 * TK + (size_t)g * 8 * R + lane * 8;
       return *reinterpret_cast<const u32x2*>(rp);
     };
-    auto load_scale = [&](uint32_t g) -> float {
+    auto load_scale = [&](int c, uint32_t g) -> float {
       const uint32_t fkg = g / FN, fng = g % FN;
       const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
-      const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane + fkg * FW) / 128];
+      const uint32_t k0 = (kt0 + c * NW + wave) * TK + 8 * (lane >> 4) + fkg * FW;
+      const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
       return __uint_as_float((uint32_t)sb << 16);
     };
-    u32x2 raw_n = {0u, 0u};
-    float sc_n = 0.f;
-    if constexpr (FMT == BF16) raw_n = load_raw(0);
-    if constexpr (FMT == INT4) sc_n = load_scale(0);
+    u32x2 raw_n[ILP];
+    float sc_n[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      raw_n[c] = u32x2{0u, 0u};
+      sc_n[c] = 0.f;
+      if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
+      if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
+    }
+    // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
+    const uint8_t* xp[MTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      const uint32_t row = row0 + mt * 16 + (lane & 15);
+      xp[mt] = a.x + (size_t)min(row, a.m - 1) * a.x_row_bytes +
+               ((size_t)kt0 * TK + 8 * (lane >> 4)) * 2;
+    }
     for (uint32_t fk = 0; fk < FK; ++fk) {
-      // X for this wave's rows and the NW k-ranges of fragment column block fk
-      // (k-tiles of 64 columns: the NW loads share one address register)
-      u32x4 A[NW][MTW];
+      // X for this wave's rows and the NT k-ranges of fragment column block fk
+      u32x4 A[NT][MTW];
+      if (has_rows) {
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
-        const uint32_t row = row0 + mt * 16 + (lane & 15);
-        const uint8_t* xp = a.x + (size_t)min(row, a.m - 1) * a.x_row_bytes +
-                            ((size_t)kt0 * TK + fk * FW + 8 * (lane >> 4)) * 2;
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(xp + j * TK * 2);
-          A[j][mt] = row < a.m ? v : u32x4{0u, 0u, 0u, 0u};
-        }
+          for (int mt = 0; mt < MTW; ++mt)
+            A[j][mt] = *reinterpret_cast<const u32x4*>(xp[mt] + fk * FW * 2 + j * TK * 2);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const uint32_t g = fk * FN + fn;
         const uint32_t s0 = g * 8;
         const uint32_t gn = min(g + 1, G - 1);
-        const u32x2 raw = raw_n;
-        const float sc = sc_n, nsc8 = -8.f * sc_n;
-        if constexpr (FMT == BF16) raw_n = load_raw(gn);
-        if constexpr (FMT == INT4) sc_n = load_scale(gn);
-        uint32_t e[8];
-        // payload steps (at most the last 16) fall in the last two fragments
-        if (fn < FN - 2 || s0 + 7 < lim_min) {
+        u32x2 raw[ILP];
+        float sc[ILP], nsc8[ILP];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            uint32_t sy[1];
-            step_all<64, false, 1>(ch, lut, smem, s0 + i, false, sy);
-            e[i] = sy[0];
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            uint32_t sy[1];
-            step_all<64, true, 1>(ch, lut, smem, s0 + i, false, sy);
-            e[i] = sy[0];
-          }
+        for (int c = 0; c < ILP; ++c) {
+          raw[c] = raw_n[c];
+          sc[c] = sc_n[c];
+          nsc8[c] = -8.f * sc[c];
+          if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
+          if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
         }
-        const BOp bop = make_b<FMT>(e, raw, sc, nsc8);
-        uint8_t* buf = xbuf + (g & 1) * (NW * 1024);
-        *reinterpret_cast<u32x4*>(buf + wave * 1024 + lane * 16) = bop.v;
+        uint32_t e[ILP][8];
+        auto steps = [&](auto careful) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            uint32_t sy[ILP];
+            step_all<64, decltype(careful)::value, ILP>(ch, lut, smem, s0 + i, false, sy);
+#pragma unroll
+            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+          }
+        };
+        // payload steps (at most the last 16) fall in the last two fragments
+        if (fn < FN - 2 || s0 + 7 < lim_min) steps(BoolC<false>{}); else steps(BoolC<true>{});
+        uint8_t* buf = xbuf + (g & 1) * (NT * 1024);
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) {
+          const BOp bop = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
+          *reinterpret_cast<u32x4*>(buf + (c * NW + wave) * 1024 + lane * 16) = bop.v;
+        }
         __syncthreads();
         if (has_rows) {
+          // fragments are read kXB at a time so their LDS latencies overlap
+          constexpr int kXB = 4;
 #pragma unroll
-          for (int j = 0; j < NW; ++j) {
-            BOp bj;
-            bj.v = *reinterpret_cast<const u32x4*>(buf + j * 1024 + lane * 16);
+          for (int j0 = 0; j0 < NT; j0 += kXB) {
+            BOp bq[kXB];
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) acc[fn][mt] = mfma<FMT>(A[j][mt], bj, acc[fn][mt]);
+            for (int q = 0; q < kXB; ++q)
+              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (j0 + q) * 1024 + lane * 16);
+#pragma unroll
+            for (int q = 0; q < kXB; ++q)
+#pragma unroll
+              for (int mt = 0; mt < MTW; ++mt)
+                acc[fn][mt] = mfma<FMT>(A[j0 + q][mt], bq[q], acc[fn][mt]);
+          }
+          // keep each group of reads ahead of its products
+#pragma unroll
+          for (int j0 = 0; j0 < NT; j0 += kXB) {
+            __builtin_amdgcn_sched_group_barrier(0x100, kXB, 0);        // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, kXB * MTW, 0);  // MFMA
           }
         }
       }
     }
     if (a.status) {
-      const uint32_t fl = final_flags<64>(ch[0], L.steps, false);
-      if (lane == 0) a.status[t] = (int32_t)fl;
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        const uint32_t fl = final_flags<64>(ch[c], L.steps, false);
+        if (lane == 0) a.status[tj[c]] = (int32_t)fl;
+      }
     }
     if (b + 1 == b1 || (b + 1) / x.bps != strip) xm_flush<FN, MTW>(x, acc, strip, flag, out_scale);
   }
