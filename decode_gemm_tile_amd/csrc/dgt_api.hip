@@ -136,7 +136,8 @@ int device_supported(const dgt_info* in) {
 }
 
 struct FusedPlan {
-  uint32_t mt, ilp, waves, threads, tpw, ups, units, wgs, slots, strips, red_cols, lds, m_chunk;
+  uint32_t mt, mix, waves, threads, cpw, n2, chains, cps, wgs, slots, strips, red_cols, lds;
+  uint32_t m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
   // large-M variant (fragments shared through LDS): used when xm != 0
   uint32_t xm, bps, bpw, batches, xbuf_off;
@@ -182,11 +183,12 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->threads = 64 * nw;
   p->m_chunk = m;
   p->mt = mtw;
-  p->ilp = 1;
+  p->mix = 0;
   p->waves = nw;
-  p->tpw = 1;
-  p->ups = p->bps;
-  p->units = p->batches;
+  p->cpw = p->bpw;
+  p->n2 = 0;
+  p->chains = p->batches;
+  p->cps = p->bps;
   p->red_cols = 0;
   size_t off = dgt::align_up((size_t)p->strips * 4, 256);
   p->part_off = off;
@@ -199,35 +201,49 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   return true;
 }
 
+// Register-resident path: every wave keeps its rows' accumulators; M above
+// one pass is handled in chunks of m_chunk rows.  Chains per workgroup C is
+// the layer's chains over the CUs (one round) when the wave cap allows it;
+// beyond the cap the first n2 waves take two chains each (MIX kernels).
 bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->xm = 0;
   if (plan_fused_xm(in, m, p)) return true;
   p->xm = 0;
   const uint32_t R = in->lanes, tpc = 64 / R;
   const uint32_t kt = in->k / in->tile_k;
+  if (kt % tpc) return false;
   // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
   p->m_chunk = std::min<uint32_t>(m, in->tile_n == 256 ? 16 : 64);
   p->mt = p->m_chunk <= 16 ? 1 : 4;
   p->strips = in->n / in->tile_n;
-  const uint32_t chains_total = in->tiles / tpc;
-  p->ilp = (kt % (2 * tpc) == 0 && chains_total >= kCUs * 4 * 5) ? 2 : 1;
-  if (kt % (p->ilp * tpc)) return false;
-  p->tpw = p->ilp * tpc;
-  p->ups = kt / p->tpw;
-  p->units = p->strips * p->ups;
+  p->chains = in->tiles / tpc;
+  p->cps = kt / tpc;
   const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
-  const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
-  const uint32_t per_wave = p->ilp * tpc * region_bytes;
-  if (kLutBytes + kCumBytes + per_wave > kMaxLds) return false;
-  const uint32_t lds_cap = (kMaxLds - kLutBytes - kCumBytes) / per_wave;
-  const uint32_t fn = in->tile_n / 16;
-  const uint32_t reg_cap =
-      fused_max_threads(R, fn == 8 ? 8 : 16, p->mt, p->ilp) / 64;  // VGPR budget per lane
-  p->waves = pick_waves(p->units, p->ups, std::min(lds_cap, reg_cap));
+  const uint32_t chain_lds = tpc * ((words + 7) & ~7u) * 2;
+  if (kLutBytes + kCumBytes + chain_lds > kMaxLds) return false;
+  const uint32_t lds_cap = (kMaxLds - kLutBytes - kCumBytes) / chain_lds;
+  const uint32_t fn = in->tile_n / 16 == 8 ? 8 : 16;
+  const uint32_t w1 = fused_max_threads(R, fn, p->mt, 1) / 64;  // one chain per wave
+  const uint32_t w2 = fused_max_threads(R, fn, p->mt, 2) / 64;  // two-chain kernels
+  uint32_t c = (p->chains + kCUs - 1) / kCUs;
+  c = std::min(c, p->cps);
+  c = std::min(c, lds_cap);
+  if (c > w1 && p->cps % 2) c = w1;
+  if (c <= w1) {
+    p->mix = 0;
+    p->n2 = 0;
+    p->waves = c;
+  } else {
+    c = std::min(c & ~1u, 2 * w2);
+    p->mix = 1;
+    p->n2 = c - w2;
+    p->waves = w2;
+  }
+  p->cpw = c;
   p->threads = 64 * std::max(p->waves, 4u);       // the LUT build uses >= 4 waves
-  p->wgs = (p->units + p->waves - 1) / p->waves;
-  p->slots = (p->ups + p->waves - 1) / p->waves + 1;
-  p->lds = kLutBytes + kCumBytes + (p->threads / 64) * per_wave;
+  p->wgs = (p->chains + c - 1) / c;
+  p->slots = (p->cps + c - 1) / c + 1;
+  p->lds = kLutBytes + kCumBytes + c * chain_lds;
   uint32_t rc = in->tile_n;
   while (rc > 16 && (uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) rc /= 2;
   if ((uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) {
@@ -321,9 +337,11 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     a.x_row_bytes = xrow;
     a.y_row = info->n;
     a.waves = p.waves;
-    a.tpw = p.tpw;
-    a.units = p.units;
-    a.ups = p.ups;
+    a.tpw = 1;
+    a.chains = p.chains;
+    a.cps = p.cps;
+    a.cpw = p.cpw;
+    a.n2 = 0;
     a.slots = p.slots;
     a.red_cols = 0;
     x.bps = p.bps;
@@ -353,24 +371,26 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     a.x_row_bytes = xrow;
     a.y_row = info->n;
     a.waves = p.waves;
-    a.tpw = p.tpw;
-    a.units = p.units;
-    a.ups = p.ups;
+    a.tpw = 64 / info->lanes;
+    a.chains = p.chains;
+    a.cps = p.cps;
+    a.cpw = p.cpw;
+    a.n2 = p.n2;
     a.slots = p.slots;
     a.red_cols = p.red_cols;
     const uint32_t grid = p.wgs, threads = p.threads;
     switch (info->fmt) {
       case DGT_FMT_INT8:
-        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       case DGT_FMT_INT4:
-        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
-        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       case DGT_FMT_BF16_SPLIT:
-        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, p.ilp, grid, threads, p.lds, st);
+        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       default:
         rc = DGT_E_ARG;
@@ -495,8 +515,10 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     a.y_row = n;
     a.waves = waves;
     a.tpw = p.tpw;
-    a.units = p.units;
-    a.ups = p.ups;
+    a.chains = p.units;
+    a.cps = p.ups;
+    a.cpw = waves;
+    a.n2 = 0;
     a.slots = p.slots;
     uint32_t rc_cols = tile_n;
     while (rc_cols > 16 && (uint64_t)waves * a.m * rc_cols * 4 > lds) rc_cols /= 2;

@@ -19,22 +19,22 @@ bool set_lds(K kernel, uint32_t bytes) {
          hipSuccess;
 }
 
-template <int R, int FN, int MT, int ILP>
+template <int R, int FN, int MT, bool MIX>
 int fused_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
-  auto k = k_fused<DGT_FMT, R, FN, MT, ILP>;
+  auto k = k_fused<DGT_FMT, R, FN, MT, MIX>;
   if (!set_lds(k, lds)) return DGT_E_HIP;
   hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
 }
 
 template <int R, int FN>
-int fused_r(const GemmArgs& a, uint32_t mt, uint32_t ilp, uint32_t grid, uint32_t threads,
+int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t threads,
             uint32_t lds, hipStream_t st) {
-  if (mt == 1 && ilp == 1) return fused_t<R, FN, 1, 1>(a, grid, threads, lds, st);
-  if (mt == 1 && ilp == 2) return fused_t<R, FN, 1, 2>(a, grid, threads, lds, st);
+  if (mt == 1 && !mix) return fused_t<R, FN, 1, false>(a, grid, threads, lds, st);
+  if (mt == 1 && mix) return fused_t<R, FN, 1, true>(a, grid, threads, lds, st);
   if constexpr (FN <= 8) {
-    if (mt == 4 && ilp == 1) return fused_t<R, FN, 4, 1>(a, grid, threads, lds, st);
-    if (mt == 4 && ilp == 2) return fused_t<R, FN, 4, 2>(a, grid, threads, lds, st);
+    if (mt == 4 && !mix) return fused_t<R, FN, 4, false>(a, grid, threads, lds, st);
+    if (mt == 4 && mix) return fused_t<R, FN, 4, true>(a, grid, threads, lds, st);
   }
   return DGT_E_UNSUPPORTED;
 }
@@ -42,13 +42,12 @@ int fused_r(const GemmArgs& a, uint32_t mt, uint32_t ilp, uint32_t grid, uint32_
 }  // namespace
 
 template <>
-int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt,
-                          uint32_t ilp, uint32_t grid, uint32_t threads, uint32_t lds,
-                          hipStream_t st) {
-  if (lanes == 64 && fn == 8) return fused_r<64, 8>(a, mt, ilp, grid, threads, lds, st);
-  if (lanes == 64 && fn == 16) return fused_r<64, 16>(a, mt, ilp, grid, threads, lds, st);
-  if (lanes == 32 && fn == 8) return fused_r<32, 8>(a, mt, ilp, grid, threads, lds, st);
-  if (lanes == 32 && fn == 16) return fused_r<32, 16>(a, mt, ilp, grid, threads, lds, st);
+int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt, bool mix,
+                          uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
+  if (lanes == 64 && fn == 8) return fused_r<64, 8>(a, mt, mix, grid, threads, lds, st);
+  if (lanes == 64 && fn == 16) return fused_r<64, 16>(a, mt, mix, grid, threads, lds, st);
+  if (lanes == 32 && fn == 8) return fused_r<32, 8>(a, mt, mix, grid, threads, lds, st);
+  if (lanes == 32 && fn == 16) return fused_r<32, 16>(a, mt, mix, grid, threads, lds, st);
   return DGT_E_UNSUPPORTED;
 }
 

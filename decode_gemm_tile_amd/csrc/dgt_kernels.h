@@ -38,23 +38,37 @@ struct GemmArgs {
   uint32_t m;                // rows of X / Y in this launch (<= 16 * MT)
   uint32_t x_row_bytes;      // row stride of x in bytes
   uint32_t y_row;            // row stride of y in floats (= N)
-  uint32_t waves;            // waves (= units) per workgroup
-  uint32_t tpw;              // k-tiles per unit (one wave's work)
-  uint32_t units;            // total units: strips * ups
-  uint32_t ups;              // units per strip
+  uint32_t waves;            // waves per workgroup
+  uint32_t tpw;              // dense path: k-tiles per unit (one wave's work)
+  uint32_t chains;           // schedule units in the layer (fused: chains; dense: units)
+  uint32_t cps;              // units per strip
+  uint32_t cpw;              // units per workgroup
+  uint32_t n2;               // waves that take two units (the first n2 waves)
   uint32_t slots;            // partial slots per strip in the workspace
   uint32_t red_cols;         // tile_n columns reduced per LDS pass
 };
 
-// Static schedule: units (ILP chains of consecutive k-tiles of one strip) are
-// numbered strip-major; workgroup b takes units [b*W, b*W + W), so it covers
-// the tail of one strip and the head of the next at most (W <= ups).  The
-// workgroups touching strip s are floor(s*ups/W) .. floor(((s+1)*ups-1)/W).
-__device__ __forceinline__ uint32_t strip_first_wg(uint32_t s, uint32_t ups, uint32_t W) {
-  return (uint32_t)(((uint64_t)s * ups) / W);
+// Static schedule: units (a chain of TPC consecutive k-tiles of one strip for
+// the fused path) are numbered strip-major; workgroup b takes units
+// [b*C, b*C + C), C <= units per strip, so it covers the tail of one strip and
+// the head of the next at most.  Its first n2 waves take two units each, the
+// others one (n2 > 0 only with C and the units per strip even, so a wave's
+// pair never straddles a strip): this evens the per-SIMD work when C is not a
+// multiple of the wave count.  The workgroups touching strip s are
+// floor(s*cps/C) .. floor(((s+1)*cps-1)/C).
+__device__ __forceinline__ uint32_t strip_first_wg(uint32_t s, uint32_t cps, uint32_t C) {
+  return (uint32_t)(((uint64_t)s * cps) / C);
 }
-__device__ __forceinline__ uint32_t strip_last_wg(uint32_t s, uint32_t ups, uint32_t W) {
-  return (uint32_t)(((uint64_t)(s + 1) * ups - 1) / W);
+__device__ __forceinline__ uint32_t strip_last_wg(uint32_t s, uint32_t cps, uint32_t C) {
+  return (uint32_t)(((uint64_t)(s + 1) * cps - 1) / C);
+}
+// first unit of wave w inside its workgroup's range, and how many waves hold
+// the first r units of the range
+__device__ __forceinline__ uint32_t wave_first_unit(uint32_t w, uint32_t n2) {
+  return w < n2 ? 2 * w : n2 + w;
+}
+__device__ __forceinline__ uint32_t waves_covering(uint32_t r, uint32_t n2) {
+  return r <= 2 * n2 ? (r + 1) / 2 : n2 + (r - 2 * n2);
 }
 
 template <int FMT>
@@ -152,12 +166,13 @@ template <int FN, int MT>
 __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
                                                  float* red, float out_scale) {
   const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t M = a.m, TN = FN * 16, W = a.waves, RC = a.red_cols;
+  const uint32_t M = a.m, TN = FN * 16, C = a.cpw, RC = a.red_cols;
   const uint32_t wg = blockIdx.x;
-  const uint32_t u0 = wg * W, u1 = min(u0 + W, a.units);
-  const uint32_t nw = u1 - u0;                       // active waves
-  const uint32_t sA = u0 / a.ups, sB = (u1 - 1) / a.ups;
-  const uint32_t split = (sA == sB) ? nw : (sA + 1) * a.ups - u0;  // waves in strip A
+  const uint32_t u0 = wg * C, u1 = min(u0 + C, a.chains);
+  const uint32_t nw = waves_covering(u1 - u0, a.n2);           // active waves
+  const uint32_t sA = u0 / a.cps, sB = (u1 - 1) / a.cps;
+  const uint32_t split =                                         // waves in strip A
+      (sA == sB) ? nw : waves_covering((sA + 1) * a.cps - u0, a.n2);
   const uint32_t nstrips = (sA == sB) ? 1u : 2u;
   __syncthreads();  // LUT / staged streams are no longer needed
   for (uint32_t c0 = 0; c0 < TN; c0 += RC) {
@@ -185,7 +200,7 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
         const uint32_t w0 = k ? split : 0u, w1 = k ? nw : split;
         float v = 0.f;
         for (uint32_t w = w0; w < w1; ++w) v += red[(size_t)w * M * RC + idx];
-        const uint32_t f = strip_first_wg(s, a.ups, W), l = strip_last_wg(s, a.ups, W);
+        const uint32_t f = strip_first_wg(s, a.cps, C), l = strip_last_wg(s, a.cps, C);
         if (f == l) {
           a.y[(size_t)m * a.y_row + s * TN + col] = v * out_scale;
         } else {
@@ -207,7 +222,7 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
   __syncthreads();
   if (t < nstrips) {
     const uint32_t s = t ? sB : sA;
-    const uint32_t f = strip_first_wg(s, a.ups, W), l = strip_last_wg(s, a.ups, W);
+    const uint32_t f = strip_first_wg(s, a.cps, C), l = strip_last_wg(s, a.cps, C);
     uint32_t last = 0;
     if (f != l) {
       const uint32_t old = __hip_atomic_fetch_add(&a.counters[s], 1u, __ATOMIC_RELAXED,
@@ -220,7 +235,7 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
   for (uint32_t k = 0; k < nstrips; ++k) {
     if (!last_flag[k]) continue;
     const uint32_t s = k ? sB : sA;
-    const uint32_t n = strip_last_wg(s, a.ups, W) - strip_first_wg(s, a.ups, W) + 1;
+    const uint32_t n = strip_last_wg(s, a.cps, C) - strip_first_wg(s, a.cps, C) + 1;
     for (uint32_t idx = t; idx < M * TN; idx += blockDim.x) {
       const uint32_t m = idx / TN, col = idx % TN;
       float v = 0.f;
@@ -235,8 +250,11 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
 }
 
 // --------------------------------------------------------------- fused GEMM
-// FN = tile_n / 16 row bands per tile, MT = 16-row blocks of X, ILP = chains
-// per wave.  LDS: LUT | cumulative table | staged stream regions.
+// FN = tile_n / 16 row bands per tile, MT = 16-row blocks of X.  A wave runs
+// one or two chains (a chain is one tile for R = 64, two for R = 32); MIX
+// kernels hold both code paths and the first n2 waves take two chains
+// interleaved step by step.  LDS: LUT | cumulative table | staged stream
+// regions (one per tile of the workgroup).
 // Workgroup size cap per variant: kernels whose registers fit in 128 VGPRs run
 // up to 16 waves per workgroup; the others (more row bands or row blocks of
 // accumulators) stay at 8 waves with up to 256 VGPRs.
@@ -247,36 +265,163 @@ __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
   return (MT == 1 && FN <= 8) ? 1024u : 512u;
 }
 
+// Decode and multiply ILP chains (ch[0..ILP)) of one strip into acc.
 template <int FMT, int R, int FN, int MT, int ILP>
-__global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(GemmArgs a) {
+__device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut,
+                                             const uint8_t* smem, Chain (&chs)[2],
+                                             const uint32_t (&tile_lane)[2],
+                                             const uint32_t (&k0_lane)[2], uint32_t strip,
+                                             floatx4 (&acc)[FN][MT]) {
+  const Layer& L = a.L;
+  constexpr uint32_t FW = R / 2;  // fragment width (columns)
+  Chain (&ch)[ILP] = *reinterpret_cast<Chain(*)[ILP]>(&chs[0]);
+  const uint32_t lane = lane_id();
+  const bool upper = lane >= 32;
+  // the word pointers are wave-uniform: keep them (and their updates) scalar
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    ch[c].p0 = uniform(ch[c].p0); ch[c].e0 = uniform(ch[c].e0); ch[c].s0 = uniform(ch[c].s0);
+    ch[c].p1 = uniform(ch[c].p1); ch[c].e1 = uniform(ch[c].e1); ch[c].s1 = uniform(ch[c].s1);
+  }
+  uint32_t lim_min = ch[0].lim;
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    lim_min = min(lim_min, uniform(ch[c].lim));
+    if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
+  }
+  const uint32_t FK = L.tile_k / FW;
+  const uint32_t G = FK * FN;
+  const uint32_t kgroups = L.k / 128;
+  // operands that come from global memory are fetched one fragment (raw
+  // bytes, scales) or one column block (X) ahead of their use
+  auto load_raw = [&](int c, uint32_t g) -> u32x2 {
+    const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
+                        (size_t)g * 8 * R + (lane % R) * 8;
+    return *reinterpret_cast<const u32x2*>(rp);
+  };
+  auto load_scale = [&](int c, uint32_t g) -> float {
+    const uint32_t fkg = g / FN, fng = g % FN;
+    const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
+    const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fkg * FW) / 128];
+    return __uint_as_float((uint32_t)sb << 16);
+  };
+  u32x2 raw_n[ILP];
+  float sc_n[ILP];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    raw_n[c] = u32x2{0u, 0u};
+    sc_n[c] = 0.f;
+    if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
+    if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
+  }
+  constexpr bool kPrefetchA = (MT == 1);
+  u32x4 A_n[ILP][MT];
+  if constexpr (kPrefetchA) {
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c]);
+  }
+  for (uint32_t fk = 0; fk < FK; ++fk) {
+    u32x4 A[ILP][MT];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (kPrefetchA) {
+          A[c][mt] = A_n[c][mt];
+          if (fk + 1 < FK)
+            A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + (fk + 1) * FW);
+        } else {
+          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
+        }
+      }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const uint32_t g = fk * FN + fn;
+      const uint32_t s0 = g * 8;
+      const uint32_t gn = min(g + 1, G - 1);
+      u32x2 raw[ILP];
+      float sc[ILP], nsc8[ILP];
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        raw[c] = raw_n[c];
+        sc[c] = sc_n[c];
+        nsc8[c] = -8.f * sc[c];
+        if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
+        if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
+      }
+      uint32_t e[ILP][8];
+      // payload steps (at most the last 16) fall in the last two fragments
+      if (fn < FN - 2 || s0 + 7 < lim_min) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t sy[ILP];
+          step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
+#pragma unroll
+          for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t sy[ILP];
+          step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
+#pragma unroll
+          for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) {
+        const BOp b = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = mfma<FMT>(A[c][mt], b, acc[fn][mt]);
+      }
+    }
+  }
+  if (a.status) {
+    const uint32_t half_lane = lane & 31;
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
+      if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+    }
+  }
+}
+
+template <int FMT, int R, int FN, int MT, bool MIX>
+__global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_fused(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
   uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
   const Layer& L = a.L;
   constexpr uint32_t TPC = 64 / R;  // tiles per chain
-  constexpr uint32_t FW = R / 2;    // fragment width (columns)
 
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t unit = uniform(blockIdx.x * a.waves + wave);
-  const bool active = (wave < a.waves) && (unit < a.units);
-  const uint32_t strip = active ? unit / a.ups : 0u;
-  const uint32_t kt_first = active ? (unit % a.ups) * a.tpw : 0u;
+  const uint32_t u0 = blockIdx.x * a.cpw, u1 = min(u0 + a.cpw, a.chains);
+  const uint32_t cw = wave_first_unit(wave, a.n2);
+  // chains of this wave: 2 for the first n2 waves, else 1; none past the range
+  uint32_t nch = (MIX && wave < a.n2) ? 2u : 1u;
+  if (u0 + cw >= u1) nch = 0;
+  else nch = min(nch, u1 - u0 - cw);
+  const uint32_t chain0 = u0 + cw;
+  const uint32_t strip = nch ? chain0 / a.cps : 0u;
+  const uint32_t kt_first = nch ? (chain0 % a.cps) * TPC : 0u;
   const bool upper = lane >= 32;
   const uint32_t half_lane = lane & 31;
 
-  Chain ch[ILP];
-  uint32_t tile_lane[ILP];
-  uint32_t k0_lane[ILP];
-  Staged stg[ILP];
-  const uint32_t region0 = wave * ILP * TPC * L.region_words;
+  Chain ch[2];
+  uint32_t tile_lane[2] = {0u, 0u};
+  uint32_t k0_lane[2] = {0u, 0u};
+  Staged stg[2];
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
   // 3) write the streams to LDS
-  if (active) {
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) {
+  for (int c = 0; c < 2; ++c) {
+    if (c < (int)nch) {
       const uint32_t ta = strip * L.kt + kt_first + c * TPC;
       const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
       tile_lane[c] = t_l;
@@ -288,11 +433,11 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
     }
   }
   build_lut(fq, L.alphabet, lut, cum);
-  __syncthreads();  // LUT complete; each wave's staged stream is private to it
-  if (active) {
+  __syncthreads();  // LUT complete; each wave's staged streams are private to it
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      const uint32_t ra = region0 + c * TPC * L.region_words;
+  for (int c = 0; c < 2; ++c) {
+    if (c < (int)nch) {
+      const uint32_t ra = (cw + c) * TPC * L.region_words;
       const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
       const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
                                          R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
@@ -309,111 +454,14 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, ILP)) void k_fused(Gem
   for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  if (active) {
-    uint32_t lim_min = ch[0].lim;
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      lim_min = min(lim_min, uniform(ch[c].lim));
-      if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
-    }
-    const uint32_t FK = L.tile_k / FW;
-    const uint32_t G = FK * FN;
-    const uint32_t kgroups = L.k / 128;
-    // operands that come from global memory are fetched one fragment (raw
-    // bytes, scales) or one column block (X) ahead of their use
-    auto load_raw = [&](int c, uint32_t g) -> u32x2 {
-      const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
-                          (size_t)g * 8 * R + (lane % R) * 8;
-      return *reinterpret_cast<const u32x2*>(rp);
-    };
-    auto load_scale = [&](int c, uint32_t g) -> float {
-      const uint32_t fkg = g / FN, fng = g % FN;
-      const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
-      const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fkg * FW) / 128];
-      return __uint_as_float((uint32_t)sb << 16);
-    };
-    u32x2 raw_n[ILP];
-    float sc_n[ILP];
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      raw_n[c] = u32x2{0u, 0u};
-      sc_n[c] = 0.f;
-      if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
-      if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
-    }
-    constexpr bool kPrefetchA = (MT == 1);
-    u32x4 A_n[ILP][MT];
-    if constexpr (kPrefetchA) {
-#pragma unroll
-      for (int c = 0; c < ILP; ++c)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c]);
-    }
-    for (uint32_t fk = 0; fk < FK; ++fk) {
-      u32x4 A[ILP][MT];
-#pragma unroll
-      for (int c = 0; c < ILP; ++c)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if constexpr (kPrefetchA) {
-            A[c][mt] = A_n[c][mt];
-            if (fk + 1 < FK)
-              A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + (fk + 1) * FW);
-          } else {
-            A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
-          }
-        }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const uint32_t g = fk * FN + fn;
-        const uint32_t s0 = g * 8;
-        const uint32_t gn = min(g + 1, G - 1);
-        u32x2 raw[ILP];
-        float sc[ILP], nsc8[ILP];
-#pragma unroll
-        for (int c = 0; c < ILP; ++c) {
-          raw[c] = raw_n[c];
-          sc[c] = sc_n[c];
-          nsc8[c] = -8.f * sc[c];
-          if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
-          if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
-        }
-        uint32_t e[ILP][8];
-        // payload steps (at most the last 16) fall in the last two fragments
-        if (fn < FN - 2 || s0 + 7 < lim_min) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            uint32_t sy[ILP];
-            step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
-#pragma unroll
-            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            uint32_t sy[ILP];
-            step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
-#pragma unroll
-            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < ILP; ++c) {
-          const BOp b = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = mfma<FMT>(A[c][mt], b, acc[fn][mt]);
-        }
-      }
-    }
-    if (a.status) {
-#pragma unroll
-      for (int c = 0; c < ILP; ++c) {
-        const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
-        if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
-      }
-    }
+  if constexpr (MIX) {
+    if (nch == 2)
+      fused_chains<FMT, R, FN, MT, 2>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
+    else if (nch == 1)
+      fused_chains<FMT, R, FN, MT, 1>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
+  } else {
+    if (nch == 1)
+      fused_chains<FMT, R, FN, MT, 1>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
   }
   float out_scale = 1.f;
   if constexpr (FMT == FP8)
@@ -828,10 +876,10 @@ __global__ __launch_bounds__(dense_max_threads(FN, MT)) void k_dense(DenseArgs d
   const GemmArgs& a = d.g;
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t unit = uniform(blockIdx.x * a.waves + wave);
-  const bool active = unit < a.units;
-  const uint32_t strip = active ? unit / a.ups : 0u;
-  const uint32_t kt_first = active ? (unit % a.ups) * a.tpw : d.kt;
+  const uint32_t unit = uniform(blockIdx.x * a.cpw + wave);
+  const bool active = wave < a.cpw && unit < a.chains;
+  const uint32_t strip = active ? unit / a.cps : 0u;
+  const uint32_t kt_first = active ? (unit % a.cps) * a.tpw : d.kt;
   floatx4 acc[FN][MT];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn)
