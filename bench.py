@@ -86,6 +86,23 @@ def timed(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
+def launch_distribution(fn, n, stream):
+    """Per-launch durations (us) of n launches, each between its own events."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"median_us": round(float(np.median(us)), 3),
+            "p10_us": round(float(np.percentile(us, 10)), 3),
+            "p90_us": round(float(np.percentile(us, 90)), 3), "launches": n}
+
+
 def cpu_baseline(d, wl, blob):
     """The CPU oracle (decode of the compressed layer + fp64 GEMV), timed on the
     host on a bounded sample of the layer: every tile of the first strips."""
@@ -162,8 +179,10 @@ def main():
                                   y=y, ws=ws, stream=stream)
 
     ms = timed(fused, args.steps, args.warmup, stream)
+    dist = launch_distribution(fused, 50, stream)
     nk = wl.n * wl.k
-    decoded_bytes = nk * 2
+    # decoded-weight bytes at the format's storage width (int4 half a byte)
+    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0}[wl.fmt]
     value = decoded_bytes / (ms * 1e-3) / 1e9
     alg_bytes = len(blob) + m * wl.k * 2 + m * wl.n * 4
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -182,14 +201,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: W %dx%d bf16 N(0,0.02) byte split, tiles %dx%d, R=%d, M=%d"
-                               % (args.workload, wl.n, wl.k, wl.tile_n, wl.tile_k, wl.lanes, m),
+        "config": {"workload": "%s: W %dx%d %s, tiles %dx%d, R=%d, M=%d"
+                               % (args.workload, wl.n, wl.k, wl.note, wl.tile_n, wl.tile_k,
+                                  wl.lanes, m),
                    "m": m, "n": wl.n, "k": wl.k, "blob_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes": alg_bytes,
-                     "source_hash": source_hash()},
+                     "per_launch": dist, "source_hash": source_hash()},
     }
 
     secondary = {"bits_per_weight": round(info.bits_per_weight, 4),
@@ -211,10 +231,16 @@ def main():
         secondary["fused_m256_ms"] = round(ms2, 4)
         secondary["fused_m256_tflops"] = round(flops / (ms2 * 1e-3) / 1e12, 3)
         secondary["fused_m256_mfma_frac"] = round(flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
-        wraw = torch.from_numpy(np.asarray(d["codes"]).view(np.int16)).to(dev)
+        codes = np.asarray(d["codes"])
+        wraw = torch.from_numpy(codes.view(np.int16) if wl.fmt == 4 else
+                                codes.view(np.uint8)).to(dev)
         dcopies = max(2, math.ceil(ROTATE_BYTES / (nk * 2)))
         wd = [wraw.clone() for _ in range(dcopies)]
         del wraw
+        dec = torch.empty((wl.n, wl.k), dtype=torch.int16 if wl.fmt == 4 else torch.uint8,
+                          device=dev)
+        reps = max(5, args.steps // 10)
+        ablation = {}
         for mm in (1, 256):
             xm = xall[:mm].contiguous()
             wsd = dgt.alloc_workspace(dgt.dgt_dense_workspace(wl.fmt, wl.n, wl.k, wl.tile_n, mm), dev)
@@ -223,14 +249,36 @@ def main():
                                                      tile_n=wl.tile_n, scales=scales,
                                                      w_scale=d["w_scale"], y=yd, ws=wsd,
                                                      stream=stream),
-                        max(5, args.steps // 10), 3, stream)
+                        reps, 3, stream)
             secondary["dense_m%d_ms" % mm] = round(msd, 4)
             if mm == 1:
                 secondary["dense_m1_weight_gbs"] = round(nk * 2 / (msd * 1e-3) / 1e9, 3)
                 secondary["fused_speedup_vs_dense_m1"] = round(msd / ms, 3)
             else:
                 secondary["dense_m256_tflops"] = round(2.0 * mm * nk / (msd * 1e-3) / 1e12, 3)
-        del wd
+            # ablation: layer-level decode to HBM, then the dense GEMM on the
+            # decoded copy (two launches per step) against the fused kernel
+            ms_dec = timed(lambda i: dgt.dgt_decode_tiles(layers[i % copies], out=dec,
+                                                          stream=stream), reps, 3, stream)
+
+            def two_stage(i, xm=xm, yd=yd, wsd=wsd):
+                dgt.dgt_decode_tiles(layers[i % copies], out=dec, stream=stream)
+                dgt.dgt_dense_gemm(wl.fmt, dec, xm, tile_n=wl.tile_n, scales=scales,
+                                   w_scale=d["w_scale"], y=yd, ws=wsd, stream=stream)
+            ms_two = timed(two_stage, reps, 3, stream)
+            ms_fused = ms if mm == 1 else secondary["fused_m256_ms"]
+            ablation["m%d" % mm] = {"decode_to_hbm_ms": round(ms_dec, 4),
+                                    "two_stage_ms": round(ms_two, 4),
+                                    "fused_ms": round(ms_fused, 4),
+                                    "fused_speedup_vs_two_stage": round(ms_two / ms_fused, 3)}
+            # vendor GEMM on the uncompressed bf16 weight (reference point only)
+            if wl.fmt == 4:
+                wts = [w.view(torch.bfloat16).t().contiguous() for w in wd]
+                ms_lib = timed(lambda i: torch.matmul(xm, wts[i % len(wts)]), reps, 3, stream)
+                secondary["torch_matmul_bf16_m%d_ms" % mm] = round(ms_lib, 4)
+                del wts
+        secondary["ablation"] = ablation
+        del wd, dec
     result["secondary"] = secondary
 
     if args.copy_calib:
@@ -241,7 +289,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = a.numel()
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.fmt == 4:
         result["cpu_baseline"] = cpu_baseline(d, wl, blob)
     print(json.dumps(result))
 

@@ -63,8 +63,10 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
 // maps to the symbol s with c_s <= r < c_s + f_s.  Caller synchronises.
 // The frequency load is split off so it can be issued before other loads
 // (the vector-memory counter retires loads in order).
+// The load is unconditional (a clamped index; build_lut drops the threads at
+// or above the alphabet size), so no branch blurs the caller's wait counts.
 __device__ __forceinline__ uint32_t lut_load_freq(const uint16_t* table, uint32_t alphabet) {
-  return (threadIdx.x < alphabet) ? (uint32_t)table[threadIdx.x] : 0u;
+  return (uint32_t)table[min(threadIdx.x, alphabet - 1)];
 }
 
 __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32x2* lut,
@@ -72,7 +74,7 @@ __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32
   const uint32_t t = threadIdx.x;
   const uint32_t lane = t & 63, wave = t >> 6;
   // inclusive scan of f over <= 256 symbols: wave scans plus wave totals
-  uint32_t v = freq_of_thread;
+  uint32_t v = (t < alphabet) ? freq_of_thread : 0u;
   for (uint32_t d = 1; d < 64; d <<= 1) {
     uint32_t o = __shfl_up(v, d, 64);
     if (lane >= d) v += o;
@@ -217,13 +219,18 @@ __device__ __forceinline__ void stage_issue(const Layer& L, uint32_t t, uint32_t
   const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
   st.words4 = o1 - o0 - L.lanes;
   st.src = L.streams + o0 + L.lanes;
-  // bound checks against the remaining count keep the per-j offsets constant
-  // (nothing lane-dependent is hoisted out of a caller's loop)
-  const int32_t rem = (int32_t)st.words4 - (int32_t)sub_lane;
-  const uint32_t* p = st.src + sub_lane;
+  // Every lane loads, without branches, so the vector-memory wait counts of
+  // the caller stay exact (a later wait for an earlier load does not have to
+  // drain these).  Positions past the stream re-read the tile's last dword
+  // (the states come first, so the tile always has one); stage_commit keeps
+  // only the words below words4.
+  const uint32_t* p = L.streams + o0;
+  const int32_t last = (int32_t)(o1 - o0) - 1;
 #pragma unroll
-  for (int j = 0; j < kPre; ++j)
-    st.v[j] = (rem > (int32_t)(j * sub_size)) ? p[j * sub_size] : 0u;
+  for (int j = 0; j < kPre; ++j) {
+    const int32_t i = (int32_t)(L.lanes + sub_lane + j * sub_size);
+    st.v[j] = p[min(i, last)];
+  }
 }
 
 // Returns the number of staged u16 words (including a possible pad word).

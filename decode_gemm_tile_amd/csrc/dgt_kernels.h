@@ -418,21 +418,26 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   Staged stg[2];
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
-  // 3) write the streams to LDS
+  // 3) write the streams to LDS.  Both chain slots always load (a missing
+  // second chain repeats the first) so that every wave has the same loads in
+  // flight and the LUT build waits for the table alone.
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    if (c < (int)nch) {
-      const uint32_t ta = strip * L.kt + kt_first + c * TPC;
-      const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
-      tile_lane[c] = t_l;
-      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
-      ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
-      ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
-      const uint32_t kt_l = kt_first + c * TPC + ((R == 32 && upper) ? 1u : 0u);
-      k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
-    }
+    const uint32_t cc = (c < (int)nch) ? (uint32_t)c : 0u;
+    const uint32_t ta = strip * L.kt + kt_first + cc * TPC;
+    const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
+    tile_lane[c] = t_l;
+    stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
+    ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
+    const uint32_t kt_l = kt_first + cc * TPC + ((R == 32 && upper) ? 1u : 0u);
+    k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
   }
   build_lut(fq, L.alphabet, lut, cum);
+  // the payload counts are read after the LUT build: a wait for them then
+  // costs nothing (the staged streams are needed next anyway)
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    if (c < (int)nch) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
   __syncthreads();  // LUT complete; each wave's staged streams are private to it
 #pragma unroll
   for (int c = 0; c < 2; ++c) {

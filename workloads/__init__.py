@@ -62,7 +62,7 @@ WORKLOADS = {
     "fp8_8192": Workload("fp8_8192", FMT_FP8, 8192, 8192, 256, 64, 64, 303, (1, 16, 64),
                          w_sigma=0.02, note="e4m3 with per-tensor scale"),
     "bf16_mlp": Workload("bf16_mlp", FMT_BF16, 14336, 4096, 128, 64, 64, 404, (1, 8, 64, 256),
-                         w_sigma=0.02, note="Llama-3-8B MLP shape, bf16 byte split"),
+                         w_sigma=0.02, note="bf16 N(0,0.02) byte split, Llama-3-8B MLP shape"),
     "int4_ffn405": Workload("int4_ffn405", FMT_INT4, 53248, 16384, 128, 64, 64, 505,
                             (1, 8, 64, 256), w_sigma=1.0, w_mean=8.0,
                             note="405B-scale FFN, int4"),
