@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdgt.so")
 
 DGT_FMT_INT8, DGT_FMT_INT4, DGT_FMT_FP8_E4M3, DGT_FMT_BF16_SPLIT = 1, 2, 3, 4
+DGT_FMT_INT4_PAIR = 5
 STATUS = {0: "DGT_OK", -1: "DGT_E_ARG", -2: "DGT_E_SHAPE", -3: "DGT_E_ALPHABET",
           -4: "DGT_E_BUFSIZE", -5: "DGT_E_FORMAT", -6: "DGT_E_CORRUPT", -7: "DGT_E_HIP",
           -8: "DGT_E_UNSUPPORTED"}

@@ -122,7 +122,7 @@ bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
   L->alphabet = in->alphabet;
   L->tiles = in->tiles;
   L->kt = in->k / in->tile_k;
-  L->steps = in->tile_n * in->tile_k / in->lanes;
+  L->steps = in->tile_n * in->tile_k / dgt::weights_per_symbol(in->fmt) / in->lanes;
   const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
   L->region_words = (words + 7) & ~7u;
   return true;
@@ -160,7 +160,7 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
 bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   const uint32_t fn = in->tile_n / 16;
   if (in->lanes != 64 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
-  if (m <= (fn == 8 ? 64u : 16u)) return false;  // one register-resident pass covers M
+  if (m <= 16) return false;  // one register-resident pass (one 16-row block) covers M
   const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn), nt = xm_tiles(fn);
   if (m > nw * mtw * 16) return false;
   const uint32_t kt = in->k / in->tile_k;
@@ -238,6 +238,17 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
     p->mix = 1;
     p->n2 = c - w2;
     p->waves = w2;
+    // More than one round of workgroups per CU: half-size workgroups (all
+    // waves on two chains) so that two share a CU and one's prologue (table
+    // and stream loads, LUT build) overlaps the other's decode.
+    const uint64_t rounds = (p->chains + (uint64_t)c * kCUs - 1) / ((uint64_t)c * kCUs);
+    const uint32_t half = w2 / 2;
+    if (rounds > 1 && half >= 8 && p->cps % 2 == 0 &&
+        2 * (kLutBytes + kCumBytes + 2 * half * chain_lds) <= kMaxLds) {
+      p->waves = half;
+      p->n2 = half;
+      c = 2 * half;
+    }
   }
   p->cpw = c;
   p->threads = 64 * std::max(p->waves, 4u);       // the LUT build uses >= 4 waves
@@ -299,7 +310,9 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     return DGT_E_ARG;
   int rc = device_supported(info);
   if (rc) return rc;
-  if (info->fmt == DGT_FMT_INT4 && (!d_scales || info->k % 128)) return DGT_E_ARG;
+  if ((info->fmt == DGT_FMT_INT4 || info->fmt == DGT_FMT_INT4_PAIR) &&
+      (!d_scales || info->k % 128))
+    return DGT_E_ARG;
   const uint32_t fn = info->tile_n / 16;
   if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
   if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
@@ -351,6 +364,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     switch (info->fmt) {
       case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
@@ -385,6 +399,9 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
         break;
       case DGT_FMT_INT4:
         rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_INT4_PAIR:
+        rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
         rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
@@ -429,6 +446,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
 switch (info->fmt) {
     case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, grid, 64 * waves, lds, st);
     default: break;
@@ -473,7 +491,8 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
                    const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
                    float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_w || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
-  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_SPLIT) return DGT_E_ARG;
+  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_INT4_PAIR) return DGT_E_ARG;
+  if (fmt == DGT_FMT_INT4_PAIR) fmt = DGT_FMT_INT4;  // same decoded layout and values
   if ((tile_n != 128 && tile_n != 256) || n % tile_n || k % 64 || (k / 64) % 2)
     return DGT_E_SHAPE;
   if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;

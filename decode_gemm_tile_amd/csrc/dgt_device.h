@@ -39,7 +39,14 @@ constexpr uint32_t kLutBytes = kSlots * 8;
 constexpr uint32_t kCumBytes = 1040;   // (256 + 1) u32, padded
 constexpr uint32_t kSlackWords = 64;   // u16 words of slack after each staged stream
 
-enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4 };
+enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5 };
+
+// Decode steps per 16-row fragment: a lane's 8 weights of a fragment take 8
+// symbols, or 4 when a symbol codes two int4 weights.
+template <int FMT>
+__host__ __device__ constexpr int steps_per_frag() { return FMT == INT4P ? 4 : 8; }
+// At most this many final steps of a tile decode the initial-state payload.
+constexpr uint32_t kPayloadMax = 16;
 
 // Everything a kernel needs to know about a layer (passed by value).
 struct Layer {

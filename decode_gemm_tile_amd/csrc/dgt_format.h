@@ -28,18 +28,23 @@ struct HeaderLayout {
 };
 
 inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : 256u; }
+// weights coded per symbol (INT4_PAIR packs two along K)
+inline uint32_t weights_per_symbol(uint32_t fmt) { return fmt == 5 ? 2u : 1u; }
+// symbols per lane per 16-row fragment (8 weights either way)
+inline uint32_t symbols_per_lane(uint32_t fmt) { return 8u / weights_per_symbol(fmt); }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Tile-local position of symbol j = s*R + p (s = 8g + e; g = fk*Fn + fn).
-inline void symbol_position(uint32_t j, uint32_t tile_n, uint32_t lanes, uint32_t* row,
-                            uint32_t* col) {
+// Tile-local position of symbol j = s*R + p (s = epl*g + e; g = fk*Fn + fn),
+// epl symbols per lane per fragment; col counts symbols (weights, or pairs).
+inline void symbol_position(uint32_t j, uint32_t tile_n, uint32_t lanes, uint32_t epl,
+                            uint32_t* row, uint32_t* col) {
   const uint32_t s = j / lanes, p = j % lanes;
-  const uint32_t g = s >> 3, e = s & 7;
+  const uint32_t g = s / epl, e = s % epl;
   const uint32_t fn_count = tile_n / 16;
   const uint32_t fk = g / fn_count, fn = g % fn_count;
   *row = fn * 16 + (p & 15);
-  *col = fk * (lanes / 2) + (p >> 4) * 8 + e;
+  *col = fk * (lanes / 16) * epl + (p >> 4) * epl + e;
 }
 
 // Tile-local position of raw byte q = g*8R + p*8 + e (lane-major).

@@ -32,18 +32,21 @@ T get(const uint8_t* base, size_t off) {
   return v;
 }
 
-bool geometry_ok(uint32_t n, uint32_t k, uint32_t tn, uint32_t tk, uint32_t lanes) {
+bool geometry_ok(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tn, uint32_t tk,
+                 uint32_t lanes) {
   if (!n || !k || !tn || !tk || !lanes) return false;
   if (n % tn || k % tk) return false;
   if (lanes % 16 || tn % 16) return false;
-  if (tk % (lanes / 2)) return false;
-  if ((uint64_t)tn * tk % lanes) return false;
+  if (tk % (lanes / 2)) return false;  // whole fragments of R/2 weights
+  const uint32_t wps = dgt::weights_per_symbol(fmt);
+  if (tk % wps) return false;
+  if ((uint64_t)tn * (tk / wps) % lanes) return false;
   return true;
 }
 
 bool params_ok(const dgt_params* p) {
   if (!p) return false;
-  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_SPLIT) return false;
+  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_INT4_PAIR) return false;
   if (p->prob_bits < 8 || p->prob_bits > 15) return false;
   return true;
 }
@@ -174,7 +177,8 @@ const char* dgt_status_string(int status) {
 }
 
 size_t dgt_compress_bound(const dgt_params* p) {
-  if (!params_ok(p) || !geometry_ok(p->n, p->k, p->tile_n, p->tile_k, p->lanes)) return 0;
+  if (!params_ok(p) || !geometry_ok(p->fmt, p->n, p->k, p->tile_n, p->tile_k, p->lanes))
+    return 0;
   const uint64_t tiles = (uint64_t)(p->n / p->tile_n) * (p->k / p->tile_k);
   const uint64_t T = (uint64_t)p->tile_n * p->tile_k;
   const uint32_t alpha = dgt::alphabet_of(p->fmt);
@@ -189,14 +193,25 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
                        size_t* out_size) {
   if (!params_ok(p) || !w || !out || !out_size) return DGT_E_ARG;
   const uint32_t n = p->n, k = p->k, tn = p->tile_n, tk = p->tile_k, R = p->lanes;
-  if (!geometry_ok(n, k, tn, tk, R)) return DGT_E_SHAPE;
+  if (!geometry_ok(p->fmt, n, k, tn, tk, R)) return DGT_E_SHAPE;
   const uint32_t fmt = p->fmt, alpha = dgt::alphabet_of(fmt), pb = p->prob_bits;
   const uint64_t NK = (uint64_t)n * k;
+  // the symbol matrix is [n, ks] with tiles of tn x tks symbols
+  const uint32_t wps = dgt::weights_per_symbol(fmt), epl = dgt::symbols_per_lane(fmt);
+  const uint32_t ks = k / wps, tks = tk / wps;
+  const uint64_t NS = (uint64_t)n * ks;
 
-  // symbolise: coded byte per weight (+ raw low byte for the bf16 split)
-  std::vector<uint8_t> sym(NK);
+  // symbolise: coded byte per symbol (+ raw low byte for the bf16 split)
+  std::vector<uint8_t> sym(NS);
   std::vector<uint8_t> raw;
-  if (fmt == DGT_FMT_BF16_SPLIT) {
+  if (fmt == DGT_FMT_INT4_PAIR) {
+    const uint8_t* q = static_cast<const uint8_t*>(w);
+    for (uint64_t i = 0; i < NS; ++i) {
+      const uint8_t a = q[2 * i], b = q[2 * i + 1];
+      if (a > 15 || b > 15) return DGT_E_ALPHABET;
+      sym[i] = (uint8_t)(a | (b << 4));
+    }
+  } else if (fmt == DGT_FMT_BF16_SPLIT) {
     raw.resize(NK);
     const uint16_t* b = static_cast<const uint16_t*>(w);
     for (uint64_t i = 0; i < NK; ++i) {
@@ -212,7 +227,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
 
   // shared per-layer table
   std::vector<uint64_t> counts(alpha, 0);
-  for (uint64_t i = 0; i < NK; ++i) counts[sym[i]]++;
+  for (uint64_t i = 0; i < NS; ++i) counts[sym[i]]++;
   std::vector<uint32_t> f;
   if (!quantize(counts, pb, &f)) return DGT_E_ALPHABET;
   std::vector<uint32_t> c(alpha + 1, 0);
@@ -220,15 +235,19 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
 
   const uint32_t kt = k / tk;
   const uint64_t tiles = (uint64_t)(n / tn) * kt;
-  const uint32_t T = tn * tk, S = T / R;
+  const uint32_t T = tn * tk, TS = tn * tks, S = TS / R;
   if (tiles > 0xFFFFFFFFull) return DGT_E_SHAPE;
 
-  // tile-local positions, shared by every tile
-  std::vector<uint32_t> pos(T), rpos(T);
-  for (uint32_t j = 0; j < T; ++j) {
+  // tile-local positions, shared by every tile (pos in the symbol matrix,
+  // rpos in the weight matrix)
+  std::vector<uint32_t> pos(TS), rpos(raw.empty() ? 0 : T);
+  for (uint32_t j = 0; j < TS; ++j) {
     uint32_t r, col;
-    dgt::symbol_position(j, tn, R, &r, &col);
-    pos[j] = r * k + col;
+    dgt::symbol_position(j, tn, R, epl, &r, &col);
+    pos[j] = r * ks + col;
+  }
+  for (uint32_t j = 0; j < (uint32_t)rpos.size(); ++j) {
+    uint32_t r, col;
     dgt::raw_position(j, tn, R, &r, &col);
     rpos[j] = r * k + col;
   }
@@ -236,12 +255,12 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   std::vector<TileOut> enc(tiles);
   std::atomic<uint64_t> next{0};
   auto work = [&]() {
-    std::vector<uint8_t> ts(T);
+    std::vector<uint8_t> ts(TS);
     for (;;) {
       const uint64_t t = next.fetch_add(1);
       if (t >= tiles) break;
-      const uint64_t base = (uint64_t)(t / kt) * tn * k + (uint64_t)(t % kt) * tk;
-      for (uint32_t j = 0; j < T; ++j) ts[j] = sym[base + pos[j]];
+      const uint64_t base = (uint64_t)(t / kt) * tn * ks + (uint64_t)(t % kt) * tks;
+      for (uint32_t j = 0; j < TS; ++j) ts[j] = sym[base + pos[j]];
       encode_tile(ts.data(), R, S, f.data(), c.data(), pb, &enc[t]);
     }
   };
@@ -344,15 +363,16 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   in.total_bytes = get<uint64_t>(b, HeaderLayout::total);
   in.max_tile_words4 = get<uint32_t>(b, HeaderLayout::max_tile_words4);
   in.kmax = get<uint32_t>(b, HeaderLayout::kmax);
-  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_SPLIT) return DGT_E_FORMAT;
+  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_INT4_PAIR) return DGT_E_FORMAT;
   if (in.flags != 0) return DGT_E_FORMAT;
   if (in.total_bytes != size) return DGT_E_CORRUPT;
-  if (!geometry_ok(in.n, in.k, in.tile_n, in.tile_k, in.lanes)) return DGT_E_CORRUPT;
+  if (!geometry_ok(in.fmt, in.n, in.k, in.tile_n, in.tile_k, in.lanes)) return DGT_E_CORRUPT;
   if (in.prob_bits < 8 || in.prob_bits > 15) return DGT_E_CORRUPT;
   if (in.alphabet != dgt::alphabet_of(in.fmt)) return DGT_E_CORRUPT;
   const uint64_t tiles = (uint64_t)(in.n / in.tile_n) * (in.k / in.tile_k);
   if (tiles != in.tiles) return DGT_E_CORRUPT;
-  const uint64_t T = (uint64_t)in.tile_n * in.tile_k, S = T / in.lanes;
+  const uint64_t T = (uint64_t)in.tile_n * in.tile_k;
+  const uint64_t S = T / dgt::weights_per_symbol(in.fmt) / in.lanes;
   if (in.kmax > 255) return DGT_E_CORRUPT;
   // section bounds and alignment
   if (in.table_off < dgt::kHeaderBytes || in.table_off % 16 ||

@@ -78,6 +78,8 @@ struct OperandTraits<INT8> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<INT4> { static constexpr int xbytes = 2; };
 template <>
+struct OperandTraits<INT4P> { static constexpr int xbytes = 2; };
+template <>
 struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<FP8> { static constexpr int xbytes = 2; };  // e4m3 widened to bf16
@@ -92,7 +94,8 @@ __device__ __forceinline__ uint32_t pack_hi_bytes(uint32_t e1, uint32_t e0) {
 }
 
 template <int FMT>
-__device__ __forceinline__ BOp make_b(const uint32_t (&e)[8], u32x2 raw, float sc, float nsc8) {
+__device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()], u32x2 raw,
+                                      float sc, float nsc8) {
   BOp b;
   if constexpr (FMT == BF16) {
     const uint32_t p01 = pack_hi_bytes(e[1], e[0]);
@@ -118,6 +121,17 @@ __device__ __forceinline__ BOp make_b(const uint32_t (&e)[8], u32x2 raw, float s
       floatx2 w;
       w.x = __builtin_fmaf((float)(e[2 * i] >> 24), sc, nsc8);
       w.y = __builtin_fmaf((float)(e[2 * i + 1] >> 24), sc, nsc8);
+      const bf16x2 h = __builtin_convertvector(w, bf16x2);
+      o[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
+  } else if constexpr (FMT == INT4P) {  // symbol i: weights 2i (low nibble), 2i+1
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx2 w;
+      w.x = __builtin_fmaf((float)((e[i] >> 24) & 15u), sc, nsc8);
+      w.y = __builtin_fmaf((float)(e[i] >> 28), sc, nsc8);
       const bf16x2 h = __builtin_convertvector(w, bf16x2);
       o[i] = __builtin_bit_cast(uint32_t, h);
     }
@@ -274,6 +288,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
                                              floatx4 (&acc)[FN][MT]) {
   const Layer& L = a.L;
   constexpr uint32_t FW = R / 2;  // fragment width (columns)
+  constexpr int SPF = steps_per_frag<FMT>();
   Chain (&ch)[ILP] = *reinterpret_cast<Chain(*)[ILP]>(&chs[0]);
   const uint32_t lane = lane_id();
   const bool upper = lane >= 32;
@@ -312,7 +327,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
     raw_n[c] = u32x2{0u, 0u};
     sc_n[c] = 0.f;
     if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
-    if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
+    if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
   }
   constexpr bool kPrefetchA = (MT == 1);
   u32x4 A_n[ILP][MT];
@@ -340,7 +355,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const uint32_t g = fk * FN + fn;
-      const uint32_t s0 = g * 8;
+      const uint32_t s0 = g * SPF;
       const uint32_t gn = min(g + 1, G - 1);
       u32x2 raw[ILP];
       float sc[ILP], nsc8[ILP];
@@ -350,13 +365,13 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         sc[c] = sc_n[c];
         nsc8[c] = -8.f * sc[c];
         if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
-        if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
+        if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
       }
-      uint32_t e[ILP][8];
-      // payload steps (at most the last 16) fall in the last two fragments
-      if (fn < FN - 2 || s0 + 7 < lim_min) {
+      uint32_t e[ILP][SPF];
+      // payload steps (at most the last kPayloadMax) fall in the last fragments
+      if (fn < FN - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < SPF; ++i) {
           uint32_t sy[ILP];
           step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
@@ -364,7 +379,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < SPF; ++i) {
           uint32_t sy[ILP];
           step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
@@ -592,6 +607,7 @@ template <int FMT, int FN>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr uint32_t R = 64, FW = 32, TK = 64, FK = TK / FW, G = FK * FN;
+  constexpr int SPF = steps_per_frag<FMT>();
   extern __shared__ __align__(16) uint8_t smem[];
   const GemmArgs& a = x.g;
   const Layer& L = a.L;
@@ -658,7 +674,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       raw_n[c] = u32x2{0u, 0u};
       sc_n[c] = 0.f;
       if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
-      if constexpr (FMT == INT4) sc_n[c] = load_scale(c, 0);
+      if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
     }
     // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
     const uint8_t* xp[MTW];
@@ -681,7 +697,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const uint32_t g = fk * FN + fn;
-        const uint32_t s0 = g * 8;
+        const uint32_t s0 = g * SPF;
         const uint32_t gn = min(g + 1, G - 1);
         u32x2 raw[ILP];
         float sc[ILP], nsc8[ILP];
@@ -691,20 +707,23 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           sc[c] = sc_n[c];
           nsc8[c] = -8.f * sc[c];
           if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
-          if constexpr (FMT == INT4) sc_n[c] = load_scale(c, gn);
+          if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
         }
-        uint32_t e[ILP][8];
+        uint32_t e[ILP][SPF];
         auto steps = [&](auto careful) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < SPF; ++i) {
             uint32_t sy[ILP];
             step_all<64, decltype(careful)::value, ILP>(ch, lut, smem, s0 + i, false, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
           }
         };
-        // payload steps (at most the last 16) fall in the last two fragments
-        if (fn < FN - 2 || s0 + 7 < lim_min) steps(BoolC<false>{}); else steps(BoolC<true>{});
+        // payload steps (at most the last kPayloadMax) fall in the last fragments
+        if (fn < FN - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min)
+          steps(BoolC<false>{});
+        else
+          steps(BoolC<true>{});
         uint8_t* buf = xbuf + (g & 1) * (NT * 1024);
 #pragma unroll
         for (int c = 0; c < ILP; ++c) {
@@ -815,15 +834,16 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     lim_min = min(lim_min, uniform(ch[c].lim));
     if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
   }
+  constexpr int SPF = steps_per_frag<FMT>();
   const uint32_t FN = L.tile_n / 16;
-  const uint32_t G = L.steps / 8;
+  const uint32_t G = L.steps / SPF;
   const uint32_t p = lane % R;
   for (uint32_t g = 0; g < G; ++g) {
-    const uint32_t s0 = g * 8;
-    uint32_t e[ILP][8];
-    if (s0 + 7 < lim_min) {
+    const uint32_t s0 = g * SPF;
+    uint32_t e[ILP][SPF];
+    if (s0 + SPF - 1 < lim_min) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < SPF; ++i) {
         uint32_t sy[ILP];
         step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
@@ -831,7 +851,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < SPF; ++i) {
         uint32_t sy[ILP];
         step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
@@ -849,6 +869,18 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
         const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);
         const BOp b = make_b<BF16>(e[c], raw, 0.f, 0.f);
         *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
+      } else if constexpr (FMT == INT4P) {
+        // symbol i -> code bytes 2i (low nibble) and 2i+1 (high nibble)
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t sy = e[c][i] >> 24;
+          h[i] = (sy & 0x0Fu) | ((sy & 0xF0u) << 4);
+        }
+        u32x2 v;
+        v.x = h[0] | (h[1] << 16);
+        v.y = h[2] | (h[3] << 16);
+        *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
       } else {
         u32x2 v;
         v.x = pack_hi_bytes(e[c][1], e[c][0]) | (pack_hi_bytes(e[c][3], e[c][2]) << 16);

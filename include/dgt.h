@@ -42,6 +42,10 @@
  * bk*tile_k..  Inside a tile, symbol j = s*R + p (step s, lane p) with
  * s = 8g + e, fragment g = fk*(tile_n/16) + fn: lane p decodes row
  * 16fn + p%16, column fk*R/2 + 8*(p/16) + e.  rANS: state in [2^16, 2^32),
+ * INT4_PAIR codes symbol c of a row for the weight pair (2c, 2c+1) and lays
+ * out a tile's tile_n*tile_k/2 symbols the same way with 4 symbols per lane
+ * per fragment (s = 4g + e, pair column fk*R/4 + 4*(p/16) + e), so a lane's
+ * 4 symbols are again its 8 consecutive weights of one row.
  * 16-bit renormalisation words; decode x' = f*(x>>n) + (x mod 2^n) - c_s,
  * then if x' < 2^16 read one word.  The last k[t] steps of a tile decode from
  * y = x - 2^16 without reading words; a valid tile ends with y == 0 on every
@@ -62,7 +66,9 @@ enum dgt_format {
   DGT_FMT_INT8 = 1,       /* int8 codes; GEMM value = the integer (exact bf16) */
   DGT_FMT_INT4 = 2,       /* codes 0..15, zero point 8, bf16 scale per 128 columns */
   DGT_FMT_FP8_E4M3 = 3,   /* OCP e4m3 bytes, per-tensor fp32 weight scale */
-  DGT_FMT_BF16_SPLIT = 4  /* bf16: high byte coded, low byte stored raw */
+  DGT_FMT_BF16_SPLIT = 4, /* bf16: high byte coded, low byte stored raw */
+  DGT_FMT_INT4_PAIR = 5   /* INT4 weights and scales, coded two per symbol:
+                             q[n,2c] | q[n,2c+1] << 4 (alphabet 256) */
 };
 
 enum dgt_status {
@@ -103,8 +109,9 @@ size_t dgt_compress_bound(const dgt_params* p);
 
 /* Offline encoder ([P §3.1] offline stage), host only.
  *   w: N*K weights row-major: one byte per weight for INT8 (two's
- *      complement), INT4 (values 0..15) and FP8_E4M3; one uint16 bf16 bit
- *      pattern per weight for BF16_SPLIT.
+ *      complement), INT4 and INT4_PAIR (values 0..15; INT4_PAIR needs even
+ *      K and tile_k) and FP8_E4M3; one uint16 bf16 bit pattern per weight
+ *      for BF16_SPLIT.
  *   out/cap: caller buffer of `cap` bytes; *out_size receives the blob size.
  * Errors: E_ARG, E_SHAPE, E_ALPHABET (INT4 code > 15), E_BUFSIZE.
  * Deterministic: the same input always gives the same bytes. */
@@ -121,9 +128,9 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out);
  * as what the fused path avoids).
  *   d_blob: device copy of the blob described by `info`.
  *   d_tile_ids: n_ids tile ids to decode, or NULL for all tiles (n_ids ignored).
- *   d_out: the full W layout, row-major [N, K]: uint8 symbols (INT8 bytes,
- *          INT4 codes, FP8 bytes) or uint16 bf16 bits (BF16_SPLIT); only the
- *          elements of the decoded tiles are written.
+ *   d_out: the full W layout, row-major [N, K]: uint8 (INT8 bytes, INT4
+ *          and INT4_PAIR codes, FP8 bytes) or uint16 bf16 bits (BF16_SPLIT);
+ *          only the elements of the decoded tiles are written.
  *   d_status: NULL or int32[tiles]; entry t is set to 0 when tile t decoded
  *          with a consistent stream, else to a positive error mask
  *          (1 = final state, 2 = stream length, 4 = stream overrun).
@@ -140,13 +147,13 @@ size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m);
 /* Fused decode + GEMM ([P §3.1] run-time stage): Y[m, n] = sum_k X[m, k] W[n, k]
  * with W decoded tile by tile on chip, never written to global memory.
  *   d_x: bf16 bits [m, K] row-major; m in 1..256.
- *   d_scales: INT4 only, bf16 bits [N, K/128]; else NULL.
+ *   d_scales: INT4 and INT4_PAIR, bf16 bits [N, K/128]; else NULL.
  *   w_scale: FP8 only, per-tensor weight scale (X is quantised to e4m3 per
  *            tensor on the device first); ignored otherwise.
  *   d_y: fp32 [m, N] row-major, overwritten.
  *   d_ws, ws_bytes: workspace of at least dgt_gemm_workspace(info, m) bytes.
  *   d_status: NULL or int32[tiles], as for dgt_decode_tiles.
- * Values: INT8 -> bf16(code); INT4 -> bf16_RNE((q-8)*scale); BF16 -> bits;
+ * Values: INT8 -> bf16(code); INT4, INT4_PAIR -> bf16_RNE((q-8)*scale); BF16 -> bits;
  * FP8 -> e4m3 products scaled by sx*w_scale; fp32 accumulation.
  * Errors: E_ARG, E_BUFSIZE (workspace), E_UNSUPPORTED, E_HIP. */
 int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
@@ -155,7 +162,8 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
 
 /* Uncompressed baseline with the same tiling and epilogue, reading W from
  * global memory: d_w is [N, K] in the same element layout dgt_decode_tiles
- * writes.  Workspace from dgt_dense_workspace (zero-filled before first use). */
+ * writes (INT4_PAIR is read as INT4).  Workspace from dgt_dense_workspace
+ * (zero-filled before first use). */
 size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n,
                            uint32_t m);
 int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const void* d_w,

@@ -8,7 +8,7 @@ pages give none); all integers are little-endian.
 
 header (128 bytes)
    0 magic  b"DGT1"              4 u16 version = 1     6 u16 header bytes = 128
-   8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split)
+   8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split, 5 int4 pairs)
   12 u32 flags = 0              16 u32 N     20 u32 K
   24 u32 tile_n  28 u32 tile_k  32 u32 lanes R  36 u32 prob_bits n
   40 u32 alphabet (16 for int4, else 256)       44 u32 tiles
@@ -26,7 +26,10 @@ raw     (bf16 split only, 16-byte aligned) T low bytes per tile, tiles in id
 total = end of raw (bf16 split) or end of streams.
 
 Symbols: int8 code & 0xFF; int4 code; e4m3 byte; bf16 bits >> 8 (sign and
-top seven exponent bits) with the low byte (exponent LSB + mantissa) raw.
+top seven exponent bits) with the low byte (exponent LSB + mantissa) raw;
+int4 pairs: q[n, 2c] | q[n, 2c+1] << 4 (two weights adjacent along K per
+symbol, alphabet 256; tile_n and tile_k stay in weights, a tile holds
+tile_n*tile_k/2 symbols laid out by ``oracle.order`` with epl = 4).
 """
 
 import struct
@@ -38,7 +41,7 @@ from . import entropy, freq, order, rans
 MAGIC = b"DGT1"
 VERSION = 1
 HEADER_BYTES = 128
-FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16 = 1, 2, 3, 4
+FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR = 1, 2, 3, 4, 5
 _HDR = struct.Struct("<4sHHIIIIIIIIII QQQQQQ II 24x")
 assert _HDR.size == HEADER_BYTES
 
@@ -50,9 +53,23 @@ def _align(v: int, a: int) -> int:
 def alphabet_of(fmt: int) -> int:
     if fmt == FMT_INT4:
         return 16
-    if fmt in (FMT_INT8, FMT_FP8, FMT_BF16):
+    if fmt in (FMT_INT8, FMT_FP8, FMT_BF16, FMT_INT4_PAIR):
         return 256
     raise ValueError("unknown format")
+
+
+def weights_per_symbol(fmt: int) -> int:
+    return 2 if fmt == FMT_INT4_PAIR else 1
+
+
+def symbol_geometry(fmt: int, n: int, k: int, tile_n: int, tile_k: int):
+    """(symbol-matrix columns, tile columns in symbols, symbols per lane per
+    fragment) of a format: pairs halve K and the fragment's symbol count."""
+    if fmt == FMT_INT4_PAIR:
+        if k % 2 or tile_k % 2:
+            raise ValueError("int4 pairs need even K and tile_k")
+        return k // 2, tile_k // 2, 4
+    return k, tile_k, 8
 
 
 def symbolise(fmt: int, w):
@@ -69,6 +86,13 @@ def symbolise(fmt: int, w):
     if fmt == FMT_BF16:
         b = w.astype(np.uint16)
         return (b >> 8).astype(np.uint8), (b & 0xFF).astype(np.uint8)
+    if fmt == FMT_INT4_PAIR:
+        if w.min() < 0 or w.max() > 15:
+            raise ValueError("int4 codes must be in [0, 15]")
+        if w.shape[1] % 2:
+            raise ValueError("int4 pairs need an even K")
+        q = w.astype(np.uint8)
+        return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8), None
     raise ValueError("unknown format")
 
 
@@ -77,11 +101,13 @@ def compress_layer(fmt: int, w, tile_n: int, tile_k: int, lanes: int,
     w = np.asarray(w)
     n, k = w.shape
     order.check_geometry(n, k, tile_n, tile_k, lanes)
+    ks_, tks, epl = symbol_geometry(fmt, n, k, tile_n, tile_k)
+    order.check_geometry(n, ks_, tile_n, tks, lanes, epl)
     sym, raw = symbolise(fmt, w)
     alpha = alphabet_of(fmt)
     counts = entropy.histogram(sym, alpha)
     f = freq.quantize_freqs(counts, prob_bits)
-    tsym = order.gather_tiles(sym, tile_n, tile_k, lanes)
+    tsym = order.gather_tiles(sym, tile_n, tks, lanes, epl=epl)
     states, words, ks = rans.encode_tiles(tsym, f, lanes, prob_bits, rans.KMAX)
     tiles = tsym.shape[0]
     T = tile_n * tile_k
@@ -138,6 +164,9 @@ def parse(blob) -> dict:
     order.check_geometry(h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"])
     if h["alphabet"] != alphabet_of(h["fmt"]):
         raise ValueError("bad alphabet")
+    ksym, tks, epl = symbol_geometry(h["fmt"], h["n"], h["k"], h["tile_n"], h["tile_k"])
+    order.check_geometry(h["n"], ksym, h["tile_n"], tks, h["lanes"], epl)
+    h["steps"] = h["tile_n"] * tks // h["lanes"]
     nt = (h["n"] // h["tile_n"]) * (h["k"] // h["tile_k"])
     if h["tiles"] != nt:
         raise ValueError("bad tile count")
@@ -154,7 +183,7 @@ def parse(blob) -> dict:
     if int(np.diff(h["index"]).max()) != h["max_tile_words4"]:
         raise ValueError("bad max tile length")
     h["ks"] = np.frombuffer(b, np.uint8, t, h["ktab_off"]).astype(np.int64)
-    S = h["tile_n"] * h["tile_k"] // h["lanes"]
+    S = h["steps"]
     if h["kmax"] > 255 or (h["ks"] > min(h["kmax"], S)).any():
         raise ValueError("bad payload step count")
     return h
@@ -175,7 +204,7 @@ def decode_symbols(blob, tiles=None) -> np.ndarray:
     h = parse(blob)
     ids = range(h["tiles"]) if tiles is None else list(tiles)
     R = h["lanes"]
-    S = h["tile_n"] * h["tile_k"] // R
+    S = h["steps"]
     st, ws = [], []
     for t in ids:
         s, w = tile_stream(blob, h, t)
@@ -193,12 +222,18 @@ def decode_symbols(blob, tiles=None) -> np.ndarray:
 
 
 def decompress_layer(blob) -> np.ndarray:
-    """Rebuild the original codes: int8 -> int8, int4/fp8 -> uint8, bf16 -> uint16."""
+    """Rebuild the original codes: int8 -> int8, int4/fp8/int4 pairs -> uint8, bf16 -> uint16."""
     h = parse(blob)
     syms = decode_symbols(blob)
     n, k, tn, tk, R = h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"]
-    sym = order.scatter_tiles(syms.astype(np.uint8), n, k, tn, tk, R)
     fmt = h["fmt"]
+    if fmt == FMT_INT4_PAIR:
+        pairs = order.scatter_tiles(syms.astype(np.uint8), n, k // 2, tn, tk // 2, R, epl=4)
+        out = np.empty((n, k), np.uint8)
+        out[:, 0::2] = pairs & 15
+        out[:, 1::2] = pairs >> 4
+        return out
+    sym = order.scatter_tiles(syms.astype(np.uint8), n, k, tn, tk, R)
     if fmt == FMT_INT8:
         return sym.view(np.int8)
     if fmt in (FMT_INT4, FMT_FP8):

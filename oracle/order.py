@@ -22,36 +22,42 @@ lane holds 8 consecutive-column values of one row.
 
 Raw (uncoded) bytes of a tile, where a format stores them, are kept in the
 lane-major order q = g*8*R + p*8 + e, i.e. a lane's 8 values are contiguous.
+
+Formats whose symbol packs two weights (int4 pairs) apply the same map to
+the matrix of symbols with epl = 4 symbols per lane per fragment: a fragment
+is then 16 rows x (R/16)*4 symbols, i.e. the same 16 x R/2 weights, and a
+lane's 4 symbols are its 8 consecutive-column weights.
 """
 
 import numpy as np
 
 
-def check_geometry(n: int, k: int, tile_n: int, tile_k: int, lanes: int) -> None:
+def check_geometry(n: int, k: int, tile_n: int, tile_k: int, lanes: int,
+                   epl: int = 8) -> None:
     if min(n, k, tile_n, tile_k, lanes) <= 0:
         raise ValueError("sizes must be positive")
     if n % tile_n or k % tile_k:
         raise ValueError("N and K must be multiples of the tile shape")
     if lanes % 16 or tile_n % 16:
         raise ValueError("lanes and tile_n must be multiples of 16")
-    if tile_k % (lanes // 2):
-        raise ValueError("tile_k must be a multiple of lanes/2")
+    if tile_k % ((lanes // 16) * epl):
+        raise ValueError("tile_k must be a multiple of the fragment width")
 
 
-def tile_positions(tile_n: int, tile_k: int, lanes: int):
+def tile_positions(tile_n: int, tile_k: int, lanes: int, epl: int = 8):
     """(rows[j], cols[j]) inside the tile for symbol index j = s*R + p."""
     R = lanes
-    fw = R // 2
+    fw = (R // 16) * epl
     fn_count = tile_n // 16
     fk_count = tile_k // fw
     T = tile_n * tile_k
     j = np.arange(T, dtype=np.int64)
     s, p = j // R, j % R
-    g, e = s // 8, s % 8
+    g, e = s // epl, s % epl
     fk, fn = g // fn_count, g % fn_count
     a, cg = p % 16, p // 16
     rows = fn * 16 + a
-    cols = fk * fw + cg * 8 + e
+    cols = fk * fw + cg * epl + e
     assert fk.max() < fk_count
     return rows, cols
 
@@ -76,12 +82,18 @@ def tile_origin(t: int, k: int, tile_n: int, tile_k: int):
     return (t // kt) * tile_n, (t % kt) * tile_k
 
 
-def gather_tiles(w, tile_n: int, tile_k: int, lanes: int, raw: bool = False):
+def _positions(tile_n, tile_k, lanes, raw, epl):
+    if raw:
+        return raw_positions(tile_n, tile_k, lanes)
+    return tile_positions(tile_n, tile_k, lanes, epl)
+
+
+def gather_tiles(w, tile_n: int, tile_k: int, lanes: int, raw: bool = False, epl: int = 8):
     """[tiles, T] array: tile t's elements in symbol order (or raw order)."""
     w = np.asarray(w)
     n, k = w.shape
-    check_geometry(n, k, tile_n, tile_k, lanes)
-    rows, cols = (raw_positions if raw else tile_positions)(tile_n, tile_k, lanes)
+    check_geometry(n, k, tile_n, tile_k, lanes, 8 if raw else epl)
+    rows, cols = _positions(tile_n, tile_k, lanes, raw, epl)
     nt, kt = n // tile_n, k // tile_k
     # view W as [nt, Tn, kt, Tk] -> [nt, kt, Tn, Tk]
     blocks = w.reshape(nt, tile_n, kt, tile_k).transpose(0, 2, 1, 3)
@@ -90,11 +102,11 @@ def gather_tiles(w, tile_n: int, tile_k: int, lanes: int, raw: bool = False):
 
 
 def scatter_tiles(tiles, n: int, k: int, tile_n: int, tile_k: int, lanes: int,
-                  raw: bool = False):
+                  raw: bool = False, epl: int = 8):
     """Inverse of gather_tiles: rebuild [N, K] from per-tile ordered values."""
     tiles = np.asarray(tiles)
-    check_geometry(n, k, tile_n, tile_k, lanes)
-    rows, cols = (raw_positions if raw else tile_positions)(tile_n, tile_k, lanes)
+    check_geometry(n, k, tile_n, tile_k, lanes, 8 if raw else epl)
+    rows, cols = _positions(tile_n, tile_k, lanes, raw, epl)
     nt, kt = n // tile_n, k // tile_k
     blocks = np.zeros((nt * kt, tile_n, tile_k), dtype=tiles.dtype)
     blocks[:, rows, cols] = tiles

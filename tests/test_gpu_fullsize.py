@@ -24,7 +24,8 @@ from tests.gpu_util import codes_as_u8_or_u16, to_dev, x_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
-NAMES = ["int8_1024", "int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405"]
+NAMES = ["int8_1024", "int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405",
+         "int4_4096_pair", "int4_ffn405_pair"]
 _CACHE = {}
 
 
@@ -65,10 +66,11 @@ def test_fullsize_encoder_matches_oracle_on_sampled_tiles(name):
     rng = np.random.default_rng(7)
     tiles = sorted(set([0, h["tiles"] - 1] + list(rng.integers(0, h["tiles"], 14))))
     kt = wl.k // wl.tile_k
+    _, tks, epl = oblob.symbol_geometry(wl.fmt, wl.n, wl.k, wl.tile_n, wl.tile_k)
     for t in tiles:
-        r0, c0 = (t // kt) * wl.tile_n, (t % kt) * wl.tile_k
-        block = sym[r0:r0 + wl.tile_n, c0:c0 + wl.tile_k]
-        ts = oorder.gather_tiles(block, wl.tile_n, wl.tile_k, wl.lanes)
+        r0, c0 = (t // kt) * wl.tile_n, (t % kt) * tks
+        block = sym[r0:r0 + wl.tile_n, c0:c0 + tks]
+        ts = oorder.gather_tiles(block, wl.tile_n, tks, wl.lanes, epl=epl)
         st, ws, ks = orans.encode_tiles(ts, f, wl.lanes, wl.prob_bits)
         gst, gws = oblob.tile_stream(blob, h, t)
         assert np.array_equal(gst, st[0]), t

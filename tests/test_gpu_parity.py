@@ -19,8 +19,8 @@ from tests.gpu_util import (codes_as_u8_or_u16, decoded_to_numpy, reference, rel
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
-F8, F4, FE, FB = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
-                  dgt.DGT_FMT_BF16_SPLIT)
+F8, F4, FE, FB, FP = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
+                      dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_INT4_PAIR)
 
 # (fmt, N, K, tile_n, tile_k, lanes, seed)
 CASES = [
@@ -33,6 +33,9 @@ CASES = [
     (FB, 384, 640, 128, 64, 64, 7),
     (FB, 512, 192, 256, 64, 64, 8),
     (FB, 256, 4096, 128, 64, 64, 9),      # 64 k-tiles: several workgroups per strip
+    (FP, 256, 1024, 128, 64, 64, 10),     # int4 pairs: 4 symbols per lane per fragment
+    (FP, 128, 768, 128, 64, 32, 11),      # int4 pairs, two tiles per wave
+    (FP, 512, 2048, 256, 64, 64, 12),     # int4 pairs, tile_n 256
 ]
 
 
@@ -81,7 +84,7 @@ def test_decode_tile_subset(fmt, n, k, tn, tk, R, seed):
 @pytest.mark.parametrize("m", [1, 5, 16, 33, 64, 100])
 def test_fused_gemm_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     import torch
-    if fmt == F4 and k % 128:
+    if fmt in (F4, FP) and k % 128:
         pytest.skip("int4 needs K % 128 == 0 for its scale groups")
     d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
     layer = dgt.DeviceLayer(blob)
@@ -107,6 +110,8 @@ XM_CASES = [
     (FE, 512, 1024, 256, 64, 64, 45),     # tile_n 256: two batches per strip
     (FB, 512, 512, 256, 64, 64, 46),
     (F4, 256, 1024, 256, 64, 64, 47),
+    (FP, 384, 2048, 128, 64, 64, 49),     # int4 pairs
+    (FP, 512, 1024, 256, 64, 64, 50),
 ]
 
 
@@ -173,7 +178,8 @@ def test_exact_integer_case():
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256)])
+@pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256),
+                                    (FP, 128)])
 @pytest.mark.parametrize("m", [1, 16, 64])
 def test_dense_baseline_matches_oracle(fmt, tn, m):
     import torch

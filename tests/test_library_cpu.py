@@ -40,6 +40,9 @@ CASES = [
     (dgt.DGT_FMT_BF16_SPLIT, 256, 128, 128, 64, 64, 6),
     (dgt.DGT_FMT_BF16_SPLIT, 32, 16, 16, 8, 16, 7),
     (dgt.DGT_FMT_BF16_SPLIT, 256, 64, 256, 32, 64, 8),
+    (dgt.DGT_FMT_INT4_PAIR, 256, 256, 128, 64, 64, 9),
+    (dgt.DGT_FMT_INT4_PAIR, 128, 256, 128, 64, 32, 10),
+    (dgt.DGT_FMT_INT4_PAIR, 512, 128, 256, 64, 64, 11),
 ]
 
 
@@ -61,7 +64,7 @@ def test_cpp_encoder_matches_oracle_bytes(fmt, n, k, tn, tk, R, seed):
 
 
 def test_cpp_encoder_matches_oracle_on_small_workloads():
-    for name in ("int8_1024", "int4_4096"):
+    for name in ("int8_1024", "int4_4096", "int4_4096_pair"):
         d = workloads.make(name)
         wl = d["workload"]
         ours = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)

@@ -69,3 +69,24 @@ def test_geometry_errors():
                  (128, 48, 128, 48, 64)]:
         with pytest.raises(ValueError):
             order.check_geometry(*args)
+
+
+@pytest.mark.parametrize("tn,tk,R", [(32, 16, 16), (128, 32, 64), (128, 16, 32), (256, 32, 64)])
+def test_pair_positions_cover_each_lanes_eight_weights(tn, tk, R):
+    """Pair layout (epl = 4 on the [rows, tk] pair matrix, i.e. tiles of 2*tk
+    weights): lane p's 4 symbols of fragment g are exactly the weights that
+    lane p decodes at fragment g in the one-weight layout, two per symbol in
+    column order (symbol e covers weight columns 2e and 2e + 1)."""
+    rows, cols = order.tile_positions(tn, tk, R, epl=4)
+    rows1, cols1 = order.tile_positions(tn, 2 * tk, R)
+    S = tn * tk // R
+    for s in range(S):
+        g, e = divmod(s, 4)
+        for p in range(R):
+            j = s * R + p
+            j_lo = (8 * g + 2 * e) * R + p
+            j_hi = (8 * g + 2 * e + 1) * R + p
+            assert (rows[j], 2 * cols[j]) == (rows1[j_lo], cols1[j_lo])
+            assert (rows[j], 2 * cols[j] + 1) == (rows1[j_hi], cols1[j_hi])
+    # and it is a bijection on the pair tile
+    assert len(set(zip(rows.tolist(), cols.tolist()))) == tn * tk

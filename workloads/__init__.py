@@ -19,6 +19,8 @@ Recipe (numpy.random.default_rng(seed); W first, then scales, then X):
                 X bf16 [256, 4096] N(0, 1).  Tiles 128x64, 64 lanes.
   int4_ffn405   W 53248x16384 int4 rint(N(8, 1.0)) clipped, scales as int4_4096;
                 X bf16 [256, 16384].  Tiles 128x64, 64 lanes.
+  int4_4096_pair, int4_ffn405_pair: the two int4 layers above (same seeds,
+                same draws) in the pair-symbol format.
   bf16_ffn405   W 53248x16384 bf16 N(0, 0.01); X bf16 [256, 16384].
                 Tiles 256x64, 64 lanes.
 rint is numpy's (ties to even); clipping follows rounding.  Casts to bf16 and
@@ -29,7 +31,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16 = 1, 2, 3, 4
+FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR = 1, 2, 3, 4, 5
 _CHUNK = 1 << 24
 
 
@@ -68,6 +70,13 @@ WORKLOADS = {
                             note="405B-scale FFN, int4"),
     "bf16_ffn405": Workload("bf16_ffn405", FMT_BF16, 53248, 16384, 256, 64, 64, 506,
                             (1, 8, 64, 256), w_sigma=0.01, note="405B-scale FFN, bf16"),
+    # the same int4 layers (same seeds, codes and scales) coded two weights per symbol
+    "int4_4096_pair": Workload("int4_4096_pair", FMT_INT4_PAIR, 4096, 4096, 128, 64, 64, 202,
+                               (1, 16), w_sigma=1.2, w_mean=8.0,
+                               note="int4_4096 coded as int4 pairs"),
+    "int4_ffn405_pair": Workload("int4_ffn405_pair", FMT_INT4_PAIR, 53248, 16384, 128, 64, 64,
+                                 505, (1, 8, 64, 256), w_sigma=1.0, w_mean=8.0,
+                                 note="int4_ffn405 coded as int4 pairs"),
 }
 
 
@@ -120,7 +129,7 @@ def make_weights(wl: Workload, rng=None):
     out = {"w_scale": 1.0, "scales": None}
     if wl.fmt == FMT_INT8:
         out["codes"] = _int_codes(rng, n, k, 0.0, wl.w_sigma, -127, 127).astype(np.int8)
-    elif wl.fmt == FMT_INT4:
+    elif wl.fmt in (FMT_INT4, FMT_INT4_PAIR):
         out["codes"] = _int_codes(rng, n, k, wl.w_mean, wl.w_sigma, 0, 15).astype(np.uint8)
         out["scales"] = _scales(rng, n, k // 128)
     elif wl.fmt == FMT_FP8:
@@ -163,7 +172,7 @@ def random_small(fmt: int, n: int, k: int, seed: int, sigma: float = None,
     if fmt == FMT_INT8:
         d["codes"] = _int_codes(rng, n, k, 0.0, 8.0 if sigma is None else sigma,
                                 -127, 127).astype(np.int8)
-    elif fmt == FMT_INT4:
+    elif fmt in (FMT_INT4, FMT_INT4_PAIR):
         d["codes"] = _int_codes(rng, n, k, 8.0 if mean is None else mean,
                                 1.2 if sigma is None else sigma, 0, 15).astype(np.uint8)
         d["scales"] = _scales(rng, n, k // 128) if k % 128 == 0 else None
