@@ -365,6 +365,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
       case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, p.wgs, p.lds, st);
       case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
@@ -402,6 +403,9 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
         break;
       case DGT_FMT_INT4_PAIR:
         rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_BF16_EXP:
+        rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
         rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
@@ -447,6 +451,7 @@ switch (info->fmt) {
     case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_EXP: return launch_decode<BF16E>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, grid, 64 * waves, lds, st);
     case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, grid, 64 * waves, lds, st);
     default: break;
@@ -491,8 +496,10 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
                    const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
                    float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_w || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
-  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_INT4_PAIR) return DGT_E_ARG;
-  if (fmt == DGT_FMT_INT4_PAIR) fmt = DGT_FMT_INT4;  // same decoded layout and values
+  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_EXP) return DGT_E_ARG;
+  // same decoded layout and values as the one-symbol-per-weight formats
+  if (fmt == DGT_FMT_INT4_PAIR) fmt = DGT_FMT_INT4;
+  if (fmt == DGT_FMT_BF16_EXP) fmt = DGT_FMT_BF16_SPLIT;
   if ((tile_n != 128 && tile_n != 256) || n % tile_n || k % 64 || (k / 64) % 2)
     return DGT_E_SHAPE;
   if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;

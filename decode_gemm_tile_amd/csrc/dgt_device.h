@@ -39,7 +39,11 @@ constexpr uint32_t kLutBytes = kSlots * 8;
 constexpr uint32_t kCumBytes = 1040;   // (256 + 1) u32, padded
 constexpr uint32_t kSlackWords = 64;   // u16 words of slack after each staged stream
 
-enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5 };
+enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5, BF16E = 6 };
+
+// formats whose tiles carry one raw byte per weight next to the coded symbol
+template <int FMT>
+__host__ __device__ constexpr bool has_raw_bytes() { return FMT == BF16 || FMT == BF16E; }
 
 // Decode steps per 16-row fragment: a lane's 8 weights of a fragment take 8
 // symbols, or 4 when a symbol codes two int4 weights.

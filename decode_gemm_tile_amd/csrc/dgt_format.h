@@ -32,6 +32,8 @@ inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : 256u; }
 inline uint32_t weights_per_symbol(uint32_t fmt) { return fmt == 5 ? 2u : 1u; }
 // symbols per lane per 16-row fragment (8 weights either way)
 inline uint32_t symbols_per_lane(uint32_t fmt) { return 8u / weights_per_symbol(fmt); }
+// formats that store one raw byte per weight beside the coded symbol
+inline bool has_raw(uint32_t fmt) { return fmt == 4 || fmt == 6; }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

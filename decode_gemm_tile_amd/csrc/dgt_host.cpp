@@ -46,7 +46,7 @@ bool geometry_ok(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tn, uint32_t tk,
 
 bool params_ok(const dgt_params* p) {
   if (!p) return false;
-  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_INT4_PAIR) return false;
+  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_EXP) return false;
   if (p->prob_bits < 8 || p->prob_bits > 15) return false;
   return true;
 }
@@ -185,7 +185,7 @@ size_t dgt_compress_bound(const dgt_params* p) {
   uint64_t b = dgt::kHeaderBytes + dgt::align_up(2 * alpha, 16) +
                dgt::align_up(4 * (tiles + 1), 16) + dgt::align_up(tiles, 16);
   b += tiles * (4ull * p->lanes + 2 * T + 4) + 16;
-  if (p->fmt == DGT_FMT_BF16_SPLIT) b += tiles * T + 16;
+  if (dgt::has_raw(p->fmt)) b += tiles * T + 16;
   return (size_t)b;
 }
 
@@ -217,6 +217,13 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
     for (uint64_t i = 0; i < NK; ++i) {
       sym[i] = (uint8_t)(b[i] >> 8);
       raw[i] = (uint8_t)(b[i] & 0xFF);
+    }
+  } else if (fmt == DGT_FMT_BF16_EXP) {
+    raw.resize(NK);
+    const uint16_t* b = static_cast<const uint16_t*>(w);
+    for (uint64_t i = 0; i < NK; ++i) {
+      sym[i] = (uint8_t)((b[i] >> 7) & 0xFF);
+      raw[i] = (uint8_t)(((b[i] >> 8) & 0x80) | (b[i] & 0x7F));
     }
   } else {
     std::memcpy(sym.data(), w, NK);
@@ -285,7 +292,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   const size_t streams_off = dgt::align_up(ktab_off + tiles, 16);
   const size_t streams_end = streams_off + 4 * (size_t)off[tiles];
   size_t raw_off = 0, total = streams_end;
-  if (fmt == DGT_FMT_BF16_SPLIT) {
+  if (dgt::has_raw(fmt)) {
     raw_off = dgt::align_up(streams_end, 16);
     total = raw_off + tiles * (size_t)T;
   }
@@ -363,7 +370,7 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   in.total_bytes = get<uint64_t>(b, HeaderLayout::total);
   in.max_tile_words4 = get<uint32_t>(b, HeaderLayout::max_tile_words4);
   in.kmax = get<uint32_t>(b, HeaderLayout::kmax);
-  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_INT4_PAIR) return DGT_E_FORMAT;
+  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_EXP) return DGT_E_FORMAT;
   if (in.flags != 0) return DGT_E_FORMAT;
   if (in.total_bytes != size) return DGT_E_CORRUPT;
   if (!geometry_ok(in.fmt, in.n, in.k, in.tile_n, in.tile_k, in.lanes)) return DGT_E_CORRUPT;
@@ -398,7 +405,7 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   const uint64_t kcap = std::min<uint64_t>(in.kmax, S);
   for (uint64_t t = 0; t < tiles; ++t)
     if (b[in.ktab_off + t] > kcap) return DGT_E_CORRUPT;
-  if (in.fmt == DGT_FMT_BF16_SPLIT) {
+  if (dgt::has_raw(in.fmt)) {
     if (in.raw_off < streams_end || in.raw_off % 16 || in.raw_off + tiles * T != size)
       return DGT_E_CORRUPT;
   } else if (in.raw_off != 0 || streams_end != size) {

@@ -80,6 +80,8 @@ struct OperandTraits<INT4> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<INT4P> { static constexpr int xbytes = 2; };
 template <>
+struct OperandTraits<BF16E> { static constexpr int xbytes = 2; };
+template <>
 struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<FP8> { static constexpr int xbytes = 2; };  // e4m3 widened to bf16
@@ -106,6 +108,19 @@ __device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()]
     b.v.y = __builtin_amdgcn_perm(p23, raw.x, 0x05030402u);
     b.v.z = __builtin_amdgcn_perm(p45, raw.y, 0x05010400u);
     b.v.w = __builtin_amdgcn_perm(p67, raw.y, 0x05030402u);
+  } else if constexpr (FMT == BF16E) {
+    // weights 2i, 2i+1: exponents from the symbols (top byte of the LUT
+    // words) into bits 14..7 and 30..23; sign and mantissa from the raw
+    // bytes, each copied into both bytes of its half by the byte permute
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ex = (e[2 * i] >> 17) | ((e[2 * i + 1] >> 1) & 0x7F800000u);
+      const uint32_t r = i < 2 ? raw.x : raw.y;
+      const uint32_t q = __builtin_amdgcn_perm(0u, r, (i & 1) ? 0x03030202u : 0x01010000u);
+      o[i] = (q & 0x807F807Fu) | (ex & ~0x807F807Fu);
+    }
+    b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
   } else if constexpr (FMT == INT8) {
     uint32_t f[8];
 #pragma unroll
@@ -326,7 +341,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
   for (int c = 0; c < ILP; ++c) {
     raw_n[c] = u32x2{0u, 0u};
     sc_n[c] = 0.f;
-    if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
+    if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, 0);
     if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
   }
   constexpr bool kPrefetchA = (MT == 1);
@@ -364,7 +379,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         raw[c] = raw_n[c];
         sc[c] = sc_n[c];
         nsc8[c] = -8.f * sc[c];
-        if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
+        if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
         if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
       }
       uint32_t e[ILP][SPF];
@@ -673,7 +688,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     for (int c = 0; c < ILP; ++c) {
       raw_n[c] = u32x2{0u, 0u};
       sc_n[c] = 0.f;
-      if constexpr (FMT == BF16) raw_n[c] = load_raw(c, 0);
+      if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, 0);
       if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
     }
     // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
@@ -706,7 +721,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           raw[c] = raw_n[c];
           sc[c] = sc_n[c];
           nsc8[c] = -8.f * sc[c];
-          if constexpr (FMT == BF16) raw_n[c] = load_raw(c, gn);
+          if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
           if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
         }
         uint32_t e[ILP][SPF];
@@ -864,10 +879,10 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       const uint32_t t = tile_lane[c];
       const uint32_t row = (t / L.kt) * L.tile_n + fn * 16 + (p & 15);
       const uint32_t col = (t % L.kt) * L.tile_k + fk * (R / 2) + 8 * (p >> 4);
-      if constexpr (FMT == BF16) {
+      if constexpr (has_raw_bytes<FMT>()) {
         const uint8_t* rp = L.raw + (size_t)t * L.tile_n * L.tile_k + (size_t)g * 8 * R + p * 8;
         const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);
-        const BOp b = make_b<BF16>(e[c], raw, 0.f, 0.f);
+        const BOp b = make_b<FMT>(e[c], raw, 0.f, 0.f);
         *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
       } else if constexpr (FMT == INT4P) {
         // symbol i -> code bytes 2i (low nibble) and 2i+1 (high nibble)

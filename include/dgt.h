@@ -37,7 +37,7 @@
  *   index  u32 off[tiles+1]: tile t's stream starts at streams + 4*off[t].
  *   ktab   u8 k[tiles]: initial-state payload steps of each tile.
  *   streams per tile: R u32 lane states, u16 words in decode order, zero pad.
- *   raw    (BF16_SPLIT) T low bytes per tile, lane-major.
+ *   raw    (BF16_SPLIT, BF16_EXP) T raw bytes per tile, lane-major.
  * Tile t = bn*(K/tile_k) + bk covers W rows bn*tile_n.. and columns
  * bk*tile_k..  Inside a tile, symbol j = s*R + p (step s, lane p) with
  * s = 8g + e, fragment g = fk*(tile_n/16) + fn: lane p decodes row
@@ -67,8 +67,10 @@ enum dgt_format {
   DGT_FMT_INT4 = 2,       /* codes 0..15, zero point 8, bf16 scale per 128 columns */
   DGT_FMT_FP8_E4M3 = 3,   /* OCP e4m3 bytes, per-tensor fp32 weight scale */
   DGT_FMT_BF16_SPLIT = 4, /* bf16: high byte coded, low byte stored raw */
-  DGT_FMT_INT4_PAIR = 5   /* INT4 weights and scales, coded two per symbol:
+  DGT_FMT_INT4_PAIR = 5,  /* INT4 weights and scales, coded two per symbol:
                              q[n,2c] | q[n,2c+1] << 4 (alphabet 256) */
+  DGT_FMT_BF16_EXP = 6    /* bf16: exponent (bits 14..7) coded, sign and mantissa
+                             stored raw as one byte (sign << 7 | mantissa) */
 };
 
 enum dgt_status {
@@ -111,7 +113,7 @@ size_t dgt_compress_bound(const dgt_params* p);
  *   w: N*K weights row-major: one byte per weight for INT8 (two's
  *      complement), INT4 and INT4_PAIR (values 0..15; INT4_PAIR needs even
  *      K and tile_k) and FP8_E4M3; one uint16 bf16 bit pattern per weight
- *      for BF16_SPLIT.
+ *      for BF16_SPLIT and BF16_EXP.
  *   out/cap: caller buffer of `cap` bytes; *out_size receives the blob size.
  * Errors: E_ARG, E_SHAPE, E_ALPHABET (INT4 code > 15), E_BUFSIZE.
  * Deterministic: the same input always gives the same bytes. */
@@ -129,7 +131,8 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out);
  *   d_blob: device copy of the blob described by `info`.
  *   d_tile_ids: n_ids tile ids to decode, or NULL for all tiles (n_ids ignored).
  *   d_out: the full W layout, row-major [N, K]: uint8 (INT8 bytes, INT4
- *          and INT4_PAIR codes, FP8 bytes) or uint16 bf16 bits (BF16_SPLIT);
+ *          and INT4_PAIR codes, FP8 bytes) or uint16 bf16 bits (BF16_SPLIT,
+ *          BF16_EXP);
  *          only the elements of the decoded tiles are written.
  *   d_status: NULL or int32[tiles]; entry t is set to 0 when tile t decoded
  *          with a consistent stream, else to a positive error mask
@@ -153,7 +156,8 @@ size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m);
  *   d_y: fp32 [m, N] row-major, overwritten.
  *   d_ws, ws_bytes: workspace of at least dgt_gemm_workspace(info, m) bytes.
  *   d_status: NULL or int32[tiles], as for dgt_decode_tiles.
- * Values: INT8 -> bf16(code); INT4, INT4_PAIR -> bf16_RNE((q-8)*scale); BF16 -> bits;
+ * Values: INT8 -> bf16(code); INT4, INT4_PAIR -> bf16_RNE((q-8)*scale); BF16_SPLIT,
+ * BF16_EXP -> the bf16 bits;
  * FP8 -> e4m3 products scaled by sx*w_scale; fp32 accumulation.
  * Errors: E_ARG, E_BUFSIZE (workspace), E_UNSUPPORTED, E_HIP. */
 int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
@@ -162,7 +166,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
 
 /* Uncompressed baseline with the same tiling and epilogue, reading W from
  * global memory: d_w is [N, K] in the same element layout dgt_decode_tiles
- * writes (INT4_PAIR is read as INT4).  Workspace from dgt_dense_workspace
+ * writes (INT4_PAIR is read as INT4, BF16_EXP as BF16_SPLIT).  Workspace from dgt_dense_workspace
  * (zero-filled before first use). */
 size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n,
                            uint32_t m);

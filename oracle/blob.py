@@ -8,7 +8,8 @@ pages give none); all integers are little-endian.
 
 header (128 bytes)
    0 magic  b"DGT1"              4 u16 version = 1     6 u16 header bytes = 128
-   8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split, 5 int4 pairs)
+   8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split, 5 int4 pairs,
+              6 bf16 exponent split)
   12 u32 flags = 0              16 u32 N     20 u32 K
   24 u32 tile_n  28 u32 tile_k  32 u32 lanes R  36 u32 prob_bits n
   40 u32 alphabet (16 for int4, else 256)       44 u32 tiles
@@ -21,13 +22,15 @@ index   u32 off[tiles + 1], 4-byte units from streams_off, off[0] = 0 (aligned)
 ktab    u8 k[tiles]: payload steps of each tile (see ``oracle.rans``) (aligned)
 streams tile t at streams_off + 4*off[t]: R u32 states (lane order) then the
         u16 words in decoder order, then one zero u16 if the count is odd
-raw     (bf16 split only, 16-byte aligned) T low bytes per tile, tiles in id
+raw     (bf16 splits only, 16-byte aligned) T raw bytes per tile, tiles in id
         order, each tile in the lane-major raw order of ``oracle.order``
 total = end of raw (bf16 split) or end of streams.
 
 Symbols: int8 code & 0xFF; int4 code; e4m3 byte; bf16 bits >> 8 (sign and
 top seven exponent bits) with the low byte (exponent LSB + mantissa) raw;
-int4 pairs: q[n, 2c] | q[n, 2c+1] << 4 (two weights adjacent along K per
+bf16 exponent split: the 8 exponent bits (bits >> 7) & 0xFF coded, the sign
+and the 7 mantissa bits raw as one byte (sign << 7 | mantissa), the split
+DFloat11 uses ([P2]); int4 pairs: q[n, 2c] | q[n, 2c+1] << 4 (two weights adjacent along K per
 symbol, alphabet 256; tile_n and tile_k stay in weights, a tile holds
 tile_n*tile_k/2 symbols laid out by ``oracle.order`` with epl = 4).
 """
@@ -41,7 +44,7 @@ from . import entropy, freq, order, rans
 MAGIC = b"DGT1"
 VERSION = 1
 HEADER_BYTES = 128
-FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR = 1, 2, 3, 4, 5
+FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
 _HDR = struct.Struct("<4sHHIIIIIIIIII QQQQQQ II 24x")
 assert _HDR.size == HEADER_BYTES
 
@@ -53,7 +56,7 @@ def _align(v: int, a: int) -> int:
 def alphabet_of(fmt: int) -> int:
     if fmt == FMT_INT4:
         return 16
-    if fmt in (FMT_INT8, FMT_FP8, FMT_BF16, FMT_INT4_PAIR):
+    if fmt in (FMT_INT8, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP):
         return 256
     raise ValueError("unknown format")
 
@@ -86,6 +89,11 @@ def symbolise(fmt: int, w):
     if fmt == FMT_BF16:
         b = w.astype(np.uint16)
         return (b >> 8).astype(np.uint8), (b & 0xFF).astype(np.uint8)
+    if fmt == FMT_BF16_EXP:
+        b = w.astype(np.uint16)
+        sym = ((b >> 7) & 0xFF).astype(np.uint8)
+        raw = (((b >> 8) & 0x80) | (b & 0x7F)).astype(np.uint8)
+        return sym, raw
     if fmt == FMT_INT4_PAIR:
         if w.min() < 0 or w.max() > 15:
             raise ValueError("int4 codes must be in [0, 15]")
@@ -240,8 +248,10 @@ def decompress_layer(blob) -> np.ndarray:
         return sym
     T = tn * tk
     raw = np.frombuffer(blob, np.uint8, h["tiles"] * T, h["raw_off"]).reshape(h["tiles"], T)
-    lo = order.scatter_tiles(raw, n, k, tn, tk, R, raw=True)
-    return (sym.astype(np.uint16) << 8) | lo.astype(np.uint16)
+    lo = order.scatter_tiles(raw, n, k, tn, tk, R, raw=True).astype(np.uint16)
+    if fmt == FMT_BF16_EXP:
+        return ((lo & 0x80) << 8) | (sym.astype(np.uint16) << 7) | (lo & 0x7F)
+    return (sym.astype(np.uint16) << 8) | lo
 
 
 def bits_per_weight(blob, n: int, k: int) -> float:

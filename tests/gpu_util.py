@@ -27,14 +27,14 @@ def codes_as_u8_or_u16(fmt, codes):
     c = np.asarray(codes)
     if fmt == dgt.DGT_FMT_INT8:
         return c.astype(np.int8).view(np.uint8)
-    if fmt == dgt.DGT_FMT_BF16_SPLIT:
+    if fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
         return c.astype(np.uint16)
     return c.astype(np.uint8)
 
 
 def decoded_to_numpy(fmt, out):
     a = out.cpu().numpy()
-    if fmt == dgt.DGT_FMT_BF16_SPLIT:
+    if fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
         return a.view(np.uint16)
     return a
 

@@ -25,7 +25,7 @@ from tests.gpu_util import codes_as_u8_or_u16, to_dev, x_dev
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 NAMES = ["int8_1024", "int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405",
-         "int4_4096_pair", "int4_ffn405_pair"]
+         "int4_4096_pair", "int4_ffn405_pair", "bf16_mlp_exp"]
 _CACHE = {}
 
 
@@ -48,7 +48,7 @@ def test_fullsize_decode_bit_exact(name):
     status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
     out = dgt.dgt_decode_tiles(layer, status=status)
     ref = to_dev(codes_as_u8_or_u16(wl.fmt, d["codes"]))
-    if wl.fmt == dgt.DGT_FMT_BF16_SPLIT:
+    if wl.fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
         ref = ref.view(torch.int16)
     torch.cuda.synchronize()
     assert torch.equal(out.view(ref.dtype), ref)

@@ -19,8 +19,8 @@ from tests.gpu_util import (codes_as_u8_or_u16, decoded_to_numpy, reference, rel
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
-F8, F4, FE, FB, FP = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
-                      dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_INT4_PAIR)
+F8, F4, FE, FB, FP, FX = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
+                          dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_INT4_PAIR, dgt.DGT_FMT_BF16_EXP)
 
 # (fmt, N, K, tile_n, tile_k, lanes, seed)
 CASES = [
@@ -36,6 +36,8 @@ CASES = [
     (FP, 256, 1024, 128, 64, 64, 10),     # int4 pairs: 4 symbols per lane per fragment
     (FP, 128, 768, 128, 64, 32, 11),      # int4 pairs, two tiles per wave
     (FP, 512, 2048, 256, 64, 64, 12),     # int4 pairs, tile_n 256
+    (FX, 384, 1024, 128, 64, 64, 13),     # bf16 exponent split
+    (FX, 256, 256, 128, 32, 32, 14),      # bf16 exponent split, two tiles per wave
 ]
 
 
@@ -112,6 +114,7 @@ XM_CASES = [
     (F4, 256, 1024, 256, 64, 64, 47),
     (FP, 384, 2048, 128, 64, 64, 49),     # int4 pairs
     (FP, 512, 1024, 256, 64, 64, 50),
+    (FX, 256, 2048, 128, 64, 64, 51),     # bf16 exponent split
 ]
 
 
@@ -179,7 +182,7 @@ def test_exact_integer_case():
 
 
 @pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256),
-                                    (FP, 128)])
+                                    (FP, 128), (FX, 128)])
 @pytest.mark.parametrize("m", [1, 16, 64])
 def test_dense_baseline_matches_oracle(fmt, tn, m):
     import torch

@@ -43,6 +43,8 @@ CASES = [
     (dgt.DGT_FMT_INT4_PAIR, 256, 256, 128, 64, 64, 9),
     (dgt.DGT_FMT_INT4_PAIR, 128, 256, 128, 64, 32, 10),
     (dgt.DGT_FMT_INT4_PAIR, 512, 128, 256, 64, 64, 11),
+    (dgt.DGT_FMT_BF16_EXP, 256, 128, 128, 64, 64, 12),
+    (dgt.DGT_FMT_BF16_EXP, 256, 64, 256, 32, 64, 13),
 ]
 
 

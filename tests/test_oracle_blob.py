@@ -19,6 +19,8 @@ CASES = [
     (blob.FMT_INT4_PAIR, 256, 256, 128, 64, 64),
     (blob.FMT_INT4_PAIR, 128, 256, 128, 64, 32),
     (blob.FMT_INT4_PAIR, 32, 32, 16, 16, 16),
+    (blob.FMT_BF16_EXP, 256, 128, 128, 64, 64),
+    (blob.FMT_BF16_EXP, 32, 16, 16, 8, 16),
 ]
 
 
@@ -137,3 +139,25 @@ def test_pair_coding_keeps_the_per_weight_entropy_of_independent_codes():
     assert h2 / 2 <= bpw <= h2 / 2 + 0.15
     assert bpw <= bpw1 + 0.002
     assert np.array_equal(blob.decompress_layer(b), codes)
+
+
+def test_exponent_split_fields_and_its_size_against_the_byte_split():
+    """bf16 exponent split: symbol = the 8 exponent bits, raw byte = sign and
+    mantissa; the decoded bits are the input.  On Gaussian bf16 weights the
+    exponent carries less entropy than sign + top exponent bits, so the blob is
+    smaller than the byte split's by about the low exponent bit's shortfall
+    from one bit of entropy."""
+    w = np.array([[0x3F80, 0xBF80, 0x0001, 0x8000, 0x7F7F, 0xC2F7]], np.uint16)
+    sym, raw = blob.symbolise(blob.FMT_BF16_EXP, w)
+    assert sym.tolist() == [[0x7F, 0x7F, 0x00, 0x00, 0xFE, 0x85]]
+    assert raw.tolist() == [[0x00, 0x80, 0x01, 0x80, 0x7F, 0xF7]]
+    d = workloads.random_small(blob.FMT_BF16_EXP, 256, 512, seed=12)
+    b6 = blob.compress_layer(blob.FMT_BF16_EXP, d["codes"], 128, 64, 64)
+    b4 = blob.compress_layer(blob.FMT_BF16, d["codes"], 128, 64, 64)
+    assert np.array_equal(blob.decompress_layer(b6), d["codes"])
+    hi, _ = blob.symbolise(blob.FMT_BF16, d["codes"])
+    ex, _ = blob.symbolise(blob.FMT_BF16_EXP, d["codes"])
+    gain = entropy.empirical_entropy(hi, 256) - entropy.empirical_entropy(ex, 256)
+    assert 0.05 < gain < 0.25
+    saved = blob.bits_per_weight(b4, 256, 512) - blob.bits_per_weight(b6, 256, 512)
+    assert abs(saved - gain) < 0.03

@@ -21,6 +21,7 @@ Recipe (numpy.random.default_rng(seed); W first, then scales, then X):
                 X bf16 [256, 16384].  Tiles 128x64, 64 lanes.
   int4_4096_pair, int4_ffn405_pair: the two int4 layers above (same seeds,
                 same draws) in the pair-symbol format.
+  bf16_mlp_exp  the bf16_mlp layer (same seed, same draws) in the exponent split.
   bf16_ffn405   W 53248x16384 bf16 N(0, 0.01); X bf16 [256, 16384].
                 Tiles 256x64, 64 lanes.
 rint is numpy's (ties to even); clipping follows rounding.  Casts to bf16 and
@@ -31,7 +32,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR = 1, 2, 3, 4, 5
+FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
 _CHUNK = 1 << 24
 
 
@@ -77,6 +78,10 @@ WORKLOADS = {
     "int4_ffn405_pair": Workload("int4_ffn405_pair", FMT_INT4_PAIR, 53248, 16384, 128, 64, 64,
                                  505, (1, 8, 64, 256), w_sigma=1.0, w_mean=8.0,
                                  note="int4_ffn405 coded as int4 pairs"),
+    # the bf16 MLP layer (same draws) with its exponent coded, sign + mantissa raw
+    "bf16_mlp_exp": Workload("bf16_mlp_exp", FMT_BF16_EXP, 14336, 4096, 128, 64, 64, 404,
+                             (1, 8, 64, 256), w_sigma=0.02,
+                             note="bf16 N(0,0.02) exponent split, Llama-3-8B MLP shape"),
 }
 
 
@@ -141,7 +146,7 @@ def make_weights(wl: Workload, rng=None):
         q = (wt / sw).to(torch.float8_e4m3fn)
         out["codes"] = q.view(torch.uint8).numpy().copy()
         out["w_scale"] = float(sw)
-    elif wl.fmt == FMT_BF16:
+    elif wl.fmt in (FMT_BF16, FMT_BF16_EXP):
         out["codes"] = _normal_bf16_bits(rng, n * k, 0.0, wl.w_sigma).reshape(n, k)
     else:
         raise ValueError("unknown format")
@@ -183,7 +188,7 @@ def random_small(fmt: int, n: int, k: int, seed: int, sigma: float = None,
         sw = (wt.abs().max() / 448.0).to(torch.float32)
         d["codes"] = (wt / sw).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(n, k).copy()
         d["w_scale"] = float(sw)
-    elif fmt == FMT_BF16:
+    elif fmt in (FMT_BF16, FMT_BF16_EXP):
         d["codes"] = _to_bf16_bits(_normal(rng, n * k, 0.0,
                                            0.02 if sigma is None else sigma)).reshape(n, k)
     d["x"] = _to_bf16_bits(rng.normal(0.0, 1.0, m * k)).reshape(m, k)
