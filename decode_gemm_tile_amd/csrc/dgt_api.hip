@@ -293,47 +293,45 @@ int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
-  if (!info || m == 0) return 0;
-  FusedPlan p;
-  if (!plan_fused(info, m, &p)) return 0;
-  return p.ws_bytes;
+// Rows per launch of the fused kernels; larger M runs in passes of this many
+// rows (each pass decodes the layer again).
+constexpr uint32_t kPassRows = 256;
+constexpr uint32_t kMaxRows = 1u << 16;
+
+// Plans of the full passes and of the remainder pass, and the workspace both
+// need: the partial region of the larger one and, for fp8, the quantised X of
+// all rows (one per-tensor scale for the whole call).
+struct CallPlan {
+  FusedPlan full, rest;
+  uint32_t n_full, rest_rows;
+  size_t quant_off, ws_bytes;
+};
+
+bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c) {
+  c->n_full = m / kPassRows;
+  c->rest_rows = m % kPassRows;
+  size_t q = 0;
+  if (c->n_full) {
+    if (!plan_fused(in, kPassRows, &c->full)) return false;
+    q = std::max(q, c->full.quant_off);
+  }
+  if (c->rest_rows) {
+    if (!plan_fused(in, c->rest_rows, &c->rest)) return false;
+    q = std::max(q, c->rest.quant_off);
+  }
+  c->quant_off = q;
+  c->ws_bytes = q;
+  if (in->fmt == DGT_FMT_FP8_E4M3) c->ws_bytes += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
+  return true;
 }
 
-int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
-                          uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
-                          void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
-  if (!d_blob || !info || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
-  if (((uintptr_t)d_blob & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
-    return DGT_E_ARG;
-  int rc = device_supported(info);
-  if (rc) return rc;
-  if ((info->fmt == DGT_FMT_INT4 || info->fmt == DGT_FMT_INT4_PAIR) &&
-      (!d_scales || info->k % 128))
-    return DGT_E_ARG;
+// One pass of at most kPassRows rows with plan p.
+int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L, const uint8_t* xsrc,
+                uint32_t xrow, uint32_t m, const uint16_t* d_scales, float* sxp, float w_scale,
+                float* d_y, uint8_t* ws, int32_t* d_status, hipStream_t st) {
   const uint32_t fn = info->tile_n / 16;
-  if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
-  if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
-  FusedPlan p;
-  if (!plan_fused(info, m, &p)) return DGT_E_UNSUPPORTED;
-  if (ws_bytes < p.ws_bytes) return DGT_E_BUFSIZE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Layer L;
-  layer_from_info(d_blob, info, &L);
-  uint8_t* ws = static_cast<uint8_t*>(d_ws);
-  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
-  uint32_t xrow = info->k * 2;
-  float* sxp = nullptr;
-  if (info->fmt == DGT_FMT_FP8_E4M3) {
-    uint16_t* xq = nullptr;
-    float* sx = nullptr;
-    rc = launch_quant(d_x, m * info->k, ws + p.quant_off, st, &xq, &sx);
-    if (rc) return rc;
-    xsrc = reinterpret_cast<const uint8_t*>(xq);
-    sxp = sx;
-  }
   if (p.xm) {
     XmArgs x;
     GemmArgs& a = x.g;
@@ -394,28 +392,87 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     a.slots = p.slots;
     a.red_cols = p.red_cols;
     const uint32_t grid = p.wgs, threads = p.threads;
+    const bool mix = p.mix != 0;
+    int rc;
     switch (info->fmt) {
       case DGT_FMT_INT8:
-        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       case DGT_FMT_INT4:
-        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       case DGT_FMT_INT4_PAIR:
-        rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       case DGT_FMT_BF16_EXP:
-        rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
-        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       case DGT_FMT_BF16_SPLIT:
-        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, p.mix != 0, grid, threads, p.lds, st);
+        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
         break;
       default:
         rc = DGT_E_ARG;
     }
+    if (rc) return rc;
+  }
+  return DGT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
+  if (!info || m == 0 || m > kMaxRows) return 0;
+  CallPlan c;
+  if (!plan_call(info, m, &c)) return 0;
+  return c.ws_bytes;
+}
+
+int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
+                          uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
+                          void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
+  if (!d_blob || !info || !d_x || !d_y || !d_ws || m == 0 || m > kMaxRows) return DGT_E_ARG;
+  if (((uintptr_t)d_blob & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
+    return DGT_E_ARG;
+  int rc = device_supported(info);
+  if (rc) return rc;
+  if ((info->fmt == DGT_FMT_INT4 || info->fmt == DGT_FMT_INT4_PAIR) &&
+      (!d_scales || info->k % 128))
+    return DGT_E_ARG;
+  const uint32_t fn = info->tile_n / 16;
+  if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
+  if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
+  CallPlan c;
+  if (!plan_call(info, m, &c)) return DGT_E_UNSUPPORTED;
+  if (ws_bytes < c.ws_bytes) return DGT_E_BUFSIZE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Layer L;
+  layer_from_info(d_blob, info, &L);
+  uint8_t* ws = static_cast<uint8_t*>(d_ws);
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
+  const uint32_t xrow = info->k * 2;
+  float* sxp = nullptr;
+  if (info->fmt == DGT_FMT_FP8_E4M3) {
+    uint16_t* xq = nullptr;
+    float* sx = nullptr;
+    rc = launch_quant(d_x, m * info->k, ws + c.quant_off, st, &xq, &sx);
+    if (rc) return rc;
+    xsrc = reinterpret_cast<const uint8_t*>(xq);
+    sxp = sx;
+  }
+  // passes run in order on the stream and share the workspace (its counters
+  // are back at zero after each)
+  for (uint32_t pass = 0; pass <= c.n_full; ++pass) {
+    const bool full = pass < c.n_full;
+    const uint32_t rows = full ? kPassRows : c.rest_rows;
+    if (rows == 0) break;
+    const size_t r0 = (size_t)pass * kPassRows;
+    rc = launch_pass(full ? c.full : c.rest, info, L, xsrc + r0 * xrow, xrow, rows, d_scales,
+                     sxp, w_scale, d_y + r0 * info->n, ws, d_status, st);
     if (rc) return rc;
   }
   return DGT_OK;

@@ -149,7 +149,9 @@ size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m);
 
 /* Fused decode + GEMM ([P §3.1] run-time stage): Y[m, n] = sum_k X[m, k] W[n, k]
  * with W decoded tile by tile on chip, never written to global memory.
- *   d_x: bf16 bits [m, K] row-major; m in 1..256.
+ *   d_x: bf16 bits [m, K] row-major; m in 1..65536.  Up to 256 rows run in
+ *        one pass in which every tile is decoded once; more rows run in
+ *        passes of 256 (the layer is decoded once per pass).
  *   d_scales: INT4 and INT4_PAIR, bf16 bits [N, K/128]; else NULL.
  *   w_scale: FP8 only, per-tensor weight scale (X is quantised to e4m3 per
  *            tensor on the device first); ignored otherwise.

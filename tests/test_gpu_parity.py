@@ -137,6 +137,22 @@ def test_fused_gemm_large_m_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     assert int(ws[:4 * strips].sum().item()) == 0   # strip counters returned to zero
 
 
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", [
+    (FB, 384, 4096, 128, 64, 64, 52),
+    (FE, 512, 1024, 256, 64, 64, 53),     # one fp8 activation scale across passes
+    (FP, 256, 2048, 128, 64, 64, 54),
+])
+@pytest.mark.parametrize("m", [257, 300, 513])
+def test_fused_gemm_beyond_one_pass(fmt, n, k, tn, tk, R, seed, m):
+    import torch
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
+
+
 def test_fused_gemm_large_m_repeatable():
     import torch
     d, blob = _layer(FB, 384, 4096, 128, 64, 64, 48, m=256)
@@ -226,7 +242,7 @@ def test_argument_errors():
         dgt.dgt_fused_decode_gemm(layer, x, ws=dgt.alloc_workspace(256)[:0])
     assert e.value.code in (-1, -4)
     import torch
-    big = torch.zeros((257, 512), dtype=torch.bfloat16, device="cuda")
+    big = torch.zeros(((1 << 16) + 1, 512), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(dgt.DgtError) as e:
         dgt.dgt_fused_decode_gemm(layer, big)
     assert e.value.code == -1

@@ -4,6 +4,7 @@ blob the oracle writes; dgt_layer_info validates like the oracle's parser."""
 
 import os
 import re
+import types
 
 import numpy as np
 import pytest
@@ -124,3 +125,18 @@ def test_device_calls_need_a_gpu_or_fail_loudly():
     b = dgt.dgt_compress_layer(dgt.DGT_FMT_INT8, d["codes"], 128, 32, 32)
     with pytest.raises(Exception):
         dgt.DeviceLayer(b, "cuda")
+
+
+def test_workspace_sizes_cover_every_pass():
+    """Host-side planner: the workspace for M rows covers the partial slots of
+    the largest pass and, for fp8, the quantised X of all M rows."""
+    d = workloads.random_small(dgt.DGT_FMT_FP8_E4M3, 512, 1024, seed=3)
+    info = dgt.dgt_layer_info(dgt.dgt_compress_layer(dgt.DGT_FMT_FP8_E4M3, d["codes"],
+                                                     256, 64, 64))
+    layer = types.SimpleNamespace(info=info)  # host-side size query: no device copy needed
+    w1, w256, w300, w513 = (dgt.dgt_gemm_workspace(layer, m) for m in (1, 256, 300, 513))
+    assert 0 < w1 < w256
+    assert w300 >= w256 + 300 * 1024 * 2 - 256 * 1024 * 2
+    assert w513 >= w256 + (513 - 256) * 1024 * 2
+    assert dgt.dgt_gemm_workspace(layer, 0) == 0
+    assert dgt.dgt_gemm_workspace(layer, (1 << 16) + 1) == 0
