@@ -106,6 +106,14 @@ namespace {
 
 using namespace dgt::dev;
 
+// u16 words of LDS per staged tile: the whole stream (longest tile + slack)
+// or, for R = 64, a two-chunk ring (any stream length).
+uint32_t region_words_of(const dgt_info* in, bool ring) {
+  if (ring) return kRingRegionWords;
+  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
+  return (words + 7) & ~7u;
+}
+
 bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
   if (!d_blob || !in) return false;
   const uint8_t* b = static_cast<const uint8_t*>(d_blob);
@@ -123,8 +131,7 @@ bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
   L->tiles = in->tiles;
   L->kt = in->k / in->tile_k;
   L->steps = in->tile_n * in->tile_k / dgt::weights_per_symbol(in->fmt) / in->lanes;
-  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
-  L->region_words = (words + 7) & ~7u;
+  L->region_words = region_words_of(in, false);  // a plan using the ring overrides it
   return true;
 }
 
@@ -136,6 +143,7 @@ int device_supported(const dgt_info* in) {
 }
 
 struct FusedPlan {
+  uint32_t ring, region_words;
   uint32_t mt, mix, waves, threads, cpw, n2, chains, cps, wgs, slots, strips, red_cols, lds;
   uint32_t m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
@@ -157,7 +165,7 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
 // LDS by waves that own disjoint row blocks, instead of one launch per chunk
 // of rows that each decode the whole layer.  Needs R = 64 and k-tiles per
 // strip divisible by the workgroup's wave count.
-bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
+bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   const uint32_t fn = in->tile_n / 16;
   if (in->lanes != 64 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
   if (m <= 16) return false;  // one register-resident pass (one 16-row block) covers M
@@ -165,8 +173,9 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
   if (m > nw * mtw * 16) return false;
   const uint32_t kt = in->k / in->tile_k;
   if (kt % nt) return false;
-  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
-  const uint32_t region_bytes = ((words + 7) & ~7u) * 2;
+  p->ring = ring ? 1 : 0;
+  p->region_words = region_words_of(in, ring);
+  const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
       (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nt * region_bytes + 16, 16);
   const uint32_t lds = xbuf_off + 2 * nt * 1024;
@@ -205,10 +214,10 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, FusedPlan* p) {
 // one pass is handled in chunks of m_chunk rows.  Chains per workgroup C is
 // the layer's chains over the CUs (one round) when the wave cap allows it;
 // beyond the cap the first n2 waves take two chains each (MIX kernels).
-bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
+bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, bool* lds_bound) {
   p->xm = 0;
-  if (plan_fused_xm(in, m, p)) return true;
-  p->xm = 0;
+  p->ring = ring ? 1 : 0;
+  p->region_words = region_words_of(in, ring);
   const uint32_t R = in->lanes, tpc = 64 / R;
   const uint32_t kt = in->k / in->tile_k;
   if (kt % tpc) return false;
@@ -218,8 +227,7 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   p->strips = in->n / in->tile_n;
   p->chains = in->tiles / tpc;
   p->cps = kt / tpc;
-  const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
-  const uint32_t chain_lds = tpc * ((words + 7) & ~7u) * 2;
+  const uint32_t chain_lds = tpc * p->region_words * 2;
   if (kLutBytes + kCumBytes + chain_lds > kMaxLds) return false;
   const uint32_t lds_cap = (kMaxLds - kLutBytes - kCumBytes) / chain_lds;
   const uint32_t fn = in->tile_n / 16 == 8 ? 8 : 16;
@@ -227,6 +235,7 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   const uint32_t w2 = fused_max_threads(R, fn, p->mt, 2) / 64;  // two-chain kernels
   uint32_t c = (p->chains + kCUs - 1) / kCUs;
   c = std::min(c, p->cps);
+  *lds_bound = c > lds_cap && lds_cap < 2 * std::max(w1, w2);
   c = std::min(c, lds_cap);
   if (c > w1 && p->cps % 2) c = w1;
   if (c <= w1) {
@@ -270,6 +279,22 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
   if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
   p->ws_bytes = off;
   return true;
+}
+
+// Staging choice (R = 64): whole streams when they fit the planned chains in
+// LDS and the launch is one round of workgroups; the ring when LDS would cap
+// the chains per CU or workgroups come in several rounds (each waits for one
+// chunk instead of its whole streams before decoding).
+bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
+  const bool r64 = in->lanes == 64;
+  if (plan_fused_xm(in, m, false, p)) return true;
+  if (r64 && plan_fused_xm(in, m, true, p)) return true;
+  bool lds_bound = false;
+  const bool whole = plan_fused_reg(in, m, false, p, &lds_bound);
+  if (!r64) return whole;
+  if (whole && !lds_bound && p->wgs <= kCUs) return true;
+  bool unused = false;
+  return plan_fused_reg(in, m, true, p, &unused);
 }
 
 int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t st,
@@ -328,10 +353,13 @@ bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c) {
 }
 
 // One pass of at most kPassRows rows with plan p.
-int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L, const uint8_t* xsrc,
+int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const uint8_t* xsrc,
                 uint32_t xrow, uint32_t m, const uint16_t* d_scales, float* sxp, float w_scale,
                 float* d_y, uint8_t* ws, int32_t* d_status, hipStream_t st) {
   const uint32_t fn = info->tile_n / 16;
+  const bool rg = p.ring != 0;
+  Layer L = L0;
+  L.region_words = p.region_words;
   if (p.xm) {
     XmArgs x;
     GemmArgs& a = x.g;
@@ -360,12 +388,12 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L, const 
     x.batches = p.batches;
     x.xbuf_off = p.xbuf_off;
     switch (info->fmt) {
-      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, p.wgs, p.lds, st);
-      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, p.wgs, p.lds, st);
-      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, fn, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, fn, p.wgs, p.lds, st);
-      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, p.wgs, p.lds, st);
+      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, rg, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
     }
   }
@@ -396,22 +424,22 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L, const 
     int rc;
     switch (info->fmt) {
       case DGT_FMT_INT8:
-        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_INT4:
-        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<INT4>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_INT4_PAIR:
-        rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<INT4P>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_BF16_EXP:
-        rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
-        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_BF16_SPLIT:
-        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st);
+        rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       default:
         rc = DGT_E_ARG;
@@ -495,8 +523,15 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   const uint32_t R = info->lanes, tpc = 64 / R;
   const uint32_t ilp = n_ids / tpc >= 1024 * 6 ? 2 : 1;
   uint32_t waves = 8;
-  const uint32_t region_bytes = a.L.region_words * 2;
-  auto lds_for = [&](uint32_t w) { return kLutBytes + kCumBytes + w * ilp * tpc * region_bytes; };
+  // whole streams when eight waves' tiles fit LDS, else (R = 64) the ring
+  bool ring = false;
+  auto lds_for = [&](uint32_t w) {
+    return kLutBytes + kCumBytes + w * ilp * tpc * a.L.region_words * 2;
+  };
+  if (R == 64 && lds_for(waves) > kMaxLds) {
+    ring = true;
+    a.L.region_words = region_words_of(info, true);
+  }
   while (waves > 4 && lds_for(waves) > kMaxLds) waves /= 2;
   if (lds_for(waves) > kMaxLds) return DGT_E_UNSUPPORTED;
   a.waves = waves;
@@ -505,12 +540,12 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   const uint32_t lds = lds_for(waves);
   hipStream_t st = static_cast<hipStream_t>(stream);
 switch (info->fmt) {
-    case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, grid, 64 * waves, lds, st);
-    case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, grid, 64 * waves, lds, st);
-    case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, grid, 64 * waves, lds, st);
-    case DGT_FMT_BF16_EXP: return launch_decode<BF16E>(a, R, ilp, grid, 64 * waves, lds, st);
-    case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, grid, 64 * waves, lds, st);
-    case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, grid, 64 * waves, lds, st);
+    case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_EXP: return launch_decode<BF16E>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     default: break;
   }
   return DGT_E_UNSUPPORTED;

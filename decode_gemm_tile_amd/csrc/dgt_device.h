@@ -127,16 +127,31 @@ __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32
 // R lane states of one chain: one tile (R = 64) or two tiles (R = 32).
 // Word positions are byte offsets into the workgroup's LDS; fields marked
 // "uniform" hold the same value on every lane.
+// A tile's words reach LDS either whole (staged before the first step) or
+// through a ring of two chunks (R = 64 only, see Ring below).
 struct Chain {
   uint32_t x;      // lane state
   uint32_t lim;    // first payload step of the lane's tile (steps - k)
-  uint32_t p0;     // uniform: next word of tile A (byte offset, not clamped)
+  uint32_t p0;     // uniform: next word of tile A: ring, 2 * words consumed;
+                   //   whole stream, LDS byte offset (not clamped)
   uint32_t p1;     // uniform: next word of tile B (R = 32)
-  uint32_t e0;     // uniform: end of tile A's staged words (byte offset)
+  uint32_t e0;     // uniform: ring, 2 * stream words; whole stream, end of A's words
   uint32_t e1;     // uniform: end of tile B's staged words
-  uint32_t s0;     // uniform: start of tile A's words (byte offset)
+  uint32_t s0;     // uniform: ring, LDS byte offset of the ring; whole stream, start of A's words
   uint32_t s1;     // uniform: start of tile B's words
 };
+
+// Ring staging (R = 64).  A fragment (8 steps) reads at most 8 * 64 words, so
+// a tile's stream is cut into chunks of that size and a ring of two chunks
+// holds the words any fragment can reach: before each fragment the chunk that
+// covers the furthest word it could read is written to the ring (loaded one
+// chunk ahead into registers), over the chunk two back, which is consumed.
+// Past the ring's end a mirror repeats the first 64 words of the even chunk
+// in slot 0, so a step's 64 consecutive words never wrap.
+constexpr uint32_t kChunkWords = 8 * 64;
+constexpr uint32_t kRingWords = 2 * kChunkWords;
+constexpr uint32_t kRingRegionWords = kRingWords + 64 + 8;  // ring, mirror, slack
+constexpr uint32_t kChunkDwords = kChunkWords / 2;          // 4 per lane
 
 // ILP chains advance one rANS step together, in three phases so that their
 // LDS round trips overlap: (1) table reads for every chain, (2) state update,
@@ -147,7 +162,7 @@ struct Chain {
 // number of renormalising lanes below p (mbcnt of the ballot).  CAREFUL also
 // handles the payload switch (x -= L at step == lim, no reads from then on).
 // Returns the table words (decoded symbol in the top byte).
-template <int R, bool CAREFUL, int ILP>
+template <int R, bool CAREFUL, int ILP, bool RING>
 __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
                                          const uint8_t* __restrict__ lds, uint32_t s,
                                          bool upper_half, uint32_t (&sym)[ILP]) {
@@ -170,7 +185,10 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
     const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
     uint32_t addr;
-    if (R == 64) {
+    if (R == 64 && RING) {
+      addr = 2 * rank + (c[i].s0 + (c[i].p0 & (2 * kRingWords - 1)));
+      c[i].p0 += 2 * (uint32_t)__builtin_popcountll(m);
+    } else if (R == 64) {
       addr = 2 * rank + min(c[i].p0, c[i].e0);
       c[i].p0 += 2 * (uint32_t)__builtin_popcountll(m);
     } else {
@@ -195,7 +213,7 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
 // Integrity flags of the chain's tile(s) after the last step, per lane's tile:
 // 1 = a lane did not return to its initial value, 2 = words consumed != stream
 // (a pad word may remain), 4 = read past the stream.
-template <int R>
+template <int R, bool RING>
 __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
                                                 bool upper_half) {
   const uint32_t want = (c.lim == steps) ? kL : 0u;
@@ -205,7 +223,7 @@ __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
                                                                  : (uint32_t)bad);
   if (half_bad) f |= 1u;
   const uint32_t p = (R == 32 && upper_half) ? c.p1 : c.p0;
-  const uint32_t st = (R == 32 && upper_half) ? c.s1 : c.s0;
+  const uint32_t st = RING ? 0u : ((R == 32 && upper_half) ? c.s1 : c.s0);
   const uint32_t en = (R == 32 && upper_half) ? c.e1 : c.e0;
   const uint32_t used = (p - st) / 2, avail = (en - st) / 2;  // words
   if (!(used == avail || used + 1 == avail)) f |= 2u;
@@ -255,6 +273,77 @@ __device__ __forceinline__ uint32_t stage_commit(const Staged& st, uint16_t* wor
   const uint32_t* src = st.src + sub_lane;
   for (int32_t i = kPre * sub_size; i < rem; i += sub_size) dst[i] = src[i];
   return 2 * st.words4;
+}
+
+// One tile's ring (R = 64): its stream, chunk count, committed chunks and the
+// next chunk in flight (4 dwords per lane: dwords lane + 64 * i of the chunk).
+struct Ring {
+  const uint32_t* tile;  // the tile's stream (states first)
+  int32_t last;          // last dword index of the tile's stream
+  uint32_t words4;       // uniform: stream dwords after the states
+  uint32_t nchunks;      // uniform
+  uint32_t cc;           // uniform: chunks written to the ring
+  uint32_t nxt[4];
+};
+
+// Load chunk j of the ring's tile into v (every lane loads, clamped to the
+// tile's own stream; dwords past the stream are never used).
+__device__ __forceinline__ void ring_load(const Ring& r, uint32_t j, uint32_t lane,
+                                          uint32_t (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t d = (int32_t)(64 + j * kChunkDwords + lane + 64 * i);
+    v[i] = r.tile[min(d, r.last)];
+  }
+}
+
+// Start tile t: chunk 0 into c0, chunk 1 in flight.
+__device__ __forceinline__ void ring_issue(const Layer& L, uint32_t t, uint32_t lane, Ring& r,
+                                           uint32_t (&c0)[4]) {
+  const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
+  r.tile = L.streams + o0;
+  r.last = (int32_t)(o1 - o0) - 1;
+  r.words4 = o1 - o0 - 64;
+  r.nchunks = (r.words4 + kChunkDwords - 1) / kChunkDwords;
+  r.cc = 0;
+  ring_load(r, 0, lane, c0);
+  ring_load(r, 1, lane, r.nxt);
+}
+
+// Write chunk j (in v) to its ring slot; even chunks after the first also
+// refresh the mirror.  base: LDS byte offset of the ring.
+// (Ring setup for a chain: ring_issue, then after the LUT barrier ring_start.)
+__device__ __forceinline__ void ring_write(uint8_t* lds, uint32_t base, uint32_t j, uint32_t lane,
+                                           const uint32_t (&v)[4]) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(lds + base) + (j & 1) * kChunkDwords + lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[64 * i] = v[i];
+  if ((j & 1) == 0 && j >= 2 && lane < 32)
+    reinterpret_cast<uint32_t*>(lds + base)[2 * kChunkDwords + lane] = v[0];
+}
+
+// Chunk 0 to the ring and the chain's word pointers (R = 64).
+__device__ __forceinline__ void ring_start(Ring& r, Chain& c, uint8_t* lds, uint32_t base,
+                                           uint32_t lane, const uint32_t (&c0)[4]) {
+  ring_write(lds, base, 0, lane, c0);
+  r.cc = min(1u, r.nchunks);
+  c.p0 = 0;
+  c.s0 = base;
+  c.e0 = 4 * r.words4;
+  c.p1 = 0; c.s1 = base; c.e1 = c.e0;
+}
+
+// Before a fragment whose first word is p (2 * words consumed): make sure the
+// chunk holding the furthest word the fragment can read is in the ring.  At
+// most one chunk per fragment is needed.
+__device__ __forceinline__ void ring_advance(Ring& r, uint8_t* lds, uint32_t base, uint32_t p,
+                                             uint32_t lane) {
+  const uint32_t need = ((p >> 1) + kChunkWords - 1) / kChunkWords;
+  if (r.cc < r.nchunks && r.cc <= need) {
+    ring_write(lds, base, r.cc, lane, r.nxt);
+    r.cc += 1;
+    if (r.cc < r.nchunks) ring_load(r, r.cc, lane, r.nxt);
+  }
 }
 
 }  // namespace dev

@@ -19,68 +19,79 @@ bool set_lds(K kernel, uint32_t bytes) {
          hipSuccess;
 }
 
-template <int R, int FN, int MT, bool MIX>
+template <int R, int FN, int MT, bool MIX, bool RING>
 int fused_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
-  auto k = k_fused<DGT_FMT, R, FN, MT, MIX>;
+  auto k = k_fused<DGT_FMT, R, FN, MT, MIX, RING>;
   if (!set_lds(k, lds)) return DGT_E_HIP;
   hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
 }
 
-template <int R, int FN>
+template <int R, int FN, bool RING>
 int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t threads,
             uint32_t lds, hipStream_t st) {
-  if (mt == 1 && !mix) return fused_t<R, FN, 1, false>(a, grid, threads, lds, st);
-  if (mt == 1 && mix) return fused_t<R, FN, 1, true>(a, grid, threads, lds, st);
+  if (mt == 1 && !mix) return fused_t<R, FN, 1, false, RING>(a, grid, threads, lds, st);
+  if (mt == 1 && mix) return fused_t<R, FN, 1, true, RING>(a, grid, threads, lds, st);
   if constexpr (FN <= 8) {
-    if (mt == 4 && !mix) return fused_t<R, FN, 4, false>(a, grid, threads, lds, st);
-    if (mt == 4 && mix) return fused_t<R, FN, 4, true>(a, grid, threads, lds, st);
+    if (mt == 4 && !mix) return fused_t<R, FN, 4, false, RING>(a, grid, threads, lds, st);
+    if (mt == 4 && mix) return fused_t<R, FN, 4, true, RING>(a, grid, threads, lds, st);
   }
   return DGT_E_UNSUPPORTED;
 }
 
 }  // namespace
 
+// The ring staging exists for R = 64 only.
 template <>
 int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt, bool mix,
-                          uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
-  if (lanes == 64 && fn == 8) return fused_r<64, 8>(a, mt, mix, grid, threads, lds, st);
-  if (lanes == 64 && fn == 16) return fused_r<64, 16>(a, mt, mix, grid, threads, lds, st);
-  if (lanes == 32 && fn == 8) return fused_r<32, 8>(a, mt, mix, grid, threads, lds, st);
-  if (lanes == 32 && fn == 16) return fused_r<32, 16>(a, mt, mix, grid, threads, lds, st);
+                          bool ring, uint32_t grid, uint32_t threads, uint32_t lds,
+                          hipStream_t st) {
+  if (lanes == 64 && fn == 8)
+    return ring ? fused_r<64, 8, true>(a, mt, mix, grid, threads, lds, st)
+                : fused_r<64, 8, false>(a, mt, mix, grid, threads, lds, st);
+  if (lanes == 64 && fn == 16)
+    return ring ? fused_r<64, 16, true>(a, mt, mix, grid, threads, lds, st)
+                : fused_r<64, 16, false>(a, mt, mix, grid, threads, lds, st);
+  if (ring) return DGT_E_UNSUPPORTED;
+  if (lanes == 32 && fn == 8) return fused_r<32, 8, false>(a, mt, mix, grid, threads, lds, st);
+  if (lanes == 32 && fn == 16) return fused_r<32, 16, false>(a, mt, mix, grid, threads, lds, st);
   return DGT_E_UNSUPPORTED;
 }
 
 template <>
-int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t fn, uint32_t grid, uint32_t lds,
-                             hipStream_t st) {
-#define DGT_XM_CASE(FNV)                                                        \
-  if (fn == FNV) {                                                              \
-    auto k = k_fused_xm<DGT_FMT, FNV>;                                          \
+int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t fn, bool ring, uint32_t grid,
+                             uint32_t lds, hipStream_t st) {
+#define DGT_XM_CASE(FNV, RG)                                                    \
+  if (fn == FNV && ring == RG) {                                                \
+    auto k = k_fused_xm<DGT_FMT, FNV, RG>;                                      \
     if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(FNV)), lds, st, x);    \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
   }
-  DGT_XM_CASE(8)
-  DGT_XM_CASE(16)
+  DGT_XM_CASE(8, false)
+  DGT_XM_CASE(8, true)
+  DGT_XM_CASE(16, false)
+  DGT_XM_CASE(16, true)
 #undef DGT_XM_CASE
   return DGT_E_UNSUPPORTED;
 }
 
 template <>
-int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, uint32_t grid,
-                           uint32_t threads, uint32_t lds, hipStream_t st) {
-#define DGT_DECODE_CASE(RR, II)                                                \
-  if (lanes == RR && ilp == II) {                                              \
-    auto k = k_decode<DGT_FMT, RR, II>;                                        \
+int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bool ring,
+                           uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st) {
+#define DGT_DECODE_CASE(RR, II, RG)                                            \
+  if (lanes == RR && ilp == II && ring == RG) {                                \
+    auto k = k_decode<DGT_FMT, RR, II, RG>;                                    \
     if (!set_lds(k, lds)) return DGT_E_HIP;                                    \
     hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);              \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;               \
   }
-  DGT_DECODE_CASE(64, 1)
-  DGT_DECODE_CASE(64, 2)
-  DGT_DECODE_CASE(32, 1)
-  DGT_DECODE_CASE(32, 2)
+  DGT_DECODE_CASE(64, 1, false)
+  DGT_DECODE_CASE(64, 2, false)
+  DGT_DECODE_CASE(64, 1, true)
+  DGT_DECODE_CASE(64, 2, true)
+  DGT_DECODE_CASE(32, 1, false)
+  DGT_DECODE_CASE(32, 2, false)
 #undef DGT_DECODE_CASE
   return DGT_E_UNSUPPORTED;
 }

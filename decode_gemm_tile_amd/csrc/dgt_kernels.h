@@ -295,9 +295,9 @@ __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
 }
 
 // Decode and multiply ILP chains (ch[0..ILP)) of one strip into acc.
-template <int FMT, int R, int FN, int MT, int ILP>
-__device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut,
-                                             const uint8_t* smem, Chain (&chs)[2],
+template <int FMT, int R, int FN, int MT, int ILP, bool RING>
+__device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut, uint8_t* smem,
+                                             Chain (&chs)[2], Ring (&rgs)[2],
                                              const uint32_t (&tile_lane)[2],
                                              const uint32_t (&k0_lane)[2], uint32_t strip,
                                              floatx4 (&acc)[FN][MT]) {
@@ -305,6 +305,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
   constexpr uint32_t FW = R / 2;  // fragment width (columns)
   constexpr int SPF = steps_per_frag<FMT>();
   Chain (&ch)[ILP] = *reinterpret_cast<Chain(*)[ILP]>(&chs[0]);
+  Ring (&rg)[ILP] = *reinterpret_cast<Ring(*)[ILP]>(&rgs[0]);
   const uint32_t lane = lane_id();
   const bool upper = lane >= 32;
   // the word pointers are wave-uniform: keep them (and their updates) scalar
@@ -312,6 +313,10 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
   for (int c = 0; c < ILP; ++c) {
     ch[c].p0 = uniform(ch[c].p0); ch[c].e0 = uniform(ch[c].e0); ch[c].s0 = uniform(ch[c].s0);
     ch[c].p1 = uniform(ch[c].p1); ch[c].e1 = uniform(ch[c].e1); ch[c].s1 = uniform(ch[c].s1);
+    if (RING) {
+      rg[c].cc = uniform(rg[c].cc);
+      rg[c].nchunks = uniform(rg[c].nchunks);
+    }
   }
   uint32_t lim_min = ch[0].lim;
 #pragma unroll
@@ -382,13 +387,17 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
         if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
       }
+      if constexpr (RING) {
+#pragma unroll
+        for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+      }
       uint32_t e[ILP][SPF];
       // payload steps (at most the last kPayloadMax) fall in the last fragments
       if (fn < FN - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min) {
 #pragma unroll
         for (int i = 0; i < SPF; ++i) {
           uint32_t sy[ILP];
-          step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
+          step_all<R, false, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
           for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
         }
@@ -396,7 +405,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
 #pragma unroll
         for (int i = 0; i < SPF; ++i) {
           uint32_t sy[ILP];
-          step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
+          step_all<R, true, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
           for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
         }
@@ -413,13 +422,15 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
     const uint32_t half_lane = lane & 31;
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
-      const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
+      const uint32_t f = final_flags<R, RING>(ch[c], L.steps, upper);
       if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
     }
   }
 }
 
-template <int FMT, int R, int FN, int MT, bool MIX>
+// RING (R = 64 only): stream the tile words through a two-chunk ring instead
+// of staging them whole (any stream length; less LDS per chain).
+template <int FMT, int R, int FN, int MT, bool MIX, bool RING>
 __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_fused(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
@@ -445,10 +456,12 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   Chain ch[2];
   uint32_t tile_lane[2] = {0u, 0u};
   uint32_t k0_lane[2] = {0u, 0u};
-  Staged stg[2];
+  Staged stg[2];   // R = 32: whole streams
+  Ring rg[2];      // R = 64: chunk 0 (c0) now, later chunks through the ring
+  uint32_t c0[2][4];
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
-  // 3) write the streams to LDS.  Both chain slots always load (a missing
+  // 3) write the first words to LDS.  Both chain slots always load (a missing
   // second chain repeats the first) so that every wave has the same loads in
   // flight and the LUT build waits for the table alone.
 #pragma unroll
@@ -457,7 +470,10 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     const uint32_t ta = strip * L.kt + kt_first + cc * TPC;
     const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
     tile_lane[c] = t_l;
-    stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
+    if constexpr (RING)
+      ring_issue(L, t_l, lane, rg[c], c0[c]);
+    else
+      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
     ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
     const uint32_t kt_l = kt_first + cc * TPC + ((R == 32 && upper) ? 1u : 0u);
     k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
@@ -473,14 +489,18 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   for (int c = 0; c < 2; ++c) {
     if (c < (int)nch) {
       const uint32_t ra = (cw + c) * TPC * L.region_words;
-      const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
-      const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
-                                         R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
-      const uint32_t na = uniform(mine);
-      const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-      const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
-      ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
-      ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
+      if constexpr (RING) {
+        ring_start(rg[c], ch[c], smem, kLutBytes + kCumBytes + 2 * ra, lane, c0[c]);
+      } else {
+        const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
+        const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
+                                           R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
+        const uint32_t na = uniform(mine);
+        const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
+        const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
+        ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
+        ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
+      }
     }
   }
 
@@ -491,12 +511,12 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MIX) {
     if (nch == 2)
-      fused_chains<FMT, R, FN, MT, 2>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 2, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
     else if (nch == 1)
-      fused_chains<FMT, R, FN, MT, 1>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
   } else {
     if (nch == 1)
-      fused_chains<FMT, R, FN, MT, 1>(a, lut, smem, ch, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
   }
   float out_scale = 1.f;
   if constexpr (FMT == FP8)
@@ -618,7 +638,7 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
 }
 
 // R = 64 lanes (one tile per chain) and tile_k = 64 only.
-template <int FMT, int FN>
+template <int FMT, int FN, bool RING>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr uint32_t R = 64, FW = 32, TK = 64, FK = TK / FW, G = FK * FN;
@@ -651,24 +671,37 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     // chain c of this wave decodes batch tile j = c * NW + wave
     uint32_t tj[ILP];
     Chain ch[ILP];
+    Ring rg[ILP];
+    uint32_t c0[ILP][4];
     Staged stg[ILP];
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       tj[c] = strip * L.kt + kt0 + c * NW + wave;
-      stage_issue(L, tj[c], lane, 64u, stg[c]);
+      if constexpr (RING)
+        ring_issue(L, tj[c], lane, rg[c], c0[c]);
+      else
+        stage_issue(L, tj[c], lane, 64u, stg[c]);
       ch[c].x = L.streams[L.index[tj[c]] + lane];
-      ch[c].lim = L.steps - (uint32_t)L.ktab[tj[c]];
     }
     if (b == b0) build_lut(fq, L.alphabet, lut, cum);
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tj[c]];
     __syncthreads();  // LUT complete; the previous batch's fragment reads are done
     uint32_t lim_min = 0xFFFFFFFFu;
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t region = (wave * ILP + c) * L.region_words;
-      const uint32_t n = uniform(stage_commit(stg[c], words, region, lane, 64u));
       const uint32_t base = kLutBytes + kCumBytes + 2 * region;
-      ch[c].p0 = base; ch[c].s0 = base; ch[c].e0 = base + 2 * n;
-      ch[c].p1 = base; ch[c].s1 = base; ch[c].e1 = base + 2 * n;
+      if constexpr (RING) {
+        ring_start(rg[c], ch[c], smem, base, lane, c0[c]);
+        ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
+        rg[c].cc = uniform(rg[c].cc);
+        rg[c].nchunks = uniform(rg[c].nchunks);
+      } else {
+        const uint32_t n = uniform(stage_commit(stg[c], words, region, lane, 64u));
+        ch[c].p0 = base; ch[c].s0 = base; ch[c].e0 = base + 2 * n;
+        ch[c].p1 = base; ch[c].s1 = base; ch[c].e1 = base + 2 * n;
+      }
       lim_min = min(lim_min, uniform(ch[c].lim));
     }
     auto load_raw = [&](int c, uint32_t g) -> u32x2 {
@@ -724,12 +757,16 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
           if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
         }
+        if constexpr (RING) {
+#pragma unroll
+          for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+        }
         uint32_t e[ILP][SPF];
         auto steps = [&](auto careful) {
 #pragma unroll
           for (int i = 0; i < SPF; ++i) {
             uint32_t sy[ILP];
-            step_all<64, decltype(careful)::value, ILP>(ch, lut, smem, s0 + i, false, sy);
+            step_all<64, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, false, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
           }
@@ -773,7 +810,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     if (a.status) {
 #pragma unroll
       for (int c = 0; c < ILP; ++c) {
-        const uint32_t fl = final_flags<64>(ch[c], L.steps, false);
+        const uint32_t fl = final_flags<64, RING>(ch[c], L.steps, false);
         if (lane == 0) a.status[tj[c]] = (int32_t)fl;
       }
     }
@@ -791,7 +828,7 @@ struct DecodeArgs {
   uint32_t waves;
 };
 
-template <int FMT, int R, int ILP>
+template <int FMT, int R, int ILP, bool RING>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
@@ -808,30 +845,42 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
-  Staged stg[ILP];
+  Staged stg[ILP];  // R = 32
+  Ring rg[ILP];     // R = 64
+  uint32_t c0[ILP][4];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
-  if (active) {
+  // every wave issues the same loads (an idle wave repeats the last id) so
+  // the LUT build waits for the table alone
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      // slots past the end repeat the last id (same tile decoded twice, same output)
-      const uint32_t ia = min(first + c * TPC, a.n_ids - 1);
-      const uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
-      const uint32_t ta = a.ids ? a.ids[ia] : ia;
-      const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
-      const uint32_t t_l = (R == 32 && upper) ? tb : ta;
-      tile_lane[c] = t_l;
+  for (int c = 0; c < ILP; ++c) {
+    // slots past the end repeat the last id (same tile decoded twice, same output)
+    const uint32_t ia = min(first + c * TPC, a.n_ids - 1);
+    const uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
+    const uint32_t ta = a.ids ? a.ids[ia] : ia;
+    const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
+    const uint32_t t_l = (R == 32 && upper) ? tb : ta;
+    tile_lane[c] = t_l;
+    if constexpr (RING)
+      ring_issue(L, t_l, lane, rg[c], c0[c]);
+    else
       stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
-      ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
-      ch[c].lim = L.steps - (uint32_t)L.ktab[t_l];
-    }
+    ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
   }
   build_lut(fq, L.alphabet, lut, cum);
-  __syncthreads();  // LUT complete; each wave's staged stream is private to it
-  if (active) {
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      const uint32_t ra = region0 + c * TPC * L.region_words;
+  for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
+  __syncthreads();  // LUT complete; each wave's staged stream is private to it
+  if (!active) return;
+#pragma unroll
+  for (int c = 0; c < ILP; ++c) {
+    const uint32_t ra = region0 + c * TPC * L.region_words;
+    if constexpr (RING) {
+      ring_start(rg[c], ch[c], smem, kLutBytes + kCumBytes + 2 * ra, lane, c0[c]);
+      ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
+      rg[c].cc = uniform(rg[c].cc);
+      rg[c].nchunks = uniform(rg[c].nchunks);
+    } else {
       const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
       const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
                                          R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
@@ -842,7 +891,6 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
     }
   }
-  if (!active) return;
   uint32_t lim_min = L.steps;
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
@@ -855,12 +903,16 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   const uint32_t p = lane % R;
   for (uint32_t g = 0; g < G; ++g) {
     const uint32_t s0 = g * SPF;
+    if constexpr (RING) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+    }
     uint32_t e[ILP][SPF];
     if (s0 + SPF - 1 < lim_min) {
 #pragma unroll
       for (int i = 0; i < SPF; ++i) {
         uint32_t sy[ILP];
-        step_all<R, false, ILP>(ch, lut, smem, s0 + i, upper, sy);
+        step_all<R, false, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
       }
@@ -868,7 +920,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < SPF; ++i) {
         uint32_t sy[ILP];
-        step_all<R, true, ILP>(ch, lut, smem, s0 + i, upper, sy);
+        step_all<R, true, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
       }
@@ -907,7 +959,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   if (a.status) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
-      const uint32_t f = final_flags<R>(ch[c], L.steps, upper);
+      const uint32_t f = final_flags<R, RING>(ch[c], L.steps, upper);
       if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
     }
   }
