@@ -27,6 +27,16 @@ Formats whose symbol packs two weights (int4 pairs) apply the same map to
 the matrix of symbols with epl = 4 symbols per lane per fragment: a fragment
 is then 16 rows x (R/16)*4 symbols, i.e. the same 16 x R/2 weights, and a
 lane's 4 symbols are its 8 consecutive-column weights.
+
+Two states per lane (R = 128, a reading for a 64-wide wavefront: the pages
+put one state on each of the warp's lanes and leave R free): the tile's top
+Tn/2 rows and bottom Tn/2 rows are two halves, each ordered as an R = 64 tile
+of shape (Tn/2) x Tk; state p < 64 codes the top half's lane p, state 64 + p
+the bottom half's lane p, and both share the tile's one word stream through
+the interleaving j = s*128 + p.  A wave lane p then holds states p and
+64 + p, whose values at a step are the same column of two row bands, so the
+two matrix-core products of a fragment share their X operand.  Raw bytes:
+q = g*1024 + p*8 + e with p in [0, 128), the half's R = 64 raw order.
 """
 
 import numpy as np
@@ -38,14 +48,34 @@ def check_geometry(n: int, k: int, tile_n: int, tile_k: int, lanes: int,
         raise ValueError("sizes must be positive")
     if n % tile_n or k % tile_k:
         raise ValueError("N and K must be multiples of the tile shape")
+    if lanes == 128:  # two R = 64 halves of Tn/2 rows
+        if tile_n % 32:
+            raise ValueError("two states per lane need tile_n a multiple of 32")
+        lanes = 64
     if lanes % 16 or tile_n % 16:
         raise ValueError("lanes and tile_n must be multiples of 16")
     if tile_k % ((lanes // 16) * epl):
         raise ValueError("tile_k must be a multiple of the fragment width")
 
 
+def _halves(pos_of_half, tile_n: int, count: int, per_block: int):
+    """Positions for R = 128 from the R = 64 positions of a (Tn/2)-row half:
+    index i splits into (block b, state p in [0,128), rest) with per_block
+    entries per state; p // 64 picks the half, p % 64 the half's lane."""
+    i = np.arange(count, dtype=np.int64)
+    b, rem = i // (128 * per_block), i % (128 * per_block)
+    p, r = rem // per_block, rem % per_block
+    h = p // 64
+    i_half = (b * 64 + p % 64) * per_block + r
+    rows, cols = pos_of_half
+    return rows[i_half] + h * (tile_n // 2), cols[i_half]
+
+
 def tile_positions(tile_n: int, tile_k: int, lanes: int, epl: int = 8):
     """(rows[j], cols[j]) inside the tile for symbol index j = s*R + p."""
+    if lanes == 128:
+        half = tile_positions(tile_n // 2, tile_k, 64, epl)
+        return _halves(half, tile_n, tile_n * tile_k, 1)
     R = lanes
     fw = (R // 16) * epl
     fn_count = tile_n // 16
@@ -64,6 +94,9 @@ def tile_positions(tile_n: int, tile_k: int, lanes: int, epl: int = 8):
 
 def raw_positions(tile_n: int, tile_k: int, lanes: int):
     """(rows[q], cols[q]) inside the tile for raw-byte index q = g*8R + p*8 + e."""
+    if lanes == 128:
+        half = raw_positions(tile_n // 2, tile_k, 64)
+        return _halves(half, tile_n, tile_n * tile_k, 8)
     R = lanes
     fw = R // 2
     fn_count = tile_n // 16

@@ -21,6 +21,13 @@ CASES = [
     (blob.FMT_INT4_PAIR, 32, 32, 16, 16, 16),
     (blob.FMT_BF16_EXP, 256, 128, 128, 64, 64),
     (blob.FMT_BF16_EXP, 32, 16, 16, 8, 16),
+    # two states per lane (R = 128): tile halves of Tn/2 rows
+    (blob.FMT_INT8, 128, 64, 64, 32, 128),
+    (blob.FMT_INT4, 256, 256, 128, 64, 128),
+    (blob.FMT_FP8, 256, 128, 256, 64, 128),
+    (blob.FMT_BF16, 256, 128, 128, 64, 128),
+    (blob.FMT_INT4_PAIR, 256, 256, 128, 64, 128),
+    (blob.FMT_BF16_EXP, 64, 128, 32, 64, 128),
 ]
 
 

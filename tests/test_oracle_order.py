@@ -6,7 +6,8 @@ import pytest
 from oracle import order
 
 GEOMS = [(16, 8, 16), (16, 32, 64), (128, 32, 32), (128, 64, 64), (256, 64, 64),
-         (32, 16, 32), (48, 24, 16)]
+         (32, 16, 32), (48, 24, 16), (32, 64, 128), (128, 64, 128), (256, 64, 128),
+         (96, 128, 128)]
 
 
 @pytest.mark.parametrize("tn,tk,R", GEOMS)
@@ -39,6 +40,38 @@ def test_hand_checked_positions_r32():
     assert (r[8 * 8 * 32], c[8 * 8 * 32]) == (0, 16)  # after 8 row bands: column block 1
 
 
+def test_hand_checked_positions_two_states_per_lane():
+    """R = 128 on a 64x64 tile: states 0..63 walk the top 32 rows as an R = 64
+    tile would, states 64..127 the bottom 32 rows."""
+    r, c = order.tile_positions(64, 64, 128)
+    assert (r[0], c[0]) == (0, 0)
+    assert (r[17], c[17]) == (1, 8)            # state 17: row 1, column group 1
+    assert (r[64], c[64]) == (32, 0)           # state 64 = lane 0 of the bottom half
+    assert (r[127], c[127]) == (47, 24)        # state 127 = lane 63 of the bottom half
+    assert (r[128], c[128]) == (0, 1)          # step 1
+    assert (r[8 * 128], c[8 * 128]) == (16, 0)       # fragment 1: the half's second band
+    assert (r[16 * 128], c[16 * 128]) == (0, 32)     # fragment 2: next column block
+    assert (r[16 * 128 + 64], c[16 * 128 + 64]) == (32, 32)
+    # raw bytes: block g = 0 holds state p's 8 values at q = p*8 + e
+    rr, cr = order.raw_positions(64, 64, 128)
+    assert (rr[8 * 64 + 3], cr[8 * 64 + 3]) == (32, 3)
+    assert (rr[1024], cr[1024]) == (16, 0)
+
+
+@pytest.mark.parametrize("tn,tk", [(64, 64), (128, 64), (256, 64), (64, 128)])
+def test_two_states_share_the_column_of_two_row_bands(tn, tk):
+    """At every step, a wave lane's two states (p and 64 + p) decode the same
+    column in rows Tn/2 apart, and over 8 steps lane p's values form the
+    matrix-core operand of its row (p % 16) and 8 columns (8 * (p // 16) + e)."""
+    r, c = order.tile_positions(tn, tk, 128)
+    S = tn * tk // 128
+    for s in range(S):
+        for p in range(64):
+            ja, jb = s * 128 + p, s * 128 + 64 + p
+            assert c[ja] == c[jb] and r[jb] == r[ja] + tn // 2
+            assert r[ja] % 16 == p % 16 and (c[ja] % 32) == 8 * (p // 16) + s % 8
+
+
 @pytest.mark.parametrize("tn,tk,R", GEOMS)
 def test_raw_order_is_lane_major_symbol_order(tn, tk, R):
     """raw index q = g*8R + p*8 + e holds the element of symbol j = (8g+e)*R + p."""
@@ -54,7 +87,7 @@ def test_raw_order_is_lane_major_symbol_order(tn, tk, R):
 def test_gather_scatter_inverse():
     rng = np.random.default_rng(0)
     w = rng.integers(0, 256, (256, 192)).astype(np.uint8)
-    for R, tn, tk in [(64, 128, 64), (32, 128, 32), (16, 16, 8)]:
+    for R, tn, tk in [(64, 128, 64), (32, 128, 32), (16, 16, 8), (128, 128, 64), (128, 64, 64)]:
         for raw in (False, True):
             t = order.gather_tiles(w, tn, tk, R, raw=raw)
             assert t.shape == ((256 // tn) * (192 // tk), tn * tk)
@@ -66,12 +99,13 @@ def test_gather_scatter_inverse():
 
 def test_geometry_errors():
     for args in [(100, 64, 128, 64, 64), (128, 64, 128, 64, 48), (128, 64, 120, 64, 64),
-                 (128, 48, 128, 48, 64)]:
+                 (128, 48, 128, 48, 64), (96, 64, 48, 64, 128), (128, 16, 128, 16, 128)]:
         with pytest.raises(ValueError):
             order.check_geometry(*args)
 
 
-@pytest.mark.parametrize("tn,tk,R", [(32, 16, 16), (128, 32, 64), (128, 16, 32), (256, 32, 64)])
+@pytest.mark.parametrize("tn,tk,R", [(32, 16, 16), (128, 32, 64), (128, 16, 32), (256, 32, 64),
+                                     (128, 32, 128), (64, 64, 128)])
 def test_pair_positions_cover_each_lanes_eight_weights(tn, tk, R):
     """Pair layout (epl = 4 on the [rows, tk] pair matrix, i.e. tiles of 2*tk
     weights): lane p's 4 symbols of fragment g are exactly the weights that

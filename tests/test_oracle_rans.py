@@ -58,7 +58,7 @@ def test_brute_force_round_trip(alpha, lanes, kmax):
 def test_vectorised_equals_scalar(seed):
     rng = np.random.default_rng(seed)
     alpha = int(rng.integers(2, 40))
-    lanes = int(rng.choice([1, 2, 4, 16, 32, 64]))
+    lanes = int(rng.choice([1, 2, 4, 16, 32, 64, 128]))
     steps = int(rng.integers(1, 40))
     tiles = int(rng.integers(1, 5))
     counts = rng.integers(1, 500, alpha) ** 2
