@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/dgt.h"
 #include "dgt_format.h"
@@ -107,7 +109,7 @@ namespace {
 using namespace dgt::dev;
 
 // u16 words of LDS per staged tile: the whole stream (longest tile + slack)
-// or, for R = 64, a two-chunk ring (any stream length).
+// or, for one tile per chain (R = 64, 128), a two-chunk ring (any length).
 uint32_t region_words_of(const dgt_info* in, bool ring) {
   if (ring) return kRingRegionWords;
   const uint32_t words = 2 * (in->max_tile_words4 - in->lanes) + kSlackWords;
@@ -138,7 +140,7 @@ bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
 int device_supported(const dgt_info* in) {
   if (!in) return DGT_E_ARG;
   if (in->prob_bits != 12) return DGT_E_UNSUPPORTED;
-  if (in->lanes != 32 && in->lanes != 64) return DGT_E_UNSUPPORTED;
+  if (in->lanes != 32 && in->lanes != 64 && in->lanes != 128) return DGT_E_UNSUPPORTED;
   return DGT_OK;
 }
 
@@ -163,11 +165,12 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
 
 // Large M: one launch in which every tile is decoded once and shared through
 // LDS by waves that own disjoint row blocks, instead of one launch per chunk
-// of rows that each decode the whole layer.  Needs R = 64 and k-tiles per
-// strip divisible by the workgroup's wave count.
+// of rows that each decode the whole layer.  Needs R = 64 or 128 and k-tiles
+// per strip divisible by the workgroup's wave count.
 bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   const uint32_t fn = in->tile_n / 16;
-  if (in->lanes != 64 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
+  if (in->lanes == 32 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
+  const uint32_t ns = in->lanes == 128 ? 2 : 1;  // operands per wave and fragment
   if (m <= 16) return false;  // one register-resident pass (one 16-row block) covers M
   const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn), nt = xm_tiles(fn);
   if (m > nw * mtw * 16) return false;
@@ -178,7 +181,7 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
       (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nt * region_bytes + 16, 16);
-  const uint32_t lds = xbuf_off + 2 * nt * 1024;
+  const uint32_t lds = xbuf_off + 2 * nt * ns * 1024;
   if (lds > kMaxLds) return false;
   p->xm = 1;
   p->xbuf_off = xbuf_off;
@@ -218,7 +221,7 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
   p->xm = 0;
   p->ring = ring ? 1 : 0;
   p->region_words = region_words_of(in, ring);
-  const uint32_t R = in->lanes, tpc = 64 / R;
+  const uint32_t R = in->lanes, tpc = R == 32 ? 2 : 1;
   const uint32_t kt = in->k / in->tile_k;
   if (kt % tpc) return false;
   // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
@@ -281,19 +284,38 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
   return true;
 }
 
-// Staging choice (R = 64): whole streams when they fit the planned chains in
-// LDS and the launch is one round of workgroups; the ring when LDS would cap
-// the chains per CU or workgroups come in several rounds (each waits for one
-// chunk instead of its whole streams before decoding).
-bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p) {
-  const bool r64 = in->lanes == 64;
+// How tile streams reach LDS: chosen per layer, or forced by the environment
+// variable DGT_STAGING ("whole" or "ring"; results are identical).
+enum Staging { kAuto = 0, kWhole = 1, kRing = 2 };
+Staging staging_from_env() {
+  const char* v = std::getenv("DGT_STAGING");
+  if (v && std::strcmp(v, "ring") == 0) return kRing;
+  if (v && std::strcmp(v, "whole") == 0) return kWhole;
+  return kAuto;
+}
+
+// Staging choice (one tile per chain: R = 64, 128): whole streams when they
+// fit the planned chains in LDS and the launch is one round of workgroups;
+// the ring when LDS would cap the chains per CU or workgroups come in several
+// rounds (each waits for one chunk instead of its whole streams to decode).
+// A forced staging that cannot serve the layer falls back to the choice.
+bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg) {
+  const bool r64 = in->lanes != 32;
+  bool unused = false;
+  if (sg == kRing && r64) {
+    if (plan_fused_xm(in, m, true, p)) return true;
+    if (plan_fused_reg(in, m, true, p, &unused)) return true;
+  }
+  if (sg == kWhole) {
+    if (plan_fused_xm(in, m, false, p)) return true;
+    if (plan_fused_reg(in, m, false, p, &unused)) return true;
+  }
   if (plan_fused_xm(in, m, false, p)) return true;
   if (r64 && plan_fused_xm(in, m, true, p)) return true;
   bool lds_bound = false;
   const bool whole = plan_fused_reg(in, m, false, p, &lds_bound);
   if (!r64) return whole;
   if (whole && !lds_bound && p->wgs <= kCUs) return true;
-  bool unused = false;
   return plan_fused_reg(in, m, true, p, &unused);
 }
 
@@ -334,16 +356,16 @@ struct CallPlan {
   size_t quant_off, ws_bytes;
 };
 
-bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c) {
+bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c, Staging sg) {
   c->n_full = m / kPassRows;
   c->rest_rows = m % kPassRows;
   size_t q = 0;
   if (c->n_full) {
-    if (!plan_fused(in, kPassRows, &c->full)) return false;
+    if (!plan_fused(in, kPassRows, &c->full, sg)) return false;
     q = std::max(q, c->full.quant_off);
   }
   if (c->rest_rows) {
-    if (!plan_fused(in, c->rest_rows, &c->rest)) return false;
+    if (!plan_fused(in, c->rest_rows, &c->rest, sg)) return false;
     q = std::max(q, c->rest.quant_off);
   }
   c->quant_off = q;
@@ -388,12 +410,12 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     x.batches = p.batches;
     x.xbuf_off = p.xbuf_off;
     switch (info->fmt) {
-      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
     }
   }
@@ -412,7 +434,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     a.x_row_bytes = xrow;
     a.y_row = info->n;
     a.waves = p.waves;
-    a.tpw = 64 / info->lanes;
+    a.tpw = info->lanes == 32 ? 2 : 1;
     a.chains = p.chains;
     a.cps = p.cps;
     a.cpw = p.cpw;
@@ -455,9 +477,14 @@ extern "C" {
 
 size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
   if (!info || m == 0 || m > kMaxRows) return 0;
-  CallPlan c;
-  if (!plan_call(info, m, &c)) return 0;
-  return c.ws_bytes;
+  // enough for every staging, so the environment may change between calls
+  size_t ws = 0;
+  for (Staging sg : {kAuto, kWhole, kRing}) {
+    CallPlan c;
+    if (!plan_call(info, m, &c, sg)) return 0;
+    ws = std::max(ws, c.ws_bytes);
+  }
+  return ws;
 }
 
 int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
@@ -475,7 +502,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
   if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
   if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
   CallPlan c;
-  if (!plan_call(info, m, &c)) return DGT_E_UNSUPPORTED;
+  if (!plan_call(info, m, &c, staging_from_env())) return DGT_E_UNSUPPORTED;
   if (ws_bytes < c.ws_bytes) return DGT_E_BUFSIZE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Layer L;
@@ -520,18 +547,21 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   a.n_ids = n_ids;
   a.out = static_cast<uint8_t*>(d_out);
   a.status = d_status;
-  const uint32_t R = info->lanes, tpc = 64 / R;
+  const uint32_t R = info->lanes, tpc = R == 32 ? 2 : 1;
   const uint32_t ilp = n_ids / tpc >= 1024 * 6 ? 2 : 1;
   uint32_t waves = 8;
-  // whole streams when eight waves' tiles fit LDS, else (R = 64) the ring
+  // whole streams when eight waves' tiles fit LDS, else (R = 64, 128) the ring
   bool ring = false;
   auto lds_for = [&](uint32_t w) {
     return kLutBytes + kCumBytes + w * ilp * tpc * a.L.region_words * 2;
   };
-  if (R == 64 && lds_for(waves) > kMaxLds) {
-    ring = true;
-    a.L.region_words = region_words_of(info, true);
+  const Staging sg = staging_from_env();
+  if (R != 32) {
+    if (sg == kRing) ring = true;
+    else if (sg == kWhole) ring = lds_for(4) > kMaxLds;
+    else ring = lds_for(waves) > kMaxLds;
   }
+  if (ring) a.L.region_words = region_words_of(info, true);
   while (waves > 4 && lds_for(waves) > kMaxLds) waves /= 2;
   if (lds_for(waves) > kMaxLds) return DGT_E_UNSUPPORTED;
   a.waves = waves;
@@ -539,7 +569,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   const uint32_t grid = (n_ids + per_wg - 1) / per_wg;
   const uint32_t lds = lds_for(waves);
   hipStream_t st = static_cast<hipStream_t>(stream);
-switch (info->fmt) {
+  switch (info->fmt) {
     case DGT_FMT_INT8: return launch_decode<INT8>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, ring, grid, 64 * waves, lds, st);

@@ -7,8 +7,9 @@
 // next tile overlaps the product of the current one.
 //
 // MI355X mapping used here:
-//   * one wave64 holds the R lane states of one tile (R = 64) or of two tiles
-//     (R = 32, lanes 0-31 and 32-63);
+//   * one wave64 holds the R lane states of one tile (R = 64), of two tiles
+//     (R = 32, lanes 0-31 and 32-63) or two states of one tile per lane
+//     (R = 128: states p and 64 + p, the tile's top and bottom row halves);
 //   * the per-layer decode table lives in LDS: 4096 slots x 8 bytes
 //     {f | symbol << 24, slot - c_s}, so one ds_read_b64 gives everything a
 //     step needs and the state update is a single v_mad_u32_u24;
@@ -51,6 +52,8 @@ template <int FMT>
 __host__ __device__ constexpr int steps_per_frag() { return FMT == INT4P ? 4 : 8; }
 // At most this many final steps of a tile decode the initial-state payload.
 constexpr uint32_t kPayloadMax = 16;
+// rANS states a wave lane holds for one chain: two when R = 128.
+__host__ __device__ constexpr int states_per_lane(int R) { return R == 128 ? 2 : 1; }
 
 // Everything a kernel needs to know about a layer (passed by value).
 struct Layer {
@@ -124,13 +127,14 @@ __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32
   }
 }
 
-// R lane states of one chain: one tile (R = 64) or two tiles (R = 32).
+// R lane states of one chain: one tile (R = 64 or 128) or two tiles (R = 32).
 // Word positions are byte offsets into the workgroup's LDS; fields marked
 // "uniform" hold the same value on every lane.
 // A tile's words reach LDS either whole (staged before the first step) or
-// through a ring of two chunks (R = 64 only, see Ring below).
+// through a ring of two chunks (R = 64 or 128, see Ring below).
 struct Chain {
-  uint32_t x;      // lane state
+  uint32_t x;      // lane state (R = 128: state p, top half of the tile)
+  uint32_t x2;     // R = 128: state 64 + p (bottom half)
   uint32_t lim;    // first payload step of the lane's tile (steps - k)
   uint32_t p0;     // uniform: next word of tile A: ring, 2 * words consumed;
                    //   whole stream, LDS byte offset (not clamped)
@@ -141,73 +145,90 @@ struct Chain {
   uint32_t s1;     // uniform: start of tile B's words
 };
 
-// Ring staging (R = 64).  A fragment (8 steps) reads at most 8 * 64 words, so
-// a tile's stream is cut into chunks of that size and a ring of two chunks
-// holds the words any fragment can reach: before each fragment the chunk that
-// covers the furthest word it could read is written to the ring (loaded one
-// chunk ahead into registers), over the chunk two back, which is consumed.
-// Past the ring's end a mirror repeats the first 64 words of the even chunk
-// in slot 0, so a step's 64 consecutive words never wrap.
+// Ring staging (R = 64 or 128).  8 steps of 64 states (4 steps of 128) read
+// at most 512 words, so a tile's stream is cut into chunks of that size and a
+// ring of two chunks holds the words any such group of steps can reach:
+// before each group the chunk that covers the furthest word it could read is
+// written to the ring (loaded one chunk ahead into registers), over the chunk
+// two back, which is consumed.  Past the ring's end a mirror repeats the first
+// 64 words of the even chunk in slot 0, so the (at most 64) consecutive words
+// one state of every lane reads never wrap.
 constexpr uint32_t kChunkWords = 8 * 64;
 constexpr uint32_t kRingWords = 2 * kChunkWords;
 constexpr uint32_t kRingRegionWords = kRingWords + 64 + 8;  // ring, mirror, slack
 constexpr uint32_t kChunkDwords = kChunkWords / 2;          // 4 per lane
+// steps between ring advances
+__host__ __device__ constexpr int ring_group_steps(int R) { return (int)kChunkWords / R; }
 
 // ILP chains advance one rANS step together, in three phases so that their
-// LDS round trips overlap: (1) table reads for every chain, (2) state update,
-// wave ballot of the lanes that renormalise, word reads for every chain,
+// LDS round trips overlap: (1) table reads for every state, (2) state update,
+// wave ballot of the lanes that renormalise, word reads for every state,
 // (3) merge.  Branch-free: every lane reads a word (in bounds: a pointer is clamped to its
 // stream end and the region has kSlackWords of slack); only the lanes that
 // renormalise take it.  The word of lane p is the next unread one plus the
-// number of renormalising lanes below p (mbcnt of the ballot).  CAREFUL also
-// handles the payload switch (x -= L at step == lim, no reads from then on).
-// Returns the table words (decoded symbol in the top byte).
+// number of renormalising lanes below p (mbcnt of the ballot).  With two
+// states per lane (R = 128) the first states' words come first, then the
+// second states' (interleaving order j = s*128 + p).  CAREFUL also handles the
+// payload switch (x -= L at step == lim, no reads from then on).
+// Returns the table words (decoded symbol in the top byte) per state.
 template <int R, bool CAREFUL, int ILP, bool RING>
 __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
                                          const uint8_t* __restrict__ lds, uint32_t s,
-                                         bool upper_half, uint32_t (&sym)[ILP]) {
-  uint32_t x[ILP];
-  u32x2 e[ILP];
+                                         bool upper_half,
+                                         uint32_t (&sym)[ILP][states_per_lane(R)]) {
+  constexpr int NS = states_per_lane(R);
+  uint32_t x[ILP][NS];
+  u32x2 e[ILP][NS];
 #pragma unroll
-  for (int i = 0; i < ILP; ++i) {
-    x[i] = c[i].x;
-    if (CAREFUL) x[i] = (s == c[i].lim) ? x[i] - kL : x[i];
-    e[i] = lut[x[i] & (kSlots - 1)];
-  }
-  uint32_t xn[ILP], w[ILP];
-  bool need[ILP];
+  for (int i = 0; i < ILP; ++i)
 #pragma unroll
-  for (int i = 0; i < ILP; ++i) {
-    xn[i] = (e[i].x & 0xFFFFFFu) * (x[i] >> 12) + e[i].y;  // v_mad_u32_u24
-    need[i] = xn[i] < kL;
-    if (CAREFUL) need[i] = need[i] && (s < c[i].lim);
-    const uint64_t m = __builtin_amdgcn_ballot_w64(need[i]);
-    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-    uint32_t addr;
-    if (R == 64 && RING) {
-      addr = 2 * rank + (c[i].s0 + (c[i].p0 & (2 * kRingWords - 1)));
-      c[i].p0 += 2 * (uint32_t)__builtin_popcountll(m);
-    } else if (R == 64) {
-      addr = 2 * rank + min(c[i].p0, c[i].e0);
-      c[i].p0 += 2 * (uint32_t)__builtin_popcountll(m);
-    } else {
-      const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
-      const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
-      // upper-half lanes count the lower half's bits too: start them pl lower
-      const uint32_t b0 = min(c[i].p0, c[i].e0);
-      const uint32_t b1 = min(c[i].p1, c[i].e1) - 2 * pl;
-      addr = 2 * rank + (upper_half ? b1 : b0);
-      c[i].p0 += 2 * pl;
-      c[i].p1 += 2 * ph;
+    for (int h = 0; h < NS; ++h) {
+      x[i][h] = h ? c[i].x2 : c[i].x;
+      if (CAREFUL) x[i][h] = (s == c[i].lim) ? x[i][h] - kL : x[i][h];
+      e[i][h] = lut[x[i][h] & (kSlots - 1)];
     }
-    w[i] = *reinterpret_cast<const uint16_t*>(lds + addr);
-  }
+  uint32_t xn[ILP][NS], w[ILP][NS];
+  bool need[ILP][NS];
 #pragma unroll
   for (int i = 0; i < ILP; ++i) {
-    c[i].x = need[i] ? ((xn[i] << 16) | w[i]) : xn[i];
-    sym[i] = e[i].x;
+    uint32_t pos = c[i].p0;  // uniform
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+      xn[i][h] = (e[i][h].x & 0xFFFFFFu) * (x[i][h] >> 12) + e[i][h].y;  // v_mad_u32_u24
+      need[i][h] = xn[i][h] < kL;
+      if (CAREFUL) need[i][h] = need[i][h] && (s < c[i].lim);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(need[i][h]);
+      const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+      uint32_t addr;
+      if (R != 32 && RING) {
+        addr = 2 * rank + (c[i].s0 + (pos & (2 * kRingWords - 1)));
+        pos += 2 * (uint32_t)__builtin_popcountll(m);
+      } else if (R != 32) {
+        addr = 2 * rank + min(pos, c[i].e0);
+        pos += 2 * (uint32_t)__builtin_popcountll(m);
+      } else {
+        const uint32_t pl = (uint32_t)__builtin_popcount(mlo);
+        const uint32_t ph = (uint32_t)__builtin_popcount(mhi);
+        // upper-half lanes count the lower half's bits too: start them pl lower
+        const uint32_t b0 = min(c[i].p0, c[i].e0);
+        const uint32_t b1 = min(c[i].p1, c[i].e1) - 2 * pl;
+        addr = 2 * rank + (upper_half ? b1 : b0);
+        pos += 2 * pl;
+        c[i].p1 += 2 * ph;
+      }
+      w[i][h] = *reinterpret_cast<const uint16_t*>(lds + addr);
+    }
+    c[i].p0 = pos;
   }
+#pragma unroll
+  for (int i = 0; i < ILP; ++i)
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+      const uint32_t v = need[i][h] ? ((xn[i][h] << 16) | w[i][h]) : xn[i][h];
+      if (h) c[i].x2 = v; else c[i].x = v;
+      sym[i][h] = e[i][h].x;
+    }
 }
 
 // Integrity flags of the chain's tile(s) after the last step, per lane's tile:
@@ -217,9 +238,9 @@ template <int R, bool RING>
 __device__ __forceinline__ uint32_t final_flags(const Chain& c, uint32_t steps,
                                                 bool upper_half) {
   const uint32_t want = (c.lim == steps) ? kL : 0u;
-  const uint64_t bad = __builtin_amdgcn_ballot_w64(c.x != want);
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(c.x != want || (R == 128 && c.x2 != want));
   uint32_t f = 0;
-  const uint32_t half_bad = (R == 64) ? (bad != 0) : (upper_half ? (uint32_t)(bad >> 32)
+  const uint32_t half_bad = (R != 32) ? (bad != 0) : (upper_half ? (uint32_t)(bad >> 32)
                                                                  : (uint32_t)bad);
   if (half_bad) f |= 1u;
   const uint32_t p = (R == 32 && upper_half) ? c.p1 : c.p0;
@@ -239,46 +260,76 @@ constexpr int kPre = 16;
 
 struct Staged {
   uint32_t v[kPre];
-  const uint32_t* src;
+  const uint32_t* src;   // the tile's words (after its states)
+  const uint32_t* tile;  // the tile's stream (states first)
+  int32_t last;          // last dword index of the tile's stream
   uint32_t words4;
 };
 
-__device__ __forceinline__ void stage_issue(const Layer& L, uint32_t t, uint32_t sub_lane,
-                                            uint32_t sub_size, Staged& st) {
+// Locate tile t's stream (no word loads yet).
+__device__ __forceinline__ void stage_begin(const Layer& L, uint32_t t, Staged& st) {
   const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
   st.words4 = o1 - o0 - L.lanes;
-  st.src = L.streams + o0 + L.lanes;
-  // Every lane loads, without branches, so the vector-memory wait counts of
-  // the caller stay exact (a later wait for an earlier load does not have to
-  // drain these).  Positions past the stream re-read the tile's last dword
-  // (the states come first, so the tile always has one); stage_commit keeps
-  // only the words below words4.
-  const uint32_t* p = L.streams + o0;
-  const int32_t last = (int32_t)(o1 - o0) - 1;
+  st.tile = L.streams + o0;
+  st.src = st.tile + L.lanes;
+  st.last = (int32_t)(o1 - o0) - 1;
+}
+
+// Load dwords j0 <= j < j1 of every lane's share into registers.  Every lane
+// loads, without branches, so the vector-memory wait counts of the caller
+// stay exact (a later wait for an earlier load does not have to drain these).
+// Positions past the stream re-read the tile's last dword (the states come
+// first, so the tile always has one); commits keep only the words below words4.
+__device__ __forceinline__ void stage_load(Staged& st, uint32_t lanes, uint32_t sub_lane,
+                                           uint32_t sub_size, int j0, int j1) {
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const int32_t i = (int32_t)(L.lanes + sub_lane + j * sub_size);
-    st.v[j] = p[min(i, last)];
+  for (int j = j0; j < j1; ++j) {
+    const int32_t i = (int32_t)(lanes + sub_lane + j * sub_size);
+    st.v[j] = st.tile[min(i, st.last)];
+  }
+}
+
+__device__ __forceinline__ void stage_issue(const Layer& L, uint32_t t, uint32_t sub_lane,
+                                            uint32_t sub_size, Staged& st) {
+  stage_begin(L, t, st);
+  stage_load(st, L.lanes, sub_lane, sub_size, 0, kPre);
+}
+
+// Write staged dwords j0 <= j < j1 to LDS; REST also copies the dwords the
+// registers did not cover straight from global memory.
+__device__ __forceinline__ void stage_commit_part(const Staged& st, uint16_t* words,
+                                                  uint32_t start, uint32_t sub_lane,
+                                                  uint32_t sub_size, int j0, int j1, bool rest) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(words + start) + sub_lane;
+  const int32_t rem = (int32_t)st.words4 - (int32_t)sub_lane;
+#pragma unroll
+  for (int j = j0; j < j1; ++j)
+    if (rem > (int32_t)(j * sub_size)) dst[j * sub_size] = st.v[j];
+  if (rest) {
+    const uint32_t* src = st.src + sub_lane;
+    for (int32_t i = kPre * sub_size; i < rem; i += sub_size) dst[i] = src[i];
   }
 }
 
 // Returns the number of staged u16 words (including a possible pad word).
 __device__ __forceinline__ uint32_t stage_commit(const Staged& st, uint16_t* words, uint32_t start,
                                                  uint32_t sub_lane, uint32_t sub_size) {
-  uint32_t* dst = reinterpret_cast<uint32_t*>(words + start) + sub_lane;
-  const int32_t rem = (int32_t)st.words4 - (int32_t)sub_lane;
-#pragma unroll
-  for (int j = 0; j < kPre; ++j)
-    if (rem > (int32_t)(j * sub_size)) dst[j * sub_size] = st.v[j];
-  const uint32_t* src = st.src + sub_lane;
-  for (int32_t i = kPre * sub_size; i < rem; i += sub_size) dst[i] = src[i];
+  stage_commit_part(st, words, start, sub_lane, sub_size, 0, kPre, true);
   return 2 * st.words4;
 }
 
-// One tile's ring (R = 64): its stream, chunk count, committed chunks and the
-// next chunk in flight (4 dwords per lane: dwords lane + 64 * i of the chunk).
+// A fragment reads fewer words than the first half of the staged registers
+// hold (8 steps x at most one word per state: 512 words for R = 64, 1024 for
+// R = 128, per tile 256 for R = 32, against kPre/2 * sub_size dwords), so the
+// decode can start once that half is in LDS and the rest is written after
+// the first fragment.
+constexpr int kPreHalf = kPre / 2;
+
+// One tile's ring: its stream, chunk count, committed chunks and the next
+// chunk in flight (4 dwords per lane: dwords lane + 64 * i of the chunk).
 struct Ring {
   const uint32_t* tile;  // the tile's stream (states first)
+  uint32_t hdr;          // state dwords before the words (R)
   int32_t last;          // last dword index of the tile's stream
   uint32_t words4;       // uniform: stream dwords after the states
   uint32_t nchunks;      // uniform
@@ -292,7 +343,7 @@ __device__ __forceinline__ void ring_load(const Ring& r, uint32_t j, uint32_t la
                                           uint32_t (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int32_t d = (int32_t)(64 + j * kChunkDwords + lane + 64 * i);
+    const int32_t d = (int32_t)(r.hdr + j * kChunkDwords + lane + 64 * i);
     v[i] = r.tile[min(d, r.last)];
   }
 }
@@ -302,8 +353,9 @@ __device__ __forceinline__ void ring_issue(const Layer& L, uint32_t t, uint32_t 
                                            uint32_t (&c0)[4]) {
   const uint32_t o0 = L.index[t], o1 = L.index[t + 1];
   r.tile = L.streams + o0;
+  r.hdr = L.lanes;
   r.last = (int32_t)(o1 - o0) - 1;
-  r.words4 = o1 - o0 - 64;
+  r.words4 = o1 - o0 - L.lanes;
   r.nchunks = (r.words4 + kChunkDwords - 1) / kChunkDwords;
   r.cc = 0;
   ring_load(r, 0, lane, c0);
@@ -322,7 +374,7 @@ __device__ __forceinline__ void ring_write(uint8_t* lds, uint32_t base, uint32_t
     reinterpret_cast<uint32_t*>(lds + base)[2 * kChunkDwords + lane] = v[0];
 }
 
-// Chunk 0 to the ring and the chain's word pointers (R = 64).
+// Chunk 0 to the ring and the chain's word pointers.
 __device__ __forceinline__ void ring_start(Ring& r, Chain& c, uint8_t* lds, uint32_t base,
                                            uint32_t lane, const uint32_t (&c0)[4]) {
   ring_write(lds, base, 0, lane, c0);
@@ -333,9 +385,9 @@ __device__ __forceinline__ void ring_start(Ring& r, Chain& c, uint8_t* lds, uint
   c.p1 = 0; c.s1 = base; c.e1 = c.e0;
 }
 
-// Before a fragment whose first word is p (2 * words consumed): make sure the
-// chunk holding the furthest word the fragment can read is in the ring.  At
-// most one chunk per fragment is needed.
+// Before a group of steps whose first word is p (2 * words consumed): make
+// sure the chunk holding the furthest word the group can read is in the ring.
+// At most one chunk per group is needed.
 __device__ __forceinline__ void ring_advance(Ring& r, uint8_t* lds, uint32_t base, uint32_t p,
                                              uint32_t lane) {
   const uint32_t need = ((p >> 1) + kChunkWords - 1) / kChunkWords;

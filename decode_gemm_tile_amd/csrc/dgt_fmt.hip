@@ -41,17 +41,20 @@ int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t th
 
 }  // namespace
 
-// The ring staging exists for R = 64 only.
+// Ring staging exists for R = 64 and 128 (one tile per chain).
 template <>
 int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt, bool mix,
                           bool ring, uint32_t grid, uint32_t threads, uint32_t lds,
                           hipStream_t st) {
-  if (lanes == 64 && fn == 8)
-    return ring ? fused_r<64, 8, true>(a, mt, mix, grid, threads, lds, st)
-                : fused_r<64, 8, false>(a, mt, mix, grid, threads, lds, st);
-  if (lanes == 64 && fn == 16)
-    return ring ? fused_r<64, 16, true>(a, mt, mix, grid, threads, lds, st)
-                : fused_r<64, 16, false>(a, mt, mix, grid, threads, lds, st);
+#define DGT_FUSED_CASE(RR, FNV)                                                      \
+  if (lanes == RR && fn == FNV)                                                      \
+    return ring ? fused_r<RR, FNV, true>(a, mt, mix, grid, threads, lds, st)         \
+                : fused_r<RR, FNV, false>(a, mt, mix, grid, threads, lds, st);
+  DGT_FUSED_CASE(64, 8)
+  DGT_FUSED_CASE(64, 16)
+  DGT_FUSED_CASE(128, 8)
+  DGT_FUSED_CASE(128, 16)
+#undef DGT_FUSED_CASE
   if (ring) return DGT_E_UNSUPPORTED;
   if (lanes == 32 && fn == 8) return fused_r<32, 8, false>(a, mt, mix, grid, threads, lds, st);
   if (lanes == 32 && fn == 16) return fused_r<32, 16, false>(a, mt, mix, grid, threads, lds, st);
@@ -59,19 +62,23 @@ int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32
 }
 
 template <>
-int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t fn, bool ring, uint32_t grid,
-                             uint32_t lds, hipStream_t st) {
-#define DGT_XM_CASE(FNV, RG)                                                    \
-  if (fn == FNV && ring == RG) {                                                \
-    auto k = k_fused_xm<DGT_FMT, FNV, RG>;                                      \
+int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring,
+                             uint32_t grid, uint32_t lds, hipStream_t st) {
+#define DGT_XM_CASE(RR, FNV, RG)                                                \
+  if (lanes == RR && fn == FNV && ring == RG) {                                 \
+    auto k = k_fused_xm<DGT_FMT, RR, FNV, RG>;                                  \
     if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(FNV)), lds, st, x);    \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
   }
-  DGT_XM_CASE(8, false)
-  DGT_XM_CASE(8, true)
-  DGT_XM_CASE(16, false)
-  DGT_XM_CASE(16, true)
+  DGT_XM_CASE(64, 8, false)
+  DGT_XM_CASE(64, 8, true)
+  DGT_XM_CASE(64, 16, false)
+  DGT_XM_CASE(64, 16, true)
+  DGT_XM_CASE(128, 8, false)
+  DGT_XM_CASE(128, 8, true)
+  DGT_XM_CASE(128, 16, false)
+  DGT_XM_CASE(128, 16, true)
 #undef DGT_XM_CASE
   return DGT_E_UNSUPPORTED;
 }
@@ -90,6 +97,10 @@ int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bo
   DGT_DECODE_CASE(64, 2, false)
   DGT_DECODE_CASE(64, 1, true)
   DGT_DECODE_CASE(64, 2, true)
+  DGT_DECODE_CASE(128, 1, false)
+  DGT_DECODE_CASE(128, 2, false)
+  DGT_DECODE_CASE(128, 1, true)
+  DGT_DECODE_CASE(128, 2, true)
   DGT_DECODE_CASE(32, 1, false)
   DGT_DECODE_CASE(32, 2, false)
 #undef DGT_DECODE_CASE

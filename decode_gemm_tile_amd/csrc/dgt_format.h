@@ -39,8 +39,16 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Tile-local position of symbol j = s*R + p (s = epl*g + e; g = fk*Fn + fn),
 // epl symbols per lane per fragment; col counts symbols (weights, or pairs).
+// R = 128 (two states per wave lane): states p < 64 order the top tile_n/2
+// rows and states 64 + p the bottom ones, each half as an R = 64 tile.
 inline void symbol_position(uint32_t j, uint32_t tile_n, uint32_t lanes, uint32_t epl,
                             uint32_t* row, uint32_t* col) {
+  if (lanes == 128) {
+    const uint32_t s = j / 128, p = j % 128;
+    symbol_position(s * 64 + (p & 63), tile_n / 2, 64, epl, row, col);
+    *row += (p >> 6) * (tile_n / 2);
+    return;
+  }
   const uint32_t s = j / lanes, p = j % lanes;
   const uint32_t g = s / epl, e = s % epl;
   const uint32_t fn_count = tile_n / 16;
@@ -52,6 +60,12 @@ inline void symbol_position(uint32_t j, uint32_t tile_n, uint32_t lanes, uint32_
 // Tile-local position of raw byte q = g*8R + p*8 + e (lane-major).
 inline void raw_position(uint32_t q, uint32_t tile_n, uint32_t lanes, uint32_t* row,
                          uint32_t* col) {
+  if (lanes == 128) {
+    const uint32_t g = q / 1024, p = (q % 1024) >> 3;
+    raw_position(g * 512 + (p & 63) * 8 + (q & 7), tile_n / 2, 64, row, col);
+    *row += (p >> 6) * (tile_n / 2);
+    return;
+  }
   const uint32_t g = q / (8 * lanes), rem = q % (8 * lanes);
   const uint32_t p = rem >> 3, e = rem & 7;
   const uint32_t fn_count = tile_n / 16;

@@ -36,6 +36,11 @@ bool geometry_ok(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tn, uint32_t tk,
                  uint32_t lanes) {
   if (!n || !k || !tn || !tk || !lanes) return false;
   if (n % tn || k % tk) return false;
+  if (lanes == 128) {  // two R = 64 halves of tn/2 rows
+    if (tn % 32) return false;
+    tn /= 2;
+    lanes = 64;
+  }
   if (lanes % 16 || tn % 16) return false;
   if (tk % (lanes / 2)) return false;  // whole fragments of R/2 weights
   const uint32_t wps = dgt::weights_per_symbol(fmt);

@@ -95,47 +95,59 @@ __device__ __forceinline__ uint32_t pack_hi_bytes(uint32_t e1, uint32_t e0) {
   return __builtin_amdgcn_perm(e1, e0, 0x0c0c0703u);  // [s0, s1, 0, 0]
 }
 
+// The B operand is built in two stages so that a fragment in flight holds 4
+// registers per state rather than 8: pair_b reduces two consecutive decoded
+// symbols (LUT words, symbol in the top byte) to one register as soon as both
+// exist; finish_b adds raw bytes or scales and yields the operand.  Formats
+// whose symbol already codes two weights (int4 pairs) keep one symbol per
+// register and skip pair_b.
 template <int FMT>
-__device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()], u32x2 raw,
-                                      float sc, float nsc8) {
+__device__ __forceinline__ uint32_t pair_b(uint32_t e0, uint32_t e1) {
+  if constexpr (FMT == BF16 || FMT == INT4) {
+    return pack_hi_bytes(e1, e0);  // [s0, s1, 0, 0]
+  } else if constexpr (FMT == BF16E) {
+    // exponents into bits 14..7 and 30..23 of the pair
+    return (e0 >> 17) | ((e1 >> 1) & 0x7F800000u);
+  } else if constexpr (FMT == INT8) {
+    const uint32_t f0 = __float_as_uint((float)((int32_t)e0 >> 24));
+    const uint32_t f1 = __float_as_uint((float)((int32_t)e1 >> 24));
+    return __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // two bf16 (exact integers)
+  } else if constexpr (FMT == FP8) {
+    return __builtin_amdgcn_perm(e1, e0, 0x07030c0cu);  // e4m3 bytes in the high half
+  } else {
+    return e0;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ BOp finish_b(const uint32_t (&q)[4], u32x2 raw, float sc,
+                                        float nsc8) {
   BOp b;
   if constexpr (FMT == BF16) {
-    const uint32_t p01 = pack_hi_bytes(e[1], e[0]);
-    const uint32_t p23 = pack_hi_bytes(e[3], e[2]);
-    const uint32_t p45 = pack_hi_bytes(e[5], e[4]);
-    const uint32_t p67 = pack_hi_bytes(e[7], e[6]);
-    b.v.x = __builtin_amdgcn_perm(p01, raw.x, 0x05010400u);
-    b.v.y = __builtin_amdgcn_perm(p23, raw.x, 0x05030402u);
-    b.v.z = __builtin_amdgcn_perm(p45, raw.y, 0x05010400u);
-    b.v.w = __builtin_amdgcn_perm(p67, raw.y, 0x05030402u);
+    b.v.x = __builtin_amdgcn_perm(q[0], raw.x, 0x05010400u);
+    b.v.y = __builtin_amdgcn_perm(q[1], raw.x, 0x05030402u);
+    b.v.z = __builtin_amdgcn_perm(q[2], raw.y, 0x05010400u);
+    b.v.w = __builtin_amdgcn_perm(q[3], raw.y, 0x05030402u);
   } else if constexpr (FMT == BF16E) {
-    // weights 2i, 2i+1: exponents from the symbols (top byte of the LUT
-    // words) into bits 14..7 and 30..23; sign and mantissa from the raw
-    // bytes, each copied into both bytes of its half by the byte permute
+    // sign and mantissa from the raw bytes, each copied into both bytes of
+    // its half by the byte permute, exponents from the pair
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t ex = (e[2 * i] >> 17) | ((e[2 * i + 1] >> 1) & 0x7F800000u);
       const uint32_t r = i < 2 ? raw.x : raw.y;
-      const uint32_t q = __builtin_amdgcn_perm(0u, r, (i & 1) ? 0x03030202u : 0x01010000u);
-      o[i] = (q & 0x807F807Fu) | (ex & ~0x807F807Fu);
+      const uint32_t sm = __builtin_amdgcn_perm(0u, r, (i & 1) ? 0x03030202u : 0x01010000u);
+      o[i] = (sm & 0x807F807Fu) | (q[i] & ~0x807F807Fu);
     }
     b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
   } else if constexpr (FMT == INT8) {
-    uint32_t f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = __float_as_uint((float)((int32_t)e[i] >> 24));
-    b.v.x = __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
-    b.v.y = __builtin_amdgcn_perm(f[3], f[2], 0x07060302u);
-    b.v.z = __builtin_amdgcn_perm(f[5], f[4], 0x07060302u);
-    b.v.w = __builtin_amdgcn_perm(f[7], f[6], 0x07060302u);
+    b.v.x = q[0]; b.v.y = q[1]; b.v.z = q[2]; b.v.w = q[3];
   } else if constexpr (FMT == INT4) {
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       floatx2 w;
-      w.x = __builtin_fmaf((float)(e[2 * i] >> 24), sc, nsc8);
-      w.y = __builtin_fmaf((float)(e[2 * i + 1] >> 24), sc, nsc8);
+      w.x = __builtin_fmaf((float)(q[i] & 0xFFu), sc, nsc8);
+      w.y = __builtin_fmaf((float)((q[i] >> 8) & 0xFFu), sc, nsc8);
       const bf16x2 h = __builtin_convertvector(w, bf16x2);
       o[i] = __builtin_bit_cast(uint32_t, h);
     }
@@ -145,8 +157,8 @@ __device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       floatx2 w;
-      w.x = __builtin_fmaf((float)((e[i] >> 24) & 15u), sc, nsc8);
-      w.y = __builtin_fmaf((float)(e[i] >> 28), sc, nsc8);
+      w.x = __builtin_fmaf((float)((q[i] >> 24) & 15u), sc, nsc8);
+      w.y = __builtin_fmaf((float)(q[i] >> 28), sc, nsc8);
       const bf16x2 h = __builtin_convertvector(w, bf16x2);
       o[i] = __builtin_bit_cast(uint32_t, h);
     }
@@ -155,13 +167,37 @@ __device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()]
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t pair = __builtin_amdgcn_perm(e[2 * i + 1], e[2 * i], 0x07030c0cu);
-      const floatx2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)pair, true);
+      const floatx2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[i], true);
       o[i] = __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
     }
     b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
   }
   return b;
+}
+
+// Collects a fragment's decoded symbols step by step into the 4 registers
+// finish_b takes.
+template <int FMT>
+struct FragAcc {
+  uint32_t q[4];
+  uint32_t prev;
+  __device__ __forceinline__ void put(int i, uint32_t e) {
+    if constexpr (steps_per_frag<FMT>() == 8) {
+      if (i & 1) q[i >> 1] = pair_b<FMT>(prev, e);
+      else prev = e;
+    } else {
+      q[i] = e;
+    }
+  }
+};
+
+template <int FMT>
+__device__ __forceinline__ BOp make_b(const uint32_t (&e)[steps_per_frag<FMT>()], u32x2 raw,
+                                      float sc, float nsc8) {
+  FragAcc<FMT> f;
+#pragma unroll
+  for (int i = 0; i < steps_per_frag<FMT>(); ++i) f.put(i, e[i]);
+  return finish_b<FMT>(f.q, raw, sc, nsc8);
 }
 
 // All formats multiply on the bf16 matrix cores with fp32 accumulation.  The
@@ -287,23 +323,43 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
 // Workgroup size cap per variant: kernels whose registers fit in 128 VGPRs run
 // up to 16 waves per workgroup; the others (more row bands or row blocks of
 // accumulators) stay at 8 waves with up to 256 VGPRs.
+template <bool V>
+struct BoolC { static constexpr bool value = V; };
+template <int V>
+struct IntC { static constexpr int value = V; };
+// f(IntC<I>{}) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __host__ __device__ constexpr uint32_t fused_max_threads(int R, int FN, int MT, int ILP) {
-  return (MT == 1 && FN <= 8 && (R == 64 || ILP == 1)) ? 1024u : 512u;
+  return (MT == 1 && FN <= 8 && (R != 32 || ILP == 1)) ? 1024u : 512u;
 }
 __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
   return (MT == 1 && FN <= 8) ? 1024u : 512u;
 }
 
-// Decode and multiply ILP chains (ch[0..ILP)) of one strip into acc.
-template <int FMT, int R, int FN, int MT, int ILP, bool RING>
+// Decode and multiply ILP chains (ch[0..ILP)) of one strip into acc.  With
+// two states per lane (R = 128) a fragment step yields the same 16x32 block
+// position in both row halves of the tile: two products that share X.
+// after_first() runs once the first fragment has been decoded (it writes the
+// rest of whole-staged streams to LDS).
+template <int FMT, int R, int FN, int MT, int ILP, bool RING, typename AfterFirst>
 __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut, uint8_t* smem,
                                              Chain (&chs)[2], Ring (&rgs)[2],
                                              const uint32_t (&tile_lane)[2],
                                              const uint32_t (&k0_lane)[2], uint32_t strip,
-                                             floatx4 (&acc)[FN][MT]) {
+                                             floatx4 (&acc)[FN][MT], AfterFirst&& after_first) {
   const Layer& L = a.L;
-  constexpr uint32_t FW = R / 2;  // fragment width (columns)
+  constexpr int NS = states_per_lane(R);
+  constexpr uint32_t FW = (R == 128 ? 64 : R) / 2;  // fragment width (columns)
+  constexpr int FNH = FN / NS;                        // row bands per state
   constexpr int SPF = steps_per_frag<FMT>();
+  constexpr int ADV = ring_group_steps(R);
   Chain (&ch)[ILP] = *reinterpret_cast<Chain(*)[ILP]>(&chs[0]);
   Ring (&rg)[ILP] = *reinterpret_cast<Ring(*)[ILP]>(&rgs[0]);
   const uint32_t lane = lane_id();
@@ -325,30 +381,42 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
     if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
   }
   const uint32_t FK = L.tile_k / FW;
-  const uint32_t G = FK * FN;
+  const uint32_t G = FK * FNH;
   const uint32_t kgroups = L.k / 128;
-  // operands that come from global memory are fetched one fragment (raw
-  // bytes, scales) or one column block (X) ahead of their use
-  auto load_raw = [&](int c, uint32_t g) -> u32x2 {
-    const uint8_t* rp = L.raw + (size_t)tile_lane[c] * L.tile_n * L.tile_k +
-                        (size_t)g * 8 * R + (lane % R) * 8;
-    return *reinterpret_cast<const u32x2*>(rp);
-  };
-  auto load_scale = [&](int c, uint32_t g) -> float {
-    const uint32_t fkg = g / FN, fng = g % FN;
-    const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
-    const uint16_t sb = a.scales[(size_t)row * kgroups + (k0_lane[c] + fkg * FW) / 128];
-    return __uint_as_float((uint32_t)sb << 16);
-  };
-  u32x2 raw_n[ILP];
-  float sc_n[ILP];
+  // one tile per chain: the tile and its first column are wave-uniform, so
+  // only the lane's offsets stay in vector registers
+  uint32_t tl[ILP], kb[ILP];
+  const uint32_t koff = (R == 32) ? 0u : 8 * (lane >> 4);
 #pragma unroll
   for (int c = 0; c < ILP; ++c) {
-    raw_n[c] = u32x2{0u, 0u};
-    sc_n[c] = 0.f;
-    if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, 0);
-    if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
+    tl[c] = (R == 32) ? tile_lane[c] : uniform(tile_lane[c]);
+    kb[c] = (R == 32) ? k0_lane[c] : uniform(k0_lane[c] - koff);
   }
+  // operands that come from global memory are fetched one fragment (raw
+  // bytes, scales) or one column block (X) ahead of their use
+  auto load_raw = [&](int c, uint32_t g, int h) __attribute__((always_inline)) -> u32x2 {
+    const uint32_t p = (R == 128) ? 64 * h + lane : lane % R;
+    const uint8_t* rp = L.raw + (size_t)tl[c] * L.tile_n * L.tile_k +
+                        (size_t)g * 8 * R + p * 8;
+    return *reinterpret_cast<const u32x2*>(rp);
+  };
+  auto load_scale = [&](int c, uint32_t g, int h) __attribute__((always_inline)) -> float {
+    const uint32_t fkg = g / FNH, fng = g % FNH;
+    const uint32_t row = strip * L.tile_n + (h * FNH + fng) * 16 + (lane & 15);
+    const uint16_t sb = a.scales[(size_t)row * kgroups + (kb[c] + koff + fkg * FW) / 128];
+    return __uint_as_float((uint32_t)sb << 16);
+  };
+  u32x2 raw_n[ILP][NS];
+  float sc_n[ILP][NS];
+#pragma unroll
+  for (int c = 0; c < ILP; ++c)
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+      raw_n[c][h] = u32x2{0u, 0u};
+      sc_n[c][h] = 0.f;
+      if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, 0, h);
+      if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, 0, h);
+    }
   constexpr bool kPrefetchA = (MT == 1);
   u32x4 A_n[ILP][MT];
   if constexpr (kPrefetchA) {
@@ -356,80 +424,119 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
     for (int c = 0; c < ILP; ++c)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c]);
+        A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + koff);
   }
-  for (uint32_t fk = 0; fk < FK; ++fk) {
-    u32x4 A[ILP][MT];
+  // A operands of column block fk (X is fetched one block ahead when MT == 1)
+  u32x4 A[ILP][MT];
+  auto take_a = [&](uint32_t fk) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (kPrefetchA) {
+        if constexpr (kPrefetchA)
           A[c][mt] = A_n[c][mt];
-          if (fk + 1 < FK)
-            A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + (fk + 1) * FW);
-        } else {
-          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), k0_lane[c] + fk * FW);
-        }
+        else
+          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + fk * FW + koff);
       }
+  };
+  auto prefetch_a = [&](uint32_t fk) __attribute__((always_inline)) {
+    if constexpr (kPrefetchA) {
+      if (fk + 1 < FK) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const uint32_t g = fk * FN + fn;
-      const uint32_t s0 = g * SPF;
-      const uint32_t gn = min(g + 1, G - 1);
-      u32x2 raw[ILP];
-      float sc[ILP], nsc8[ILP];
+        for (int c = 0; c < ILP; ++c)
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) {
-        raw[c] = raw_n[c];
-        sc[c] = sc_n[c];
-        nsc8[c] = -8.f * sc[c];
-        if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
-        if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
-      }
-      if constexpr (RING) {
-#pragma unroll
-        for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
-      }
-      uint32_t e[ILP][SPF];
-      // payload steps (at most the last kPayloadMax) fall in the last fragments
-      if (fn < FN - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min) {
-#pragma unroll
-        for (int i = 0; i < SPF; ++i) {
-          uint32_t sy[ILP];
-          step_all<R, false, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
-#pragma unroll
-          for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < SPF; ++i) {
-          uint32_t sy[ILP];
-          step_all<R, true, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
-#pragma unroll
-          for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < ILP; ++c) {
-        const BOp b = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = mfma<FMT>(A[c][mt], b, acc[fn][mt]);
+          for (int mt = 0; mt < MT; ++mt)
+            A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + (fk + 1) * FW + koff);
       }
     }
+  };
+  // Loads for later fragments are issued after the fragment's last ring
+  // advance: a chunk written to the ring waits for the loads issued before it,
+  // and these are then one fragment old instead of just issued.
+  constexpr int kPrefetchStep = RING ? ((SPF - 1) / ADV) * ADV : 0;
+  // one fragment: row band fn of every state, column block fk
+  auto frag = [&](uint32_t fk, auto fnc) __attribute__((always_inline)) {
+    constexpr int fn = decltype(fnc)::value;
+    const uint32_t g = fk * FNH + fn;
+    const uint32_t s0 = g * SPF;
+    const uint32_t gn = min(g + 1, G - 1);
+    u32x2 raw[ILP][NS];
+    float sc[ILP][NS], nsc8[ILP][NS];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+      for (int h = 0; h < NS; ++h) {
+        raw[c][h] = raw_n[c][h];
+        sc[c][h] = sc_n[c][h];
+        nsc8[c][h] = -8.f * sc[c][h];
+      }
+    auto prefetch = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int h = 0; h < NS; ++h) {
+          if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, gn, h);
+          if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, gn, h);
+        }
+      if (fn == 0) prefetch_a(fk);
+    };
+    FragAcc<FMT> e[ILP][NS];
+    auto steps = [&](auto careful) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < SPF; ++i) {
+        if constexpr (RING) {
+          if (i % ADV == 0) {
+#pragma unroll
+            for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+          }
+        }
+        if (i == kPrefetchStep) prefetch();
+        uint32_t sy[ILP][NS];
+        step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
+#pragma unroll
+        for (int c = 0; c < ILP; ++c)
+#pragma unroll
+          for (int h = 0; h < NS; ++h) e[c][h].put(i, sy[c][h]);
+      }
+    };
+    // payload steps (at most the last kPayloadMax) fall in the last fragments
+    if (fn < FNH - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min)
+      steps(BoolC<false>{});
+    else
+      steps(BoolC<true>{});
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+      for (int h = 0; h < NS; ++h) {
+        const BOp b = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], nsc8[c][h]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[h * FNH + fn][mt] = mfma<FMT>(A[c][mt], b, acc[h * FNH + fn][mt]);
+      }
+  };
+  // The first fragment runs ahead of the loop, so that whatever after_first()
+  // consumes is dead inside the loop (whose copy of it skips block 0).
+  take_a(0);
+  frag(0u, IntC<0>{});
+  after_first();
+  for (uint32_t fk = 0; fk < FK; ++fk) {
+    if (fk > 0) take_a(fk);
+    static_for<0, FNH>([&](auto fnc) __attribute__((always_inline)) {
+      if (decltype(fnc)::value > 0 || fk > 0) frag(fk, fnc);
+    });
   }
   if (a.status) {
     const uint32_t half_lane = lane & 31;
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t f = final_flags<R, RING>(ch[c], L.steps, upper);
-      if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+      if (R != 32 ? lane == 0 : half_lane == 0) a.status[tl[c]] = (int32_t)f;
     }
   }
 }
 
-// RING (R = 64 only): stream the tile words through a two-chunk ring instead
-// of staging them whole (any stream length; less LDS per chain).
+// RING (R = 64 or 128): stream the tile words through a two-chunk ring
+// instead of staging them whole (any stream length; less LDS per chain).
 template <int FMT, int R, int FN, int MT, bool MIX, bool RING>
 __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_fused(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -437,7 +544,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
   uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
   const Layer& L = a.L;
-  constexpr uint32_t TPC = 64 / R;  // tiles per chain
+  constexpr uint32_t TPC = R == 32 ? 2 : 1;  // tiles per chain
 
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -456,14 +563,17 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   Chain ch[2];
   uint32_t tile_lane[2] = {0u, 0u};
   uint32_t k0_lane[2] = {0u, 0u};
-  Staged stg[2];   // R = 32: whole streams
-  Ring rg[2];      // R = 64: chunk 0 (c0) now, later chunks through the ring
+  Staged stg[2];   // whole streams
+  Ring rg[2];      // ring: chunk 0 (c0) now, later chunks through the ring
   uint32_t c0[2][4];
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
+  const uint32_t sub_lane = R != 32 ? lane : half_lane, sub_size = R != 32 ? 64u : 32u;
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
   // 3) write the first words to LDS.  Both chain slots always load (a missing
   // second chain repeats the first) so that every wave has the same loads in
-  // flight and the LUT build waits for the table alone.
+  // flight and the LUT build waits for the table alone.  Whole streams load
+  // in two halves, the first halves of both chains first: decoding starts
+  // once they are in LDS and the second halves follow after one fragment.
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const uint32_t cc = (c < (int)nch) ? (uint32_t)c : 0u;
@@ -473,10 +583,17 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
-      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
+      stage_begin(L, t_l, stg[c]);
     ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
+    ch[c].x2 = (R == 128) ? L.streams[L.index[t_l] + 64 + lane] : 0u;
     const uint32_t kt_l = kt_first + cc * TPC + ((R == 32 && upper) ? 1u : 0u);
     k0_lane[c] = kt_l * L.tile_k + 8 * ((lane % R) >> 4);
+  }
+  if constexpr (!RING) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) stage_load(stg[c], L.lanes, sub_lane, sub_size, 0, kPreHalf);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) stage_load(stg[c], L.lanes, sub_lane, sub_size, kPreHalf, kPre);
   }
   build_lut(fq, L.alphabet, lut, cum);
   // the payload counts are read after the LUT build: a wait for them then
@@ -485,6 +602,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   for (int c = 0; c < 2; ++c)
     if (c < (int)nch) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
   __syncthreads();  // LUT complete; each wave's staged streams are private to it
+  uint32_t cstart[2] = {0u, 0u};  // this lane's tile region (u16 words)
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c < (int)nch) {
@@ -493,8 +611,9 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
         ring_start(rg[c], ch[c], smem, kLutBytes + kCumBytes + 2 * ra, lane, c0[c]);
       } else {
         const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
-        const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
-                                           R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
+        cstart[c] = (R == 32 && upper) ? rb : ra;
+        stage_commit_part(stg[c], words, cstart[c], sub_lane, sub_size, 0, kPreHalf, false);
+        const uint32_t mine = 2 * stg[c].words4;
         const uint32_t na = uniform(mine);
         const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
         const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
@@ -503,6 +622,14 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
       }
     }
   }
+  auto commit_rest = [&]() __attribute__((always_inline)) {
+    if constexpr (!RING) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        if (c < (int)nch)
+          stage_commit_part(stg[c], words, cstart[c], sub_lane, sub_size, kPreHalf, kPre, true);
+    }
+  };
 
   floatx4 acc[FN][MT];
 #pragma unroll
@@ -511,12 +638,15 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MIX) {
     if (nch == 2)
-      fused_chains<FMT, R, FN, MT, 2, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 2, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc,
+                                            commit_rest);
     else if (nch == 1)
-      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc,
+                                            commit_rest);
   } else {
     if (nch == 1)
-      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc);
+      fused_chains<FMT, R, FN, MT, 1, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc,
+                                            commit_rest);
   }
   float out_scale = 1.f;
   if constexpr (FMT == FP8)
@@ -540,8 +670,6 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
 // tile_n 256: 8 waves x 32 rows).  A workgroup runs bpw consecutive batches;
 // each wave owns distinct rows, so accumulators go straight to Y (or to the
 // strip's workspace slot) when the strip changes, with no LDS reduction.
-template <bool V>
-struct BoolC { static constexpr bool value = V; };
 
 struct XmArgs {
   GemmArgs g;
@@ -569,14 +697,14 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t M = a.m, TN = FN * 16, wg = blockIdx.x;
   const uint32_t f = strip_first_wg(strip, x.bps, x.bpw), l = strip_last_wg(strip, x.bps, x.bpw);
-  auto store_y = [&](int fn, int mt, floatx4 v) {
+  auto store_y = [&](int fn, int mt, floatx4 v) __attribute__((always_inline)) {
     const uint32_t col = strip * TN + fn * 16 + (lane & 15);
     const uint32_t m0 = (wave * MTW + mt) * 16 + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (m0 + i < M) a.y[(size_t)(m0 + i) * a.y_row + col] = v[i] * out_scale;
   };
-  auto pair_ptr = [&](uint32_t slot, int fn, int mt, int h) {
+  auto pair_ptr = [&](uint32_t slot, int fn, int mt, int h) __attribute__((always_inline)) {
     return reinterpret_cast<uint64_t*>(a.part) + ((size_t)strip * a.slots + slot) * kSlotPairs +
            ((((wave * MTW + mt) * FN + fn) * 2 + h) * 64 + lane);
   };
@@ -637,12 +765,16 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
     __hip_atomic_store(&a.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// R = 64 lanes (one tile per chain) and tile_k = 64 only.
-template <int FMT, int FN, bool RING>
+// R = 64 or 128 (one tile per chain) and tile_k = 64 only.  With two states
+// per lane a wave publishes two operands per fragment (the tile's two row
+// halves at the same k), multiplied into the two halves' accumulators.
+template <int FMT, int R, int FN, bool RING>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
-  constexpr uint32_t R = 64, FW = 32, TK = 64, FK = TK / FW, G = FK * FN;
+  constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
+  constexpr uint32_t FW = 32, TK = 64, FK = TK / FW, G = FK * FNH;
   constexpr int SPF = steps_per_frag<FMT>();
+  constexpr int ADV = ring_group_steps(R);
   extern __shared__ __align__(16) uint8_t smem[];
   const GemmArgs& a = x.g;
   const Layer& L = a.L;
@@ -682,6 +814,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       else
         stage_issue(L, tj[c], lane, 64u, stg[c]);
       ch[c].x = L.streams[L.index[tj[c]] + lane];
+      ch[c].x2 = (R == 128) ? L.streams[L.index[tj[c]] + 64 + lane] : 0u;
     }
     if (b == b0) build_lut(fq, L.alphabet, lut, cum);
 #pragma unroll
@@ -704,26 +837,29 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       }
       lim_min = min(lim_min, uniform(ch[c].lim));
     }
-    auto load_raw = [&](int c, uint32_t g) -> u32x2 {
-      const uint8_t* rp = L.raw + (size_t)tj[c] * FN * 16 * TK + (size_t)g * 8 * R + lane * 8;
+    auto load_raw = [&](int c, uint32_t g, int h) __attribute__((always_inline)) -> u32x2 {
+      const uint8_t* rp = L.raw + (size_t)tj[c] * FN * 16 * TK + (size_t)g * 8 * R +
+                          (64 * h + lane) * 8;
       return *reinterpret_cast<const u32x2*>(rp);
     };
-    auto load_scale = [&](int c, uint32_t g) -> float {
-      const uint32_t fkg = g / FN, fng = g % FN;
-      const uint32_t row = strip * L.tile_n + fng * 16 + (lane & 15);
+    auto load_scale = [&](int c, uint32_t g, int h) __attribute__((always_inline)) -> float {
+      const uint32_t fkg = g / FNH, fng = g % FNH;
+      const uint32_t row = strip * L.tile_n + (h * FNH + fng) * 16 + (lane & 15);
       const uint32_t k0 = (kt0 + c * NW + wave) * TK + 8 * (lane >> 4) + fkg * FW;
       const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
       return __uint_as_float((uint32_t)sb << 16);
     };
-    u32x2 raw_n[ILP];
-    float sc_n[ILP];
+    u32x2 raw_n[ILP][NS];
+    float sc_n[ILP][NS];
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      raw_n[c] = u32x2{0u, 0u};
-      sc_n[c] = 0.f;
-      if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, 0);
-      if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, 0);
-    }
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+      for (int h = 0; h < NS; ++h) {
+        raw_n[c][h] = u32x2{0u, 0u};
+        sc_n[c][h] = 0.f;
+        if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, 0, h);
+        if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, 0, h);
+      }
     // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
     const uint8_t* xp[MTW];
 #pragma unroll
@@ -743,64 +879,88 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
             A[j][mt] = *reinterpret_cast<const u32x4*>(xp[mt] + fk * FW * 2 + j * TK * 2);
       }
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const uint32_t g = fk * FN + fn;
+      for (int fn = 0; fn < FNH; ++fn) {
+        const uint32_t g = fk * FNH + fn;
         const uint32_t s0 = g * SPF;
         const uint32_t gn = min(g + 1, G - 1);
-        u32x2 raw[ILP];
-        float sc[ILP], nsc8[ILP];
+        u32x2 raw[ILP][NS];
+        float sc[ILP][NS], nsc8[ILP][NS];
 #pragma unroll
-        for (int c = 0; c < ILP; ++c) {
-          raw[c] = raw_n[c];
-          sc[c] = sc_n[c];
-          nsc8[c] = -8.f * sc[c];
-          if constexpr (has_raw_bytes<FMT>()) raw_n[c] = load_raw(c, gn);
-          if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c] = load_scale(c, gn);
-        }
-        if constexpr (RING) {
+        for (int c = 0; c < ILP; ++c)
 #pragma unroll
-          for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
-        }
-        uint32_t e[ILP][SPF];
-        auto steps = [&](auto careful) {
+          for (int h = 0; h < NS; ++h) {
+            raw[c][h] = raw_n[c][h];
+            sc[c][h] = sc_n[c][h];
+            nsc8[c][h] = -8.f * sc[c][h];
+          }
+        // next fragment's loads go after this fragment's last ring advance
+        // (a chunk written to the ring waits for the loads issued before it)
+        auto prefetch = [&]() __attribute__((always_inline)) {
+#pragma unroll
+          for (int c = 0; c < ILP; ++c)
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+              if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, gn, h);
+              if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, gn, h);
+            }
+        };
+        constexpr int kPrefetchStep = RING ? ((SPF - 1) / ADV) * ADV : 0;
+        FragAcc<FMT> e[ILP][NS];
+        auto steps = [&](auto careful) __attribute__((always_inline)) {
 #pragma unroll
           for (int i = 0; i < SPF; ++i) {
-            uint32_t sy[ILP];
-            step_all<64, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, false, sy);
+            if constexpr (RING) {
+              if (i % ADV == 0) {
 #pragma unroll
-            for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
+                for (int c = 0; c < ILP; ++c)
+                  ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+              }
+            }
+            if (i == kPrefetchStep) prefetch();
+            uint32_t sy[ILP][NS];
+            step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, false, sy);
+#pragma unroll
+            for (int c = 0; c < ILP; ++c)
+#pragma unroll
+              for (int h = 0; h < NS; ++h) e[c][h].put(i, sy[c][h]);
           }
         };
         // payload steps (at most the last kPayloadMax) fall in the last fragments
-        if (fn < FN - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min)
+        if (fn < FNH - (int)(kPayloadMax / SPF) || s0 + SPF - 1 < lim_min)
           steps(BoolC<false>{});
         else
           steps(BoolC<true>{});
-        uint8_t* buf = xbuf + (g & 1) * (NT * 1024);
+        // operand o = j * NS + h: batch tile j = c * NW + wave, row half h
+        uint8_t* buf = xbuf + (g & 1) * (NO * 1024);
 #pragma unroll
-        for (int c = 0; c < ILP; ++c) {
-          const BOp bop = make_b<FMT>(e[c], raw[c], sc[c], nsc8[c]);
-          *reinterpret_cast<u32x4*>(buf + (c * NW + wave) * 1024 + lane * 16) = bop.v;
-        }
+        for (int c = 0; c < ILP; ++c)
+#pragma unroll
+          for (int h = 0; h < NS; ++h) {
+            const BOp bop = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], nsc8[c][h]);
+            *reinterpret_cast<u32x4*>(buf + ((c * NW + wave) * NS + h) * 1024 + lane * 16) =
+                bop.v;
+          }
         __syncthreads();
         if (has_rows) {
           // fragments are read kXB at a time so their LDS latencies overlap
           constexpr int kXB = 4;
 #pragma unroll
-          for (int j0 = 0; j0 < NT; j0 += kXB) {
+          for (int o0 = 0; o0 < NO; o0 += kXB) {
             BOp bq[kXB];
 #pragma unroll
             for (int q = 0; q < kXB; ++q)
-              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (j0 + q) * 1024 + lane * 16);
+              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (o0 + q) * 1024 + lane * 16);
 #pragma unroll
-            for (int q = 0; q < kXB; ++q)
+            for (int q = 0; q < kXB; ++q) {
+              const int o = o0 + q, h = o % NS;
 #pragma unroll
               for (int mt = 0; mt < MTW; ++mt)
-                acc[fn][mt] = mfma<FMT>(A[j0 + q][mt], bq[q], acc[fn][mt]);
+                acc[h * FNH + fn][mt] = mfma<FMT>(A[o / NS][mt], bq[q], acc[h * FNH + fn][mt]);
+            }
           }
           // keep each group of reads ahead of its products
 #pragma unroll
-          for (int j0 = 0; j0 < NT; j0 += kXB) {
+          for (int o0 = 0; o0 < NO; o0 += kXB) {
             __builtin_amdgcn_sched_group_barrier(0x100, kXB, 0);        // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, kXB * MTW, 0);  // MFMA
           }
@@ -810,7 +970,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     if (a.status) {
 #pragma unroll
       for (int c = 0; c < ILP; ++c) {
-        const uint32_t fl = final_flags<64, RING>(ch[c], L.steps, false);
+        const uint32_t fl = final_flags<R, RING>(ch[c], L.steps, false);
         if (lane == 0) a.status[tj[c]] = (int32_t)fl;
       }
     }
@@ -835,7 +995,9 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
   uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
   const Layer& L = a.L;
-  constexpr uint32_t TPC = 64 / R;
+  constexpr uint32_t TPC = R == 32 ? 2 : 1;
+  constexpr int NS = states_per_lane(R);
+  constexpr int ADV = ring_group_steps(R);
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const bool upper = lane >= 32;
@@ -845,8 +1007,8 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
-  Staged stg[ILP];  // R = 32
-  Ring rg[ILP];     // R = 64
+  Staged stg[ILP];  // whole streams
+  Ring rg[ILP];     // ring
   uint32_t c0[ILP][4];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
   const uint32_t fq = lut_load_freq(L.table, L.alphabet);
@@ -864,8 +1026,9 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
-      stage_issue(L, t_l, R == 64 ? lane : half_lane, R == 64 ? 64u : 32u, stg[c]);
+      stage_issue(L, t_l, R != 32 ? lane : half_lane, R != 32 ? 64u : 32u, stg[c]);
     ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
+    ch[c].x2 = (R == 128) ? L.streams[L.index[t_l] + 64 + lane] : 0u;
   }
   build_lut(fq, L.alphabet, lut, cum);
 #pragma unroll
@@ -883,7 +1046,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     } else {
       const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
       const uint32_t mine = stage_commit(stg[c], words, (R == 32 && upper) ? rb : ra,
-                                         R == 64 ? lane : half_lane, R == 64 ? 64u : 32u);
+                                         R != 32 ? lane : half_lane, R != 32 ? 64u : 32u);
       const uint32_t na = uniform(mine);
       const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
       const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
@@ -898,69 +1061,74 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     if (R == 32) lim_min = min(lim_min, (uint32_t)__builtin_amdgcn_readlane((int)ch[c].lim, 32));
   }
   constexpr int SPF = steps_per_frag<FMT>();
-  const uint32_t FN = L.tile_n / 16;
+  constexpr uint32_t FW = (R == 128 ? 64 : R) / 2;  // fragment width (columns)
+  const uint32_t FNH = L.tile_n / 16 / NS;            // row bands per state
   const uint32_t G = L.steps / SPF;
   const uint32_t p = lane % R;
+  auto steps = [&](uint32_t s0, auto careful, uint32_t (&e)[ILP][NS][SPF]) {
+#pragma unroll
+    for (int i = 0; i < SPF; ++i) {
+      if constexpr (RING) {
+        if (i % ADV == 0) {
+#pragma unroll
+          for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
+        }
+      }
+      uint32_t sy[ILP][NS];
+      step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int h = 0; h < NS; ++h) e[c][h][i] = sy[c][h];
+    }
+  };
   for (uint32_t g = 0; g < G; ++g) {
     const uint32_t s0 = g * SPF;
-    if constexpr (RING) {
+    uint32_t e[ILP][NS][SPF];
+    if (s0 + SPF - 1 < lim_min)
+      steps(s0, BoolC<false>{}, e);
+    else
+      steps(s0, BoolC<true>{}, e);
+    const uint32_t fk = g / FNH, fn = g % FNH;
 #pragma unroll
-      for (int c = 0; c < ILP; ++c) ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
-    }
-    uint32_t e[ILP][SPF];
-    if (s0 + SPF - 1 < lim_min) {
+    for (int c = 0; c < ILP; ++c)
 #pragma unroll
-      for (int i = 0; i < SPF; ++i) {
-        uint32_t sy[ILP];
-        step_all<R, false, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
+      for (int h = 0; h < NS; ++h) {
+        const uint32_t t = tile_lane[c];
+        const uint32_t row = (t / L.kt) * L.tile_n + (h * FNH + fn) * 16 + (p & 15);
+        const uint32_t col = (t % L.kt) * L.tile_k + fk * FW + 8 * (p >> 4);
+        if constexpr (has_raw_bytes<FMT>()) {
+          const uint8_t* rp = L.raw + (size_t)t * L.tile_n * L.tile_k + (size_t)g * 8 * R +
+                              (64 * h + p) * 8;
+          const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);
+          const BOp b = make_b<FMT>(e[c][h], raw, 0.f, 0.f);
+          *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
+        } else if constexpr (FMT == INT4P) {
+          // symbol i -> code bytes 2i (low nibble) and 2i+1 (high nibble)
+          uint32_t q[4];
 #pragma unroll
-        for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < SPF; ++i) {
-        uint32_t sy[ILP];
-        step_all<R, true, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
-#pragma unroll
-        for (int c = 0; c < ILP; ++c) e[c][i] = sy[c];
-      }
-    }
-    const uint32_t fk = g / FN, fn = g % FN;
-#pragma unroll
-    for (int c = 0; c < ILP; ++c) {
-      const uint32_t t = tile_lane[c];
-      const uint32_t row = (t / L.kt) * L.tile_n + fn * 16 + (p & 15);
-      const uint32_t col = (t % L.kt) * L.tile_k + fk * (R / 2) + 8 * (p >> 4);
-      if constexpr (has_raw_bytes<FMT>()) {
-        const uint8_t* rp = L.raw + (size_t)t * L.tile_n * L.tile_k + (size_t)g * 8 * R + p * 8;
-        const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);
-        const BOp b = make_b<FMT>(e[c], raw, 0.f, 0.f);
-        *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
-      } else if constexpr (FMT == INT4P) {
-        // symbol i -> code bytes 2i (low nibble) and 2i+1 (high nibble)
-        uint32_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sy = e[c][i] >> 24;
-          h[i] = (sy & 0x0Fu) | ((sy & 0xF0u) << 4);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t sy = e[c][h][i] >> 24;
+            q[i] = (sy & 0x0Fu) | ((sy & 0xF0u) << 4);
+          }
+          u32x2 v;
+          v.x = q[0] | (q[1] << 16);
+          v.y = q[2] | (q[3] << 16);
+          *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
+        } else {
+          const uint32_t(&ec)[SPF] = e[c][h];
+          u32x2 v;
+          v.x = pack_hi_bytes(ec[1], ec[0]) | (pack_hi_bytes(ec[3], ec[2]) << 16);
+          v.y = pack_hi_bytes(ec[5], ec[4]) | (pack_hi_bytes(ec[7], ec[6]) << 16);
+          *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
         }
-        u32x2 v;
-        v.x = h[0] | (h[1] << 16);
-        v.y = h[2] | (h[3] << 16);
-        *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
-      } else {
-        u32x2 v;
-        v.x = pack_hi_bytes(e[c][1], e[c][0]) | (pack_hi_bytes(e[c][3], e[c][2]) << 16);
-        v.y = pack_hi_bytes(e[c][5], e[c][4]) | (pack_hi_bytes(e[c][7], e[c][6]) << 16);
-        *reinterpret_cast<u32x2*>(a.out + (size_t)row * L.k + col) = v;
       }
-    }
   }
   if (a.status) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t f = final_flags<R, RING>(ch[c], L.steps, upper);
-      if (R == 64 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+      if (R != 32 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
     }
   }
 }

@@ -27,6 +27,10 @@
  *     the ABI.  On error nothing has been enqueued.
  *   - Device blobs must be 16-byte aligned.  All multi-byte fields are
  *     little-endian.  Calls are thread-safe.
+ *   - Environment: DGT_STAGING=whole|ring overrides the per-layer choice of
+ *     how device kernels bring tile streams on chip (whole streams, or a
+ *     two-chunk ring for one tile per wave); results are identical.  Read at
+ *     every call; dgt_gemm_workspace covers every choice.
  *
  * Compressed layer ("blob") format, version 1 (all offsets in bytes):
  *   header (128 B): magic "DGT1", u16 version, u16 header size, u32 fmt,
@@ -46,6 +50,10 @@
  * out a tile's tile_n*tile_k/2 symbols the same way with 4 symbols per lane
  * per fragment (s = 4g + e, pair column fk*R/4 + 4*(p/16) + e), so a lane's
  * 4 symbols are again its 8 consecutive weights of one row.
+ * R = 128 (two states per wave lane; tile_n a multiple of 32): states p < 64
+ * order the top tile_n/2 rows and states 64 + p the bottom tile_n/2 rows,
+ * each half exactly as an R = 64 tile of tile_n/2 rows; both share the one
+ * word stream (interleaving j = s*128 + p); raw byte q = g*1024 + p*8 + e.
  * 16-bit renormalisation words; decode x' = f*(x>>n) + (x mod 2^n) - c_s,
  * then if x' < 2^16 read one word.  The last k[t] steps of a tile decode from
  * y = x - 2^16 without reading words; a valid tile ends with y == 0 on every
@@ -137,7 +145,7 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out);
  *   d_status: NULL or int32[tiles]; entry t is set to 0 when tile t decoded
  *          with a consistent stream, else to a positive error mask
  *          (1 = final state, 2 = stream length, 4 = stream overrun).
- * Errors (synchronous): E_ARG, E_UNSUPPORTED (lanes not 32/64, stream too
+ * Errors (synchronous): E_ARG, E_UNSUPPORTED (lanes not 32/64/128, stream too
  * long for on-chip staging), E_HIP. */
 int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d_tile_ids,
                      uint32_t n_ids, void* d_out, int32_t* d_status, void* stream);

@@ -25,7 +25,8 @@ from tests.gpu_util import codes_as_u8_or_u16, to_dev, x_dev
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 NAMES = ["int8_1024", "int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405",
-         "int4_4096_pair", "int4_ffn405_pair", "bf16_mlp_exp"]
+         "int4_4096_pair", "int4_ffn405_pair", "bf16_mlp_exp", "int4_4096_r128",
+         "fp8_8192_r128", "bf16_mlp_r128"]
 _CACHE = {}
 
 

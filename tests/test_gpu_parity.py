@@ -38,6 +38,14 @@ CASES = [
     (FP, 512, 2048, 256, 64, 64, 12),     # int4 pairs, tile_n 256
     (FX, 384, 1024, 128, 64, 64, 13),     # bf16 exponent split
     (FX, 256, 256, 128, 32, 32, 14),      # bf16 exponent split, two tiles per wave
+    # two states per lane (R = 128)
+    (F8, 256, 512, 128, 32, 128, 15),
+    (F4, 256, 1024, 128, 64, 128, 16),
+    (FE, 512, 448, 256, 64, 128, 17),     # 7 k-tiles, tile_n 256
+    (FB, 384, 640, 128, 64, 128, 18),
+    (FB, 256, 4096, 128, 64, 128, 19),    # several workgroups per strip
+    (FP, 256, 1024, 128, 64, 128, 20),
+    (FX, 384, 1024, 128, 64, 128, 22),
 ]
 
 
@@ -115,6 +123,11 @@ XM_CASES = [
     (FP, 384, 2048, 128, 64, 64, 49),     # int4 pairs
     (FP, 512, 1024, 256, 64, 64, 50),
     (FX, 256, 2048, 128, 64, 64, 51),     # bf16 exponent split
+    (FB, 384, 4096, 128, 64, 128, 55),    # two states per lane: two operands per fragment
+    (FE, 512, 1024, 256, 64, 128, 56),
+    (F4, 256, 2048, 128, 64, 128, 57),
+    (FP, 512, 1024, 256, 64, 128, 58),
+    (FX, 256, 2048, 128, 64, 128, 59),
 ]
 
 
@@ -141,6 +154,7 @@ def test_fused_gemm_large_m_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     (FB, 384, 4096, 128, 64, 64, 52),
     (FE, 512, 1024, 256, 64, 64, 53),     # one fp8 activation scale across passes
     (FP, 256, 2048, 128, 64, 64, 54),
+    (FB, 384, 4096, 128, 64, 128, 60),
 ])
 @pytest.mark.parametrize("m", [257, 300, 513])
 def test_fused_gemm_beyond_one_pass(fmt, n, k, tn, tk, R, seed, m):
@@ -151,6 +165,42 @@ def test_fused_gemm_beyond_one_pass(fmt, n, k, tn, tk, R, seed, m):
     y = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
+
+
+STAGING_CASES = [
+    (FB, 384, 4096, 128, 64, 64, 71),
+    (FB, 256, 2048, 128, 64, 128, 72),
+    (FE, 512, 1024, 256, 64, 64, 73),
+    (FE, 512, 1024, 256, 64, 128, 74),
+    (FP, 256, 2048, 128, 64, 128, 75),
+    (F8, 256, 2048, 128, 64, 128, 76),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", STAGING_CASES)
+@pytest.mark.parametrize("staging", ["ring", "whole"])
+def test_forced_staging_matches_oracle(fmt, n, k, tn, tk, R, seed, staging, monkeypatch):
+    """Both ways of bringing tile streams on chip (whole, or a two-chunk ring)
+    give the oracle's results, for the decode and for the fused GEMM at small
+    (register path) and large (LDS-shared fragments) M."""
+    import torch
+    monkeypatch.setenv("DGT_STAGING", staging)
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=100)
+    layer = dgt.DeviceLayer(blob)
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    out = dgt.dgt_decode_tiles(layer, status=status)
+    torch.cuda.synchronize()
+    assert np.array_equal(decoded_to_numpy(fmt, out), codes_as_u8_or_u16(fmt, d["codes"]))
+    assert (status.cpu().numpy() == 0).all()
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    for m in (1, 16, 100):
+        xb = d["x"][:m]
+        status.fill_(-1)
+        y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), scales=scales, w_scale=d["w_scale"],
+                                      status=status)
+        torch.cuda.synchronize()
+        assert rel_err(y.cpu().numpy(), reference(fmt, d, xb)) <= TOL, m
+        assert (status.cpu().numpy() == 0).all()
 
 
 def test_fused_gemm_large_m_repeatable():
@@ -212,11 +262,14 @@ def test_dense_baseline_matches_oracle(fmt, tn, m):
     assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
 
 
-def test_corrupt_stream_sets_status_and_stays_in_bounds():
+@pytest.mark.parametrize("R,staging", [(64, "whole"), (64, "ring"), (128, "whole"),
+                                       (128, "ring")])
+def test_corrupt_stream_sets_status_and_stays_in_bounds(R, staging, monkeypatch):
     """Bytes flipped inside tile word streams (the index untouched): the
     kernel's clamps keep every access in bounds and the tile status reports it."""
     import torch
-    d, blob = _layer(F8, 256, 512, 128, 64, 64, 51)
+    monkeypatch.setenv("DGT_STAGING", staging)
+    d, blob = _layer(F8, 256, 512, 128, 64, R, 51)
     info = dgt.dgt_layer_info(blob)
     h = oblob.parse(blob)
     b = bytearray(blob)

@@ -46,6 +46,13 @@ CASES = [
     (dgt.DGT_FMT_INT4_PAIR, 512, 128, 256, 64, 64, 11),
     (dgt.DGT_FMT_BF16_EXP, 256, 128, 128, 64, 64, 12),
     (dgt.DGT_FMT_BF16_EXP, 256, 64, 256, 32, 64, 13),
+    # two states per lane
+    (dgt.DGT_FMT_INT8, 256, 64, 64, 32, 128, 14),
+    (dgt.DGT_FMT_INT4, 256, 256, 128, 64, 128, 15),
+    (dgt.DGT_FMT_FP8_E4M3, 512, 128, 256, 64, 128, 16),
+    (dgt.DGT_FMT_BF16_SPLIT, 256, 128, 128, 64, 128, 17),
+    (dgt.DGT_FMT_INT4_PAIR, 256, 256, 128, 64, 128, 18),
+    (dgt.DGT_FMT_BF16_EXP, 256, 128, 128, 64, 128, 19),
 ]
 
 

@@ -22,6 +22,8 @@ Recipe (numpy.random.default_rng(seed); W first, then scales, then X):
   int4_4096_pair, int4_ffn405_pair: the two int4 layers above (same seeds,
                 same draws) in the pair-symbol format.
   bf16_mlp_exp  the bf16_mlp layer (same seed, same draws) in the exponent split.
+  *_r128        the named layer (same seed, same draws) coded with two rANS
+                states per lane (R = 128: tile halves of tile_n/2 rows).
   bf16_ffn405   W 53248x16384 bf16 N(0, 0.01); X bf16 [256, 16384].
                 Tiles 256x64, 64 lanes.
 rint is numpy's (ties to even); clipping follows rounding.  Casts to bf16 and
@@ -83,6 +85,13 @@ WORKLOADS = {
                              (1, 8, 64, 256), w_sigma=0.02,
                              note="bf16 N(0,0.02) exponent split, Llama-3-8B MLP shape"),
 }
+# two states per lane: the same layers with R = 128
+for _base in ("int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405"):
+    _w = WORKLOADS[_base]
+    WORKLOADS[_base + "_r128"] = Workload(
+        _base + "_r128", _w.fmt, _w.n, _w.k, _w.tile_n, _w.tile_k, 128, _w.seed, _w.m_values,
+        w_sigma=_w.w_sigma, w_mean=_w.w_mean, prob_bits=_w.prob_bits,
+        note=_w.note + ", two states per lane (R = 128)")
 
 
 def _normal(rng, count: int, mean: float, sigma: float) -> np.ndarray:
