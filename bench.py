@@ -182,7 +182,7 @@ def main():
     dist = launch_distribution(fused, 50, stream)
     nk = wl.n * wl.k
     # decoded-weight bytes at the format's storage width (int4 half a byte)
-    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0}[wl.fmt]
+    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0}[wl.fmt]
     value = decoded_bytes / (ms * 1e-3) / 1e9
     alg_bytes = len(blob) + m * wl.k * 2 + m * wl.n * 4
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -279,6 +279,22 @@ def main():
                 del wts
         secondary["ablation"] = ablation
         del wd, dec
+        # the same layer with two rANS states per lane (R = 128): bits and time
+        if wl.lanes == 64 and wl.tile_n % 32 == 0:
+            blob2 = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, 128)
+            c2 = max(2, math.ceil(ROTATE_BYTES / len(blob2)))
+            l2 = [dgt.DeviceLayer(blob2, dev) for _ in range(c2)]
+            r128 = {"bits_per_weight": round(dgt.dgt_layer_info(blob2).bits_per_weight, 4)}
+            for mm, xm_ in ((1, x1), (256, x2)):
+                wsr = dgt.alloc_workspace(dgt.dgt_gemm_workspace(l2[0], mm), dev)
+                yr = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
+                r128["fused_m%d_ms" % mm] = round(timed(
+                    lambda i: dgt.dgt_fused_decode_gemm(l2[i % c2], xm_, scales=scales,
+                                                        w_scale=d["w_scale"], y=yr, ws=wsr,
+                                                        stream=stream),
+                    reps, 3, stream), 4)
+            secondary["two_states_per_lane"] = r128
+            del l2
     result["secondary"] = secondary
 
     if args.copy_calib:

@@ -697,6 +697,8 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t M = a.m, TN = FN * 16, wg = blockIdx.x;
   const uint32_t f = strip_first_wg(strip, x.bps, x.bpw), l = strip_last_wg(strip, x.bps, x.bpw);
+  // waves whose rows all lie at or past M hold nothing to hand over
+  const bool rows = wave * MTW * 16 < M;
   auto store_y = [&](int fn, int mt, floatx4 v) __attribute__((always_inline)) {
     const uint32_t col = strip * TN + fn * 16 + (lane & 15);
     const uint32_t m0 = (wave * MTW + mt) * 16 + 4 * (lane >> 4);
@@ -723,12 +725,14 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
       // agent-scope stores: coherent across XCDs without an L2 writeback
+      if (rows) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint64_t bits = (uint64_t)__float_as_uint(acc[fn][mt][2 * h]) |
-                              ((uint64_t)__float_as_uint(acc[fn][mt][2 * h + 1]) << 32);
-        __hip_atomic_store(pair_ptr(wg - f, fn, mt, h), bits, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        for (int h = 0; h < 2; ++h) {
+          const uint64_t bits = (uint64_t)__float_as_uint(acc[fn][mt][2 * h]) |
+                                ((uint64_t)__float_as_uint(acc[fn][mt][2 * h + 1]) << 32);
+          __hip_atomic_store(pair_ptr(wg - f, fn, mt, h), bits, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
       acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -743,7 +747,7 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
   __syncthreads();
   const bool last = *flag != 0;
   __syncthreads();  // flag is rewritten by the next flush
-  if (!last) return;
+  if (!last || !rows) return;  // (wave 0 always has rows: it resets the counter)
   const uint32_t n = l - f + 1;
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn)
