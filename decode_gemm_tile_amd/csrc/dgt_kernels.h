@@ -853,17 +853,6 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
       return __uint_as_float((uint32_t)sb << 16);
     };
-    u32x2 raw_n[ILP][NS];
-    float sc_n[ILP][NS];
-#pragma unroll
-    for (int c = 0; c < ILP; ++c)
-#pragma unroll
-      for (int h = 0; h < NS; ++h) {
-        raw_n[c][h] = u32x2{0u, 0u};
-        sc_n[c][h] = 0.f;
-        if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, 0, h);
-        if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, 0, h);
-      }
     // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
     const uint8_t* xp[MTW];
 #pragma unroll
@@ -886,26 +875,22 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       for (int fn = 0; fn < FNH; ++fn) {
         const uint32_t g = fk * FNH + fn;
         const uint32_t s0 = g * SPF;
-        const uint32_t gn = min(g + 1, G - 1);
+        // this fragment's raw bytes and scales: a fragment's decode (8
+        // dependent steps) outlasts their load, so they are not fetched a
+        // fragment ahead (registers are the budget here); the loads go after
+        // the fragment's last ring advance (a chunk written to the ring waits
+        // for the loads issued before it)
         u32x2 raw[ILP][NS];
-        float sc[ILP][NS], nsc8[ILP][NS];
-#pragma unroll
-        for (int c = 0; c < ILP; ++c)
-#pragma unroll
-          for (int h = 0; h < NS; ++h) {
-            raw[c][h] = raw_n[c][h];
-            sc[c][h] = sc_n[c][h];
-            nsc8[c][h] = -8.f * sc[c][h];
-          }
-        // next fragment's loads go after this fragment's last ring advance
-        // (a chunk written to the ring waits for the loads issued before it)
+        float sc[ILP][NS];
         auto prefetch = [&]() __attribute__((always_inline)) {
 #pragma unroll
           for (int c = 0; c < ILP; ++c)
 #pragma unroll
             for (int h = 0; h < NS; ++h) {
-              if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, gn, h);
-              if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, gn, h);
+              raw[c][h] = u32x2{0u, 0u};
+              sc[c][h] = 0.f;
+              if constexpr (has_raw_bytes<FMT>()) raw[c][h] = load_raw(c, g, h);
+              if constexpr (FMT == INT4 || FMT == INT4P) sc[c][h] = load_scale(c, g, h);
             }
         };
         constexpr int kPrefetchStep = RING ? ((SPF - 1) / ADV) * ADV : 0;
@@ -940,7 +925,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
           for (int h = 0; h < NS; ++h) {
-            const BOp bop = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], nsc8[c][h]);
+            const BOp bop = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], -8.f * sc[c][h]);
             *reinterpret_cast<u32x4*>(buf + ((c * NW + wave) * NS + h) * 1024 + lane * 16) =
                 bop.v;
           }
