@@ -100,6 +100,52 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs q) {
 }
 
 
+// Small activations (count <= kQuantOneBlock): the maximum and the
+// quantisation in one workgroup, one launch instead of two (same arithmetic
+// as k_amax + k_quant; the shared maximum and counter stay at zero).
+constexpr uint32_t kQuantOneBlock = 65536;
+
+__global__ __launch_bounds__(1024) void k_amax_quant(QuantArgs q) {
+  __shared__ uint32_t wmax[16];
+  const uint32_t t = threadIdx.x, n8 = q.count / 8;  // count % 8 == 0 (K % 64 == 0)
+  const u32x4* x8 = reinterpret_cast<const u32x4*>(q.x);
+  uint32_t mx = 0;
+  for (uint32_t i = t; i < n8; i += 1024) {
+    const u32x4 v = x8[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mx = max(mx, (v[j] << 16) & 0x7FFFFFFFu);
+      mx = max(mx, v[j] & 0x7FFF0000u);
+    }
+  }
+  for (int d = 32; d > 0; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, d, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = mx;
+  __syncthreads();
+  uint32_t am = 0;
+  for (uint32_t w = 0; w < (blockDim.x >> 6); ++w) am = max(am, wmax[w]);
+  const float amax = __uint_as_float(am);
+  float inv = 1.f, sx = 1.f;
+  const bool zero = !(amax > 0.f) || amax > 3.4e38f;
+  if (!zero) {
+    inv = (float)(448.0 / (double)amax);
+    sx = (float)((double)amax / 448.0);
+  }
+  u32x4* xq8 = reinterpret_cast<u32x4*>(q.xq);
+  for (uint32_t i = t; i < n8; i += 1024) {
+    const u32x4 v = x8[i];
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xFFFF0000u);
+      const uint32_t ql = zero ? 0u : e4m3_to_bf16(f32_to_e4m3(lo * inv));
+      const uint32_t qh = zero ? 0u : e4m3_to_bf16(f32_to_e4m3(hi * inv));
+      o[j] = ql | (qh << 16);
+    }
+    xq8[i] = o;
+  }
+  if (t == 0) __hip_atomic_store(q.sx, sx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dev
 }  // namespace dgt
 
@@ -328,14 +374,17 @@ int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t
   q.done = reinterpret_cast<uint32_t*>(ws_q + 4);
   q.sx = reinterpret_cast<float*>(ws_q + 8);
   q.count = count;
+  *xq = q.xq;
+  *sx = q.sx;
+  if (count <= kQuantOneBlock && count % 8 == 0) {
+    hipLaunchKernelGGL(k_amax_quant, dim3(1), dim3(1024), 0, st, q);
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
+  }
   const uint32_t blocks = std::max<uint32_t>(1, std::min<uint32_t>(1024, (count + 2047) / 2048));
   hipLaunchKernelGGL(k_amax, dim3(blocks), dim3(256), 0, st, q);
   if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
   hipLaunchKernelGGL(k_quant, dim3(blocks), dim3(256), 0, st, q);
-  if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
-  *xq = q.xq;
-  *sx = q.sx;
-  return DGT_OK;
+  return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
 }
 
 }  // namespace
