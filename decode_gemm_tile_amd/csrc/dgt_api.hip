@@ -227,7 +227,8 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
       (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nt * region_bytes + 16, 16);
-  const uint32_t lds = xbuf_off + 2 * nt * ns * 1024;
+  const uint32_t fpb = in->lanes == 128 ? xm_fpb(128, fn) : xm_fpb(64, fn);
+  const uint32_t lds = xbuf_off + 2 * fpb * nt * ns * 1024;
   if (lds > kMaxLds) return false;
   p->xm = 1;
   p->xbuf_off = xbuf_off;

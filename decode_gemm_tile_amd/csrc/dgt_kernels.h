@@ -683,6 +683,11 @@ __host__ __device__ constexpr int xm_waves(int FN) { return FN == 8 ? 16 : 8; }
 __host__ __device__ constexpr int xm_row_blocks(int FN) { return FN == 8 ? 1 : 2; }
 __host__ __device__ constexpr int xm_ilp(int FN) { return 1; }
 __host__ __device__ constexpr int xm_tiles(int FN) { return xm_waves(FN) * xm_ilp(FN); }
+// fragments published per barrier: two when the doubled buffers stay within
+// 64 KiB of LDS (operands of 1 KiB: tiles x states per lane per fragment)
+__host__ __device__ constexpr int xm_fpb(int R, int FN) {
+  return 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024 ? 2 : 1;
+}
 
 // Partials of a strip shared by several workgroups are kept in the
 // accumulators' register layout (slot, wave, row block, fragment, float pair,
@@ -776,6 +781,8 @@ template <int FMT, int R, int FN, bool RING>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
+  constexpr int FPB = xm_fpb(R, FN);
+  static_assert(FNH % FPB == 0 && (NO * FPB) % 4 == 0, "fragment groups");
   constexpr uint32_t FW = 32, TK = 64, FK = TK / FW, G = FK * FNH;
   constexpr int SPF = steps_per_frag<FMT>();
   constexpr int ADV = ring_group_steps(R);
@@ -871,8 +878,16 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           for (int mt = 0; mt < MTW; ++mt)
             A[j][mt] = *reinterpret_cast<const u32x4*>(xp[mt] + fk * FW * 2 + j * TK * 2);
       }
+      // FPB fragments per barrier: each wave decodes and publishes them, then
+      // every wave multiplies all of them (alternating accumulators, so
+      // consecutive matrix operations do not wait for each other)
 #pragma unroll
-      for (int fn = 0; fn < FNH; ++fn) {
+      for (int f0 = 0; f0 < FNH; f0 += FPB) {
+        const uint32_t gq = (fk * FNH + f0) / FPB;
+        uint8_t* buf = xbuf + (gq & 1) * (FPB * NO * 1024);
+#pragma unroll
+        for (int d = 0; d < FPB; ++d) {
+        const int fn = f0 + d;
         const uint32_t g = fk * FNH + fn;
         const uint32_t s0 = g * SPF;
         // this fragment's raw bytes and scales: a fragment's decode (8
@@ -919,37 +934,39 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           steps(BoolC<false>{});
         else
           steps(BoolC<true>{});
-        // operand o = j * NS + h: batch tile j = c * NW + wave, row half h
-        uint8_t* buf = xbuf + (g & 1) * (NO * 1024);
+        // operand o = j * NS + h of fragment d: batch tile j = c * NW + wave, row half h
 #pragma unroll
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
           for (int h = 0; h < NS; ++h) {
             const BOp bop = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], -8.f * sc[c][h]);
-            *reinterpret_cast<u32x4*>(buf + ((c * NW + wave) * NS + h) * 1024 + lane * 16) =
-                bop.v;
+            *reinterpret_cast<u32x4*>(buf + (d * NO + (c * NW + wave) * NS + h) * 1024 +
+                                      lane * 16) = bop.v;
           }
+        }
         __syncthreads();
         if (has_rows) {
-          // fragments are read kXB at a time so their LDS latencies overlap
+          // operands are read kXB at a time so their LDS latencies overlap
           constexpr int kXB = 4;
 #pragma unroll
-          for (int o0 = 0; o0 < NO; o0 += kXB) {
+          for (int o0 = 0; o0 < NO; o0 += kXB / FPB) {
             BOp bq[kXB];
 #pragma unroll
-            for (int q = 0; q < kXB; ++q)
-              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (o0 + q) * 1024 + lane * 16);
+            for (int q = 0; q < kXB; ++q) {
+              const int d = q % FPB, o = o0 + q / FPB;
+              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (d * NO + o) * 1024 + lane * 16);
+            }
 #pragma unroll
             for (int q = 0; q < kXB; ++q) {
-              const int o = o0 + q, h = o % NS;
+              const int d = q % FPB, o = o0 + q / FPB, h = o % NS, ai = h * FNH + f0 + d;
 #pragma unroll
               for (int mt = 0; mt < MTW; ++mt)
-                acc[h * FNH + fn][mt] = mfma<FMT>(A[o / NS][mt], bq[q], acc[h * FNH + fn][mt]);
+                acc[ai][mt] = mfma<FMT>(A[o / NS][mt], bq[q], acc[ai][mt]);
             }
           }
           // keep each group of reads ahead of its products
 #pragma unroll
-          for (int o0 = 0; o0 < NO; o0 += kXB) {
+          for (int o0 = 0; o0 < NO; o0 += kXB / FPB) {
             __builtin_amdgcn_sched_group_barrier(0x100, kXB, 0);        // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, kXB * MTW, 0);  // MFMA
           }
