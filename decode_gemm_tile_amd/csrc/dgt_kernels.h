@@ -683,10 +683,13 @@ __host__ __device__ constexpr int xm_waves(int FN) { return FN == 8 ? 16 : 8; }
 __host__ __device__ constexpr int xm_row_blocks(int FN) { return FN == 8 ? 1 : 2; }
 __host__ __device__ constexpr int xm_ilp(int FN) { return 1; }
 __host__ __device__ constexpr int xm_tiles(int FN) { return xm_waves(FN) * xm_ilp(FN); }
-// fragments published per barrier: two when the doubled buffers stay within
-// 64 KiB of LDS (operands of 1 KiB: tiles x states per lane per fragment)
+// fragments published per barrier: the most (4, 2 or 1) whose doubled buffers
+// stay within 64 KiB of LDS (operands of 1 KiB: tiles x states per lane per
+// fragment)
 __host__ __device__ constexpr int xm_fpb(int R, int FN) {
-  return 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024 ? 2 : 1;
+  return 2 * 4 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024   ? 4
+         : 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024 ? 2
+                                                                          : 1;
 }
 
 // Partials of a strip shared by several workgroups are kept in the
