@@ -159,6 +159,7 @@ def main():
     blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
     encode_s = time.perf_counter() - t0
     info = dgt.dgt_layer_info(blob)
+    wide = wl.fmt in (4, 6)  # bf16 layers: one uint16 code per weight
     sym = (np.asarray(d["codes"]) >> 8).astype(np.uint8) if wl.fmt == 4 else None
     h_hi = oentropy.empirical_entropy(sym, 256) if sym is not None else None
 
@@ -218,8 +219,9 @@ def main():
         secondary["entropy_hi_byte_bits"] = round(h_hi, 4)
         secondary["bits_over_entropy"] = round(info.bits_per_weight - (h_hi + 8.0), 4)
     if not args.no_secondary:
-        # fused at M = 256 (TFLOP/s) and the uncompressed baseline at M = 1 and 256
-        m2 = 256
+        # fused at M = 256 (TFLOP/s; the workload's largest M if smaller) and
+        # the uncompressed baseline at M = 1 and that M
+        m2 = min(256, xall.shape[0])
         x2 = xall[:m2].contiguous()
         ws2 = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layers[0], m2), dev)
         y2 = torch.empty((m2, wl.n), dtype=torch.float32, device=dev)
@@ -228,20 +230,20 @@ def main():
                                                         stream=stream),
                     max(5, args.steps // 10), 3, stream)
         flops = 2.0 * m2 * nk
-        secondary["fused_m256_ms"] = round(ms2, 4)
-        secondary["fused_m256_tflops"] = round(flops / (ms2 * 1e-3) / 1e12, 3)
-        secondary["fused_m256_mfma_frac"] = round(flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        secondary["fused_m%d_ms" % m2] = round(ms2, 4)
+        secondary["fused_m%d_tflops" % m2] = round(flops / (ms2 * 1e-3) / 1e12, 3)
+        secondary["fused_m%d_mfma_frac" % m2] = round(
+            flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         codes = np.asarray(d["codes"])
-        wraw = torch.from_numpy(codes.view(np.int16) if wl.fmt == 4 else
-                                codes.view(np.uint8)).to(dev)
+        wraw = torch.from_numpy(codes.view(np.int16) if wide else codes.view(np.uint8)).to(dev)
         dcopies = max(2, math.ceil(ROTATE_BYTES / (nk * 2)))
         wd = [wraw.clone() for _ in range(dcopies)]
         del wraw
-        dec = torch.empty((wl.n, wl.k), dtype=torch.int16 if wl.fmt == 4 else torch.uint8,
+        dec = torch.empty((wl.n, wl.k), dtype=torch.int16 if wide else torch.uint8,
                           device=dev)
         reps = max(5, args.steps // 10)
         ablation = {}
-        for mm in (1, 256):
+        for mm in sorted({1, m2}):
             xm = xall[:mm].contiguous()
             wsd = dgt.alloc_workspace(dgt.dgt_dense_workspace(wl.fmt, wl.n, wl.k, wl.tile_n, mm), dev)
             yd = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
@@ -255,7 +257,7 @@ def main():
                 secondary["dense_m1_weight_gbs"] = round(nk * 2 / (msd * 1e-3) / 1e9, 3)
                 secondary["fused_speedup_vs_dense_m1"] = round(msd / ms, 3)
             else:
-                secondary["dense_m256_tflops"] = round(2.0 * mm * nk / (msd * 1e-3) / 1e12, 3)
+                secondary["dense_m%d_tflops" % mm] = round(2.0 * mm * nk / (msd * 1e-3) / 1e12, 3)
             # ablation: layer-level decode to HBM, then the dense GEMM on the
             # decoded copy (two launches per step) against the fused kernel
             ms_dec = timed(lambda i: dgt.dgt_decode_tiles(layers[i % copies], out=dec,
@@ -266,17 +268,27 @@ def main():
                 dgt.dgt_dense_gemm(wl.fmt, dec, xm, tile_n=wl.tile_n, scales=scales,
                                    w_scale=d["w_scale"], y=yd, ws=wsd, stream=stream)
             ms_two = timed(two_stage, reps, 3, stream)
-            ms_fused = ms if mm == 1 else secondary["fused_m256_ms"]
+            ms_fused = ms if mm == 1 else secondary["fused_m%d_ms" % mm]
             ablation["m%d" % mm] = {"decode_to_hbm_ms": round(ms_dec, 4),
                                     "two_stage_ms": round(ms_two, 4),
                                     "fused_ms": round(ms_fused, 4),
                                     "fused_speedup_vs_two_stage": round(ms_two / ms_fused, 3)}
-            # vendor GEMM on the uncompressed bf16 weight (reference point only)
-            if wl.fmt == 4:
+            # vendor GEMM on the uncompressed bf16 weight (reference point only),
+            # alone and after the layer-level decode (the two-stage path with
+            # the vendor library's GEMM on the decoded copy)
+            if wide:
                 wts = [w.view(torch.bfloat16).t().contiguous() for w in wd]
                 ms_lib = timed(lambda i: torch.matmul(xm, wts[i % len(wts)]), reps, 3, stream)
                 secondary["torch_matmul_bf16_m%d_ms" % mm] = round(ms_lib, 4)
                 del wts
+                decb = dec.view(torch.bfloat16)
+
+                def two_stage_vendor(i, xm=xm):
+                    dgt.dgt_decode_tiles(layers[i % copies], out=dec, stream=stream)
+                    torch.nn.functional.linear(xm, decb)  # x @ W^T, W [N, K] as decoded
+                ms_tv = timed(two_stage_vendor, reps, 3, stream)
+                ablation["m%d" % mm]["two_stage_vendor_gemm_ms"] = round(ms_tv, 4)
+                ablation["m%d" % mm]["fused_speedup_vs_two_stage_vendor"] = round(ms_tv / ms_fused, 3)
         secondary["ablation"] = ablation
         del wd, dec
         # the same layer with two rANS states per lane (R = 128): bits and time
@@ -285,7 +297,7 @@ def main():
             c2 = max(2, math.ceil(ROTATE_BYTES / len(blob2)))
             l2 = [dgt.DeviceLayer(blob2, dev) for _ in range(c2)]
             r128 = {"bits_per_weight": round(dgt.dgt_layer_info(blob2).bits_per_weight, 4)}
-            for mm, xm_ in ((1, x1), (256, x2)):
+            for mm, xm_ in ((1, x1), (m2, x2)):
                 wsr = dgt.alloc_workspace(dgt.dgt_gemm_workspace(l2[0], mm), dev)
                 yr = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
                 r128["fused_m%d_ms" % mm] = round(timed(
