@@ -598,9 +598,13 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   a.out = static_cast<uint8_t*>(d_out);
   a.status = d_status;
   const uint32_t R = info->lanes, tpc = R == 32 ? 2 : 1;
-  const uint32_t ilp = n_ids / tpc >= 1024 * 6 ? 2 : 1;
-  uint32_t waves = 8;
-  // whole streams when eight waves' tiles fit LDS, else (R = 64, 128) the ring
+  // chains (tpc tiles each) over the CUs in one round of workgroups when the
+  // wave cap allows: two chains per wave for large layers, 4..16 waves
+  const uint32_t units = (n_ids + tpc - 1) / tpc;
+  const uint32_t ilp = units >= kCUs * 16 ? 2 : 1;
+  uint32_t waves = (units + kCUs * ilp - 1) / (kCUs * ilp);
+  waves = std::min(std::max(waves, 4u), 16u);
+  // whole streams when the workgroup's tiles fit LDS, else (R = 64, 128) the ring
   bool ring = false;
   auto lds_for = [&](uint32_t w) {
     return kLutBytes + kCumBytes + w * ilp * tpc * a.L.region_words * 2;
@@ -612,7 +616,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
     else ring = lds_for(waves) > kMaxLds;
   }
   if (ring) a.L.region_words = region_words_of(info, true);
-  while (waves > 4 && lds_for(waves) > kMaxLds) waves /= 2;
+  while (waves > 4 && lds_for(waves) > kMaxLds) --waves;
   if (lds_for(waves) > kMaxLds) return DGT_E_UNSUPPORTED;
   a.waves = waves;
   const uint32_t per_wg = waves * ilp * tpc;

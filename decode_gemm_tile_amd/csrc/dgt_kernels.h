@@ -998,7 +998,7 @@ struct DecodeArgs {
 };
 
 template <int FMT, int R, int ILP, bool RING>
-__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
