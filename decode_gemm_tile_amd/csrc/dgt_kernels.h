@@ -659,11 +659,12 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
 // fragments are shared through an LDS ping-pong buffer (the double-buffered
 // decode/compute overlap of [P1 §3.1]).  A workgroup of NW waves works on
 // batches of NT = NW * ILP consecutive k-tiles of one strip; each wave decodes
-// ILP of them as interleaved chains.  After every fragment (8 steps) each wave
-// publishes its finished 16x32 B operands into buffer (g & 1); after one
-// barrier every wave multiplies all NT fragments of the batch with its own MTW
+// ILP of them as interleaved chains.  After every group of FPB fragments (8
+// steps each) each wave publishes its finished 16x32 B operands (two per
+// fragment with two states per lane) into buffer (group & 1); after one
+// barrier every wave multiplies all the group's operands with its own MTW
 // 16-row blocks of X (A operands of the NT k-ranges stay in registers for the
-// FN fragments that share them).  Each weight is decoded once for all
+// fragments that share them).  Each weight is decoded once for all
 // M <= NW * MTW * 16 rows.  Registers bound the shape: A takes
 // rows * NT / 4 and the accumulators rows * 2 VGPRs per wave, so a CU holds
 // 16 decode chains at most (tile_n 128: 16 waves x 16 rows, one chain each;

@@ -145,8 +145,8 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out);
  *   d_status: NULL or int32[tiles]; entry t is set to 0 when tile t decoded
  *          with a consistent stream, else to a positive error mask
  *          (1 = final state, 2 = stream length, 4 = stream overrun).
- * Errors (synchronous): E_ARG, E_UNSUPPORTED (lanes not 32/64/128, stream too
- * long for on-chip staging), E_HIP. */
+ * Errors (synchronous): E_ARG, E_UNSUPPORTED (lanes not 32/64/128; R = 32
+ * streams too long for on-chip staging), E_HIP. */
 int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d_tile_ids,
                      uint32_t n_ids, void* d_out, int32_t* d_status, void* stream);
 
