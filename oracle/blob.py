@@ -9,15 +9,18 @@ pages give none); all integers are little-endian.
 header (128 bytes)
    0 magic  b"DGT1"              4 u16 version = 1     6 u16 header bytes = 128
    8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split, 5 int4 pairs,
-              6 bf16 exponent split)
+              6 bf16 exponent split, 7 bf16 byte split with high-byte pairs)
   12 u32 flags = 0              16 u32 N     20 u32 K
   24 u32 tile_n  28 u32 tile_k  32 u32 lanes R  36 u32 prob_bits n
-  40 u32 alphabet (16 for int4, else 256)       44 u32 tiles
+  40 u32 alphabet (16 for int4, 256 for the other dense tables; format 7:
+         the number P of table entries)            44 u32 tiles
   48 u64 table_off   56 u64 index_off   64 u64 ktab_off   72 u64 streams_off
   80 u64 raw_off (0 when the format stores no raw bytes)   88 u64 total bytes
   96 u32 max tile stream length in 4-byte units
  100 u32 kmax (payload-step cap, 16)    104..127 zero
-table   u16 f[alphabet]                                   (16-byte aligned)
+table   u16 f[alphabet]; format 7 (alphabet 65536, at most 2**n symbols
+        present): u32 entry[P] = symbol | f << 16 for the symbols with f > 0,
+        in increasing symbol order                        (16-byte aligned)
 index   u32 off[tiles + 1], 4-byte units from streams_off, off[0] = 0 (aligned)
 ktab    u8 k[tiles]: payload steps of each tile (see ``oracle.rans``) (aligned)
 streams tile t at streams_off + 4*off[t]: R u32 states (lane order) then the
@@ -32,7 +35,10 @@ bf16 exponent split: the 8 exponent bits (bits >> 7) & 0xFF coded, the sign
 and the 7 mantissa bits raw as one byte (sign << 7 | mantissa), the split
 DFloat11 uses ([P2]); int4 pairs: q[n, 2c] | q[n, 2c+1] << 4 (two weights adjacent along K per
 symbol, alphabet 256; tile_n and tile_k stay in weights, a tile holds
-tile_n*tile_k/2 symbols laid out by ``oracle.order`` with epl = 4).
+tile_n*tile_k/2 symbols laid out by ``oracle.order`` with epl = 4); bf16
+high-byte pairs (format 7): the bf16 byte split with the high bytes of two
+weights adjacent along K coded as one 16-bit symbol hi[n, 2c] | hi[n, 2c+1] << 8
+(the same pair geometry as int4 pairs), the low bytes raw as in format 4.
 """
 
 import struct
@@ -45,6 +51,8 @@ MAGIC = b"DGT1"
 VERSION = 1
 HEADER_BYTES = 128
 FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
+FMT_BF16_PAIR = 7
+_PAIR_FORMATS = (FMT_INT4_PAIR, FMT_BF16_PAIR)
 _HDR = struct.Struct("<4sHHIIIIIIIIII QQQQQQ II 24x")
 assert _HDR.size == HEADER_BYTES
 
@@ -58,25 +66,33 @@ def alphabet_of(fmt: int) -> int:
         return 16
     if fmt in (FMT_INT8, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP):
         return 256
+    if fmt == FMT_BF16_PAIR:
+        return 65536
     raise ValueError("unknown format")
 
 
+def sparse_table(fmt: int) -> bool:
+    """Formats whose table lists only the present symbols (symbol, f)."""
+    return fmt == FMT_BF16_PAIR
+
+
 def weights_per_symbol(fmt: int) -> int:
-    return 2 if fmt == FMT_INT4_PAIR else 1
+    return 2 if fmt in _PAIR_FORMATS else 1
 
 
 def symbol_geometry(fmt: int, n: int, k: int, tile_n: int, tile_k: int):
     """(symbol-matrix columns, tile columns in symbols, symbols per lane per
     fragment) of a format: pairs halve K and the fragment's symbol count."""
-    if fmt == FMT_INT4_PAIR:
+    if fmt in _PAIR_FORMATS:
         if k % 2 or tile_k % 2:
-            raise ValueError("int4 pairs need even K and tile_k")
+            raise ValueError("pair symbols need even K and tile_k")
         return k // 2, tile_k // 2, 4
     return k, tile_k, 8
 
 
 def symbolise(fmt: int, w):
-    """Return (symbols uint8 [N,K], raw low bytes uint8 [N,K] or None)."""
+    """Return (symbols [N,K] (uint16 [N,K/2] for bf16 pairs, uint8 [N,K/2]
+    for int4 pairs, else uint8), raw low bytes uint8 [N,K] or None)."""
     w = np.asarray(w)
     if fmt == FMT_INT8:
         return w.astype(np.int8).view(np.uint8), None
@@ -101,6 +117,12 @@ def symbolise(fmt: int, w):
             raise ValueError("int4 pairs need an even K")
         q = w.astype(np.uint8)
         return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8), None
+    if fmt == FMT_BF16_PAIR:
+        b = w.astype(np.uint16)
+        if b.shape[1] % 2:
+            raise ValueError("bf16 pairs need an even K")
+        hi = (b >> 8).astype(np.uint16)
+        return (hi[:, 0::2] | (hi[:, 1::2] << 8)).astype(np.uint16), (b & 0xFF).astype(np.uint8)
     raise ValueError("unknown format")
 
 
@@ -129,7 +151,13 @@ def compress_layer(fmt: int, w, tile_n: int, tile_k: int, lanes: int,
         chunks.append(c)
         off.append(off[-1] + len(c) // 4)
     table_off = HEADER_BYTES
-    index_off = _align(table_off + 2 * alpha, 16)
+    if sparse_table(fmt):
+        present = np.nonzero(f)[0]
+        table = (present.astype(np.uint32) | (f[present].astype(np.uint32) << 16)).astype("<u4")
+        table_bytes, alpha_field = table.tobytes(), int(present.size)
+    else:
+        table_bytes, alpha_field = f.astype("<u2").tobytes(), alpha
+    index_off = _align(table_off + len(table_bytes), 16)
     ktab_off = _align(index_off + 4 * (tiles + 1), 16)
     streams_off = _align(ktab_off + tiles, 16)
     streams_end = streams_off + 4 * off[-1]
@@ -140,11 +168,11 @@ def compress_layer(fmt: int, w, tile_n: int, tile_k: int, lanes: int,
         raw_off, total = 0, streams_end
     max_len = max(off[t + 1] - off[t] for t in range(tiles))
     hdr = _HDR.pack(MAGIC, VERSION, HEADER_BYTES, fmt, 0, n, k, tile_n, tile_k,
-                    lanes, prob_bits, alpha, tiles, table_off, index_off,
+                    lanes, prob_bits, alpha_field, tiles, table_off, index_off,
                     ktab_off, streams_off, raw_off, total, max_len, rans.KMAX)
     buf = bytearray(total)
     buf[0:HEADER_BYTES] = hdr
-    buf[table_off:table_off + 2 * alpha] = f.astype("<u2").tobytes()
+    buf[table_off:table_off + len(table_bytes)] = table_bytes
     buf[index_off:index_off + 4 * (tiles + 1)] = np.asarray(off, "<u4").tobytes()
     buf[ktab_off:ktab_off + tiles] = ks.astype(np.uint8).tobytes()
     buf[streams_off:streams_end] = b"".join(chunks)
@@ -170,7 +198,10 @@ def parse(blob) -> dict:
     if h["total"] != len(b):
         raise ValueError("size mismatch")
     order.check_geometry(h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"])
-    if h["alphabet"] != alphabet_of(h["fmt"]):
+    if sparse_table(h["fmt"]):
+        if not 1 <= h["alphabet"] <= (1 << h["prob_bits"]):
+            raise ValueError("bad table size")
+    elif h["alphabet"] != alphabet_of(h["fmt"]):
         raise ValueError("bad alphabet")
     ksym, tks, epl = symbol_geometry(h["fmt"], h["n"], h["k"], h["tile_n"], h["tile_k"])
     order.check_geometry(h["n"], ksym, h["tile_n"], tks, h["lanes"], epl)
@@ -179,7 +210,15 @@ def parse(blob) -> dict:
     if h["tiles"] != nt:
         raise ValueError("bad tile count")
     a, t = h["alphabet"], h["tiles"]
-    h["freq"] = np.frombuffer(b, "<u2", a, h["table_off"]).astype(np.int64)
+    if sparse_table(h["fmt"]):
+        ent = np.frombuffer(b, "<u4", a, h["table_off"]).astype(np.int64)
+        syms, fs = ent & 0xFFFF, ent >> 16
+        if (fs == 0).any() or (np.diff(syms) <= 0).any():
+            raise ValueError("bad sparse table")
+        h["freq"] = np.zeros(alphabet_of(h["fmt"]), np.int64)
+        h["freq"][syms] = fs
+    else:
+        h["freq"] = np.frombuffer(b, "<u2", a, h["table_off"]).astype(np.int64)
     if h["freq"].sum() != (1 << h["prob_bits"]):
         raise ValueError("frequencies do not sum to 2**prob_bits")
     h["index"] = np.frombuffer(b, "<u4", t + 1, h["index_off"]).astype(np.int64)
@@ -235,6 +274,15 @@ def decompress_layer(blob) -> np.ndarray:
     syms = decode_symbols(blob)
     n, k, tn, tk, R = h["n"], h["k"], h["tile_n"], h["tile_k"], h["lanes"]
     fmt = h["fmt"]
+    if fmt == FMT_BF16_PAIR:
+        pairs = order.scatter_tiles(syms.astype(np.uint16), n, k // 2, tn, tk // 2, R, epl=4)
+        hi = np.empty((n, k), np.uint16)
+        hi[:, 0::2] = pairs & 0xFF
+        hi[:, 1::2] = pairs >> 8
+        T = tn * tk
+        raw = np.frombuffer(blob, np.uint8, h["tiles"] * T, h["raw_off"]).reshape(h["tiles"], T)
+        lo = order.scatter_tiles(raw, n, k, tn, tk, R, raw=True).astype(np.uint16)
+        return (hi << 8) | lo
     if fmt == FMT_INT4_PAIR:
         pairs = order.scatter_tiles(syms.astype(np.uint8), n, k // 2, tn, tk // 2, R, epl=4)
         out = np.empty((n, k), np.uint8)

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import workloads
-from oracle import blob, entropy, rans
+from oracle import blob, entropy, freq, rans
 
 CASES = [
     (blob.FMT_INT8, 128, 64, 128, 32, 32),
@@ -28,6 +28,12 @@ CASES = [
     (blob.FMT_BF16, 256, 128, 128, 64, 128),
     (blob.FMT_INT4_PAIR, 256, 256, 128, 64, 128),
     (blob.FMT_BF16_EXP, 64, 128, 32, 64, 128),
+    # bf16 byte split with high-byte pairs (16-bit symbols, sparse table)
+    (blob.FMT_BF16_PAIR, 256, 128, 128, 64, 64),
+    (blob.FMT_BF16_PAIR, 512, 128, 256, 64, 64),
+    (blob.FMT_BF16_PAIR, 128, 128, 128, 32, 32),
+    (blob.FMT_BF16_PAIR, 256, 128, 128, 64, 128),
+    (blob.FMT_BF16_PAIR, 32, 32, 16, 16, 16),
 ]
 
 
@@ -168,3 +174,37 @@ def test_exponent_split_fields_and_its_size_against_the_byte_split():
     assert 0.05 < gain < 0.25
     saved = blob.bits_per_weight(b4, 256, 512) - blob.bits_per_weight(b6, 256, 512)
     assert abs(saved - gain) < 0.03
+
+
+def test_bf16_pair_symbols_sparse_table_and_size():
+    """bf16 high-byte pairs: symbol = hi[n,2c] | hi[n,2c+1] << 8, low bytes raw;
+    the table lists (symbol, f) for the present symbols only, in symbol order,
+    and parses back to the dense quantised histogram.  On independent Gaussian
+    weights the pair entropy is twice the high byte's (so pairs cost nothing in
+    principle); the 12-bit table costs a little more than for single bytes
+    (many pairs are rarer than 2^-12), and the blob stays within 0.12 bit per
+    weight of the byte split's."""
+    w = np.array([[0x3F80, 0xBF80, 0x0001, 0x8000]], np.uint16)
+    sym, raw = blob.symbolise(blob.FMT_BF16_PAIR, w)
+    assert sym.dtype == np.uint16 and sym.tolist() == [[0xBF3F, 0x8000]]
+    assert raw.tolist() == [[0x80, 0x80, 0x01, 0x00]]
+    with pytest.raises(ValueError):
+        blob.symbolise(blob.FMT_BF16_PAIR, np.array([[1, 2, 3]], np.uint16))
+    d = workloads.random_small(blob.FMT_BF16_PAIR, 256, 1024, seed=17)
+    b7 = blob.compress_layer(blob.FMT_BF16_PAIR, d["codes"], 128, 64, 64)
+    h = blob.parse(b7)
+    ent = np.frombuffer(b7, "<u4", h["alphabet"], h["table_off"])
+    syms, fs = ent & 0xFFFF, ent >> 16
+    assert (np.diff(syms.astype(np.int64)) > 0).all() and (fs > 0).all()
+    assert fs.sum() == 4096 and h["alphabet"] == (h["freq"] > 0).sum()
+    ps, _ = blob.symbolise(blob.FMT_BF16_PAIR, d["codes"])
+    f_ref = freq.quantize_freqs(entropy.histogram(ps, 65536), 12)
+    assert np.array_equal(h["freq"], f_ref)
+    assert np.array_equal(blob.decompress_layer(b7), d["codes"])
+    hi, _ = blob.symbolise(blob.FMT_BF16, d["codes"])
+    h1 = entropy.empirical_entropy(hi, 256)
+    h2 = entropy.empirical_entropy(ps, 65536)
+    assert h2 <= 2 * h1 + 1e-12 and 2 * h1 - h2 < 0.05   # independent draws
+    b4 = blob.compress_layer(blob.FMT_BF16, d["codes"], 128, 64, 64)
+    extra = blob.bits_per_weight(b7, 256, 1024) - blob.bits_per_weight(b4, 256, 1024)
+    assert -0.05 < extra < 0.12

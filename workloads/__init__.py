@@ -22,6 +22,8 @@ Recipe (numpy.random.default_rng(seed); W first, then scales, then X):
   int4_4096_pair, int4_ffn405_pair: the two int4 layers above (same seeds,
                 same draws) in the pair-symbol format.
   bf16_mlp_exp  the bf16_mlp layer (same seed, same draws) in the exponent split.
+  bf16_mlp_pair, bf16_ffn405_pair: the two bf16 layers (same seeds, same draws)
+                in the byte split with the high bytes coded in pairs.
   *_r128        the named layer (same seed, same draws) coded with two rANS
                 states per lane (R = 128: tile halves of tile_n/2 rows).
   bf16_ffn405   W 53248x16384 bf16 N(0, 0.01); X bf16 [256, 16384].
@@ -35,6 +37,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
+FMT_BF16_PAIR = 7
+_BF16_FORMATS = (FMT_BF16, FMT_BF16_EXP, FMT_BF16_PAIR)
 _CHUNK = 1 << 24
 
 
@@ -85,6 +89,13 @@ WORKLOADS = {
                              (1, 8, 64, 256), w_sigma=0.02,
                              note="bf16 N(0,0.02) exponent split, Llama-3-8B MLP shape"),
 }
+# the bf16 layers (same draws) with the high bytes of adjacent weights coded in pairs
+for _base in ("bf16_mlp", "bf16_ffn405"):
+    _w = WORKLOADS[_base]
+    WORKLOADS[_base + "_pair"] = Workload(
+        _base + "_pair", FMT_BF16_PAIR, _w.n, _w.k, _w.tile_n, _w.tile_k, _w.lanes, _w.seed,
+        _w.m_values, w_sigma=_w.w_sigma, prob_bits=_w.prob_bits,
+        note=_w.note + ", high bytes coded in pairs")
 # two states per lane: the same layers with R = 128
 for _base in ("int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405"):
     _w = WORKLOADS[_base]
@@ -155,7 +166,7 @@ def make_weights(wl: Workload, rng=None):
         q = (wt / sw).to(torch.float8_e4m3fn)
         out["codes"] = q.view(torch.uint8).numpy().copy()
         out["w_scale"] = float(sw)
-    elif wl.fmt in (FMT_BF16, FMT_BF16_EXP):
+    elif wl.fmt in _BF16_FORMATS:
         out["codes"] = _normal_bf16_bits(rng, n * k, 0.0, wl.w_sigma).reshape(n, k)
     else:
         raise ValueError("unknown format")
@@ -197,7 +208,7 @@ def random_small(fmt: int, n: int, k: int, seed: int, sigma: float = None,
         sw = (wt.abs().max() / 448.0).to(torch.float32)
         d["codes"] = (wt / sw).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(n, k).copy()
         d["w_scale"] = float(sw)
-    elif fmt in (FMT_BF16, FMT_BF16_EXP):
+    elif fmt in _BF16_FORMATS:
         d["codes"] = _to_bf16_bits(_normal(rng, n * k, 0.0,
                                            0.02 if sigma is None else sigma)).reshape(n, k)
     d["x"] = _to_bf16_bits(rng.normal(0.0, 1.0, m * k)).reshape(m, k)
