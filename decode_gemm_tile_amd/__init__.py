@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libdgt.so")
 DGT_FMT_INT8, DGT_FMT_INT4, DGT_FMT_FP8_E4M3, DGT_FMT_BF16_SPLIT = 1, 2, 3, 4
 DGT_FMT_INT4_PAIR = 5
 DGT_FMT_BF16_EXP = 6
+DGT_FMT_BF16_PAIR = 7
 STATUS = {0: "DGT_OK", -1: "DGT_E_ARG", -2: "DGT_E_SHAPE", -3: "DGT_E_ALPHABET",
           -4: "DGT_E_BUFSIZE", -5: "DGT_E_FORMAT", -6: "DGT_E_CORRUPT", -7: "DGT_E_HIP",
           -8: "DGT_E_UNSUPPORTED"}
@@ -160,7 +161,8 @@ def dgt_decode_tiles(layer: DeviceLayer, tile_ids=None, out=None, status=None, s
     inf = layer.info
     dev = layer.blob.device
     if out is None:
-        dt = torch.int16 if inf.fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP) else torch.uint8
+        dt = (torch.int16 if inf.fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
+              else torch.uint8)
         out = torch.zeros((inf.n, inf.k), dtype=dt, device=dev)
     ids = None
     n_ids = 0

@@ -226,7 +226,7 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   p->region_words = region_words_of(in, ring);
   const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
-      (uint32_t)dgt::align_up((size_t)kLutBytes + kCumBytes + nt * region_bytes + 16, 16);
+      (uint32_t)dgt::align_up((size_t)tab_bytes_of((int)in->fmt) + nt * region_bytes + 16, 16);
   const uint32_t fpb = in->lanes == 128 ? xm_fpb(128, fn) : xm_fpb(64, fn);
   const uint32_t lds = xbuf_off + 2 * fpb * nt * ns * 1024;
   if (lds > kMaxLds) return false;
@@ -278,8 +278,9 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
   p->chains = in->tiles / tpc;
   p->cps = kt / tpc;
   const uint32_t chain_lds = tpc * p->region_words * 2;
-  if (kLutBytes + kCumBytes + chain_lds > kMaxLds) return false;
-  const uint32_t lds_cap = (kMaxLds - kLutBytes - kCumBytes) / chain_lds;
+  const uint32_t tab = tab_bytes_of((int)in->fmt);
+  if (tab + chain_lds > kMaxLds) return false;
+  const uint32_t lds_cap = (kMaxLds - tab) / chain_lds;
   const uint32_t fn = in->tile_n / 16 == 8 ? 8 : 16;
   const uint32_t w1 = fused_max_threads(R, fn, p->mt, 1) / 64;  // one chain per wave
   const uint32_t w2 = fused_max_threads(R, fn, p->mt, 2) / 64;  // two-chain kernels
@@ -303,7 +304,7 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
     const uint64_t rounds = (p->chains + (uint64_t)c * kCUs - 1) / ((uint64_t)c * kCUs);
     const uint32_t half = w2 / 2;
     if (rounds > 1 && half >= 8 && p->cps % 2 == 0 &&
-        2 * (kLutBytes + kCumBytes + 2 * half * chain_lds) <= kMaxLds) {
+        2 * (tab + 2 * half * chain_lds) <= kMaxLds) {
       p->waves = half;
       p->n2 = half;
       c = 2 * half;
@@ -313,7 +314,7 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
   p->threads = 64 * std::max(p->waves, 4u);       // the LUT build uses >= 4 waves
   p->wgs = (p->chains + c - 1) / c;
   p->slots = (p->cps + c - 1) / c + 1;
-  p->lds = kLutBytes + kCumBytes + c * chain_lds;
+  p->lds = tab + c * chain_lds;
   uint32_t rc = in->tile_n;
   while (rc > 16 && (uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) rc /= 2;
   if ((uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) {
@@ -464,6 +465,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
       case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
@@ -506,6 +508,9 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
         break;
       case DGT_FMT_BF16_EXP:
         rc = launch_fused<BF16E>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_BF16_PAIR:
+        rc = launch_fused<BF16P>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       case DGT_FMT_FP8_E4M3:
         rc = launch_fused<FP8>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
@@ -607,7 +612,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   // whole streams when the workgroup's tiles fit LDS, else (R = 64, 128) the ring
   bool ring = false;
   auto lds_for = [&](uint32_t w) {
-    return kLutBytes + kCumBytes + w * ilp * tpc * a.L.region_words * 2;
+    return tab_bytes_of((int)info->fmt) + w * ilp * tpc * a.L.region_words * 2;
   };
   const Staging sg = staging_from_env();
   if (R != 32) {
@@ -628,6 +633,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
     case DGT_FMT_INT4: return launch_decode<INT4>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_INT4_PAIR: return launch_decode<INT4P>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_BF16_EXP: return launch_decode<BF16E>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_PAIR: return launch_decode<BF16P>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     default: break;
@@ -672,10 +678,10 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
                    const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
                    float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_w || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
-  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_EXP) return DGT_E_ARG;
+  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_PAIR) return DGT_E_ARG;
   // same decoded layout and values as the one-symbol-per-weight formats
   if (fmt == DGT_FMT_INT4_PAIR) fmt = DGT_FMT_INT4;
-  if (fmt == DGT_FMT_BF16_EXP) fmt = DGT_FMT_BF16_SPLIT;
+  if (fmt == DGT_FMT_BF16_EXP || fmt == DGT_FMT_BF16_PAIR) fmt = DGT_FMT_BF16_SPLIT;
   if ((tile_n != 128 && tile_n != 256) || n % tile_n || k % 64 || (k / 64) % 2)
     return DGT_E_SHAPE;
   if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;

@@ -40,16 +40,30 @@ constexpr uint32_t kLutBytes = kSlots * 8;
 constexpr uint32_t kCumBytes = 1040;   // (256 + 1) u32, padded
 constexpr uint32_t kSlackWords = 64;   // u16 words of slack after each staged stream
 
-enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5, BF16E = 6 };
+enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5, BF16E = 6, BF16P = 7 };
 
 // formats whose tiles carry one raw byte per weight next to the coded symbol
 template <int FMT>
-__host__ __device__ constexpr bool has_raw_bytes() { return FMT == BF16 || FMT == BF16E; }
+__host__ __device__ constexpr bool has_raw_bytes() {
+  return FMT == BF16 || FMT == BF16E || FMT == BF16P;
+}
 
 // Decode steps per 16-row fragment: a lane's 8 weights of a fragment take 8
-// symbols, or 4 when a symbol codes two int4 weights.
+// symbols, or 4 when a symbol codes two weights.
 template <int FMT>
-__host__ __device__ constexpr int steps_per_frag() { return FMT == INT4P ? 4 : 8; }
+__host__ __device__ constexpr int steps_per_frag() { return (FMT == INT4P || FMT == BF16P) ? 4 : 8; }
+
+// 16-bit symbols (BF16P): the table lists the present symbols only and the
+// decode table carries the symbol's high byte beside the slot offset.
+template <int FMT>
+__host__ __device__ constexpr bool wide_symbols() { return FMT == BF16P; }
+constexpr uint32_t kCumBytesWide = 16400;  // (4096 + 1) u32 {c_s | symbol << 16}, padded
+// LDS bytes of the decode table plus the cumulative table built with it
+__host__ __device__ constexpr uint32_t tab_bytes_of(int fmt) {
+  return kLutBytes + (fmt == BF16P ? kCumBytesWide : kCumBytes);
+}
+template <int FMT>
+__host__ __device__ constexpr uint32_t tab_bytes() { return tab_bytes_of(FMT); }
 // At most this many final steps of a tile decode the initial-state payload.
 constexpr uint32_t kPayloadMax = 16;
 // rANS states a wave lane holds for one chain: two when R = 128.
@@ -127,6 +141,76 @@ __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32
   }
 }
 
+// Slot table from a sparse table of P entries {symbol | f << 16} in symbol
+// order (16-bit symbols): entry .x = f | (symbol & 0xFF) << 24, .y = (slot -
+// c_s) | (symbol >> 8) << 24, so the state update masks .y to 12 bits and the
+// symbol's two bytes are the top bytes of .x and .y.  Every thread sums a
+// contiguous run of entries; a block scan of the run sums gives each run's
+// start; cum[e] = c_e | symbol_e << 16 (cum[P] = 2^12) is then searched per
+// slot as in build_lut.  The decode table's memory serves as scratch for the
+// per-wave sums before it is filled.  Caller synchronises.
+__device__ inline void build_lut_sparse(const uint32_t* table, uint32_t P, u32x2* lut,
+                                        uint32_t* cum) {
+  const uint32_t t = threadIdx.x, B = blockDim.x;
+  const uint32_t lane = t & 63, wave = t >> 6;
+  uint32_t* wsum = reinterpret_cast<uint32_t*>(lut);
+  const uint32_t q = (P + B - 1) / B;
+  const uint32_t e0 = min(t * q, P), e1 = min(e0 + q, P);
+  uint32_t run = 0;
+  for (uint32_t e = e0; e < e1; ++e) run += table[e] >> 16;
+  uint32_t v = run;  // inclusive scan over the wave's threads
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  uint32_t c = v - run;
+  for (uint32_t w = 0; w < wave; ++w) c += wsum[w];
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t en = table[e];
+    cum[e] = c | ((en & 0xFFFFu) << 16);
+    c += en >> 16;
+  }
+  if (t == 0) cum[P] = kSlots;
+  __syncthreads();  // cum complete and the scratch sums read: the table may be written
+  const uint32_t per = (kSlots + B - 1) / B;
+  const uint32_t r0 = t * per, r1 = min(r0 + per, kSlots);
+  uint32_t s_cur = 0, c_lo = 0, c_hi = 0;  // empty range: forces the first search
+  for (uint32_t r = r0; r < r1; ++r) {
+    if (r >= c_hi) {
+      uint32_t lo = 0, hi = P;  // (cum[lo] & 0xFFFF) <= r < (cum[hi] & 0xFFFF)
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if ((cum[mid] & 0xFFFFu) <= r) lo = mid; else hi = mid;
+      }
+      s_cur = cum[lo] >> 16;
+      c_lo = cum[lo] & 0xFFFFu;
+      c_hi = cum[lo + 1] & 0xFFFFu;
+    }
+    u32x2 e;
+    e.x = (c_hi - c_lo) | ((s_cur & 0xFFu) << 24);
+    e.y = (r - c_lo) | ((s_cur >> 8) << 24);
+    lut[r] = e;
+  }
+}
+
+// Table load and decode-table build of a format: the dense table's
+// frequency load is issued early (table_issue) and used by table_build.
+template <int FMT>
+__device__ __forceinline__ uint32_t table_issue(const Layer& L) {
+  if constexpr (wide_symbols<FMT>()) return 0u;
+  else return lut_load_freq(L.table, L.alphabet);
+}
+template <int FMT>
+__device__ __forceinline__ void table_build(uint32_t fq, const Layer& L, u32x2* lut,
+                                            uint32_t* cum) {
+  if constexpr (wide_symbols<FMT>())
+    build_lut_sparse(reinterpret_cast<const uint32_t*>(L.table), L.alphabet, lut, cum);
+  else
+    build_lut(fq, L.alphabet, lut, cum);
+}
+
 // R lane states of one chain: one tile (R = 64 or 128) or two tiles (R = 32).
 // Word positions are byte offsets into the workgroup's LDS; fields marked
 // "uniform" hold the same value on every lane.
@@ -170,8 +254,9 @@ __host__ __device__ constexpr int ring_group_steps(int R) { return (int)kChunkWo
 // states per lane (R = 128) the first states' words come first, then the
 // second states' (interleaving order j = s*128 + p).  CAREFUL also handles the
 // payload switch (x -= L at step == lim, no reads from then on).
-// Returns the table words (decoded symbol in the top byte) per state.
-template <int R, bool CAREFUL, int ILP, bool RING>
+// Returns the table words (decoded symbol in the top byte) per state, or for
+// 16-bit symbols (SYM16) the symbol's two bytes in the low half.
+template <int R, bool CAREFUL, int ILP, bool RING, bool SYM16 = false>
 __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
                                          const uint8_t* __restrict__ lds, uint32_t s,
                                          bool upper_half,
@@ -194,7 +279,8 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
     uint32_t pos = c[i].p0;  // uniform
 #pragma unroll
     for (int h = 0; h < NS; ++h) {
-      xn[i][h] = (e[i][h].x & 0xFFFFFFu) * (x[i][h] >> 12) + e[i][h].y;  // v_mad_u32_u24
+      const uint32_t bias = SYM16 ? (e[i][h].y & 0xFFFu) : e[i][h].y;
+      xn[i][h] = (e[i][h].x & 0xFFFFFFu) * (x[i][h] >> 12) + bias;  // v_mad_u32_u24
       need[i][h] = xn[i][h] < kL;
       if (CAREFUL) need[i][h] = need[i][h] && (s < c[i].lim);
       const uint64_t m = __builtin_amdgcn_ballot_w64(need[i][h]);
@@ -227,7 +313,8 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
     for (int h = 0; h < NS; ++h) {
       const uint32_t v = need[i][h] ? ((xn[i][h] << 16) | w[i][h]) : xn[i][h];
       if (h) c[i].x2 = v; else c[i].x = v;
-      sym[i][h] = e[i][h].x;
+      // 16-bit symbols: [low byte, high byte, 0, 0] from the entry's top bytes
+      sym[i][h] = SYM16 ? __builtin_amdgcn_perm(e[i][h].y, e[i][h].x, 0x0c0c0703u) : e[i][h].x;
     }
 }
 

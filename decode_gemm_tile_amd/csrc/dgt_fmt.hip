@@ -110,7 +110,7 @@ int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bo
 template <>
 int launch_dense<DGT_FMT>(const DenseArgs& d, uint32_t fn, uint32_t mt, uint32_t grid,
                           uint32_t threads, uint32_t lds, hipStream_t st) {
-  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E) {
+  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E || DGT_FMT == BF16P) {
     return DGT_E_UNSUPPORTED;  // their decoded weights are read as INT4 / BF16_SPLIT
   } else {
 #define DGT_DENSE_CASE(FNV, MTV)                                                        \

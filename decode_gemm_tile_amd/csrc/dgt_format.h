@@ -27,13 +27,15 @@ struct HeaderLayout {
                           total = 88, max_tile_words4 = 96, kmax = 100;
 };
 
-inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : 256u; }
-// weights coded per symbol (INT4_PAIR packs two along K)
-inline uint32_t weights_per_symbol(uint32_t fmt) { return fmt == 5 ? 2u : 1u; }
+inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : fmt == 7 ? 65536u : 256u; }
+// formats whose table lists the present symbols only: u32 symbol | f << 16
+inline bool sparse_table(uint32_t fmt) { return fmt == 7; }
+// weights coded per symbol (INT4_PAIR and BF16_PAIR pack two along K)
+inline uint32_t weights_per_symbol(uint32_t fmt) { return (fmt == 5 || fmt == 7) ? 2u : 1u; }
 // symbols per lane per 16-row fragment (8 weights either way)
 inline uint32_t symbols_per_lane(uint32_t fmt) { return 8u / weights_per_symbol(fmt); }
 // formats that store one raw byte per weight beside the coded symbol
-inline bool has_raw(uint32_t fmt) { return fmt == 4 || fmt == 6; }
+inline bool has_raw(uint32_t fmt) { return fmt == 4 || fmt == 6 || fmt == 7; }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

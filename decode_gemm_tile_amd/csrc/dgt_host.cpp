@@ -51,7 +51,7 @@ bool geometry_ok(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tn, uint32_t tk,
 
 bool params_ok(const dgt_params* p) {
   if (!p) return false;
-  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_EXP) return false;
+  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_PAIR) return false;
   if (p->prob_bits < 8 || p->prob_bits > 15) return false;
   return true;
 }
@@ -112,7 +112,7 @@ struct TileOut {
 };
 
 // Encode one tile: symbols in j order (j = step*R + lane).
-void encode_tile(const uint8_t* sym, uint32_t lanes, uint32_t steps, const uint32_t* f,
+void encode_tile(const uint16_t* sym, uint32_t lanes, uint32_t steps, const uint32_t* f,
                  const uint32_t* c, uint32_t prob_bits, TileOut* out) {
   const uint64_t M = 1ull << prob_bits;
   const uint64_t y_limit = (1ull << 32) - dgt::kStateL;
@@ -187,7 +187,8 @@ size_t dgt_compress_bound(const dgt_params* p) {
   const uint64_t tiles = (uint64_t)(p->n / p->tile_n) * (p->k / p->tile_k);
   const uint64_t T = (uint64_t)p->tile_n * p->tile_k;
   const uint32_t alpha = dgt::alphabet_of(p->fmt);
-  uint64_t b = dgt::kHeaderBytes + dgt::align_up(2 * alpha, 16) +
+  const uint64_t table = dgt::sparse_table(p->fmt) ? 4ull << p->prob_bits : 2ull * alpha;
+  uint64_t b = dgt::kHeaderBytes + dgt::align_up(table, 16) +
                dgt::align_up(4 * (tiles + 1), 16) + dgt::align_up(tiles, 16);
   b += tiles * (4ull * p->lanes + 2 * T + 4) + 16;
   if (dgt::has_raw(p->fmt)) b += tiles * T + 16;
@@ -206,10 +207,16 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   const uint32_t ks = k / wps, tks = tk / wps;
   const uint64_t NS = (uint64_t)n * ks;
 
-  // symbolise: coded byte per symbol (+ raw low byte for the bf16 split)
-  std::vector<uint8_t> sym(NS);
+  // symbolise: coded symbol (+ raw low byte for the bf16 splits)
+  std::vector<uint16_t> sym(NS);
   std::vector<uint8_t> raw;
-  if (fmt == DGT_FMT_INT4_PAIR) {
+  if (fmt == DGT_FMT_BF16_PAIR) {
+    raw.resize(NK);
+    const uint16_t* b = static_cast<const uint16_t*>(w);
+    for (uint64_t i = 0; i < NS; ++i)
+      sym[i] = (uint16_t)((b[2 * i] >> 8) | (b[2 * i + 1] & 0xFF00u));
+    for (uint64_t i = 0; i < NK; ++i) raw[i] = (uint8_t)(b[i] & 0xFF);
+  } else if (fmt == DGT_FMT_INT4_PAIR) {
     const uint8_t* q = static_cast<const uint8_t*>(w);
     for (uint64_t i = 0; i < NS; ++i) {
       const uint8_t a = q[2 * i], b = q[2 * i + 1];
@@ -231,7 +238,8 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
       raw[i] = (uint8_t)(((b[i] >> 8) & 0x80) | (b[i] & 0x7F));
     }
   } else {
-    std::memcpy(sym.data(), w, NK);
+    const uint8_t* q = static_cast<const uint8_t*>(w);
+    for (uint64_t i = 0; i < NK; ++i) sym[i] = q[i];
     if (fmt == DGT_FMT_INT4)
       for (uint64_t i = 0; i < NK; ++i)
         if (sym[i] > 15) return DGT_E_ALPHABET;
@@ -267,7 +275,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   std::vector<TileOut> enc(tiles);
   std::atomic<uint64_t> next{0};
   auto work = [&]() {
-    std::vector<uint8_t> ts(TS);
+    std::vector<uint16_t> ts(TS);
     for (;;) {
       const uint64_t t = next.fetch_add(1);
       if (t >= tiles) break;
@@ -291,8 +299,18 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
     off[t + 1] = off[t] + (uint32_t)len4;
     max_len = std::max<uint32_t>(max_len, (uint32_t)len4);
   }
+  // the table: dense u16 f[alphabet], or (sparse formats) u32 symbol | f << 16
+  // for the present symbols in symbol order; the header's alphabet field then
+  // holds the entry count
+  uint32_t table_entries = alpha;
+  size_t table_bytes = 2 * (size_t)alpha;
+  if (dgt::sparse_table(fmt)) {
+    table_entries = 0;
+    for (uint32_t s = 0; s < alpha; ++s) table_entries += f[s] ? 1 : 0;
+    table_bytes = 4 * (size_t)table_entries;
+  }
   const size_t table_off = dgt::kHeaderBytes;
-  const size_t index_off = dgt::align_up(table_off + 2 * alpha, 16);
+  const size_t index_off = dgt::align_up(table_off + table_bytes, 16);
   const size_t ktab_off = dgt::align_up(index_off + 4 * (tiles + 1), 16);
   const size_t streams_off = dgt::align_up(ktab_off + tiles, 16);
   const size_t streams_end = streams_off + 4 * (size_t)off[tiles];
@@ -317,7 +335,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   put<uint32_t>(o, HeaderLayout::tile_k, tk);
   put<uint32_t>(o, HeaderLayout::lanes, R);
   put<uint32_t>(o, HeaderLayout::prob_bits, pb);
-  put<uint32_t>(o, HeaderLayout::alphabet, alpha);
+  put<uint32_t>(o, HeaderLayout::alphabet, table_entries);
   put<uint32_t>(o, HeaderLayout::tiles, (uint32_t)tiles);
   put<uint64_t>(o, HeaderLayout::table_off, table_off);
   put<uint64_t>(o, HeaderLayout::index_off, index_off);
@@ -327,7 +345,13 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   put<uint64_t>(o, HeaderLayout::total, total);
   put<uint32_t>(o, HeaderLayout::max_tile_words4, max_len);
   put<uint32_t>(o, HeaderLayout::kmax, dgt::kKmax);
-  for (uint32_t s = 0; s < alpha; ++s) put<uint16_t>(o, table_off + 2 * s, (uint16_t)f[s]);
+  if (dgt::sparse_table(fmt)) {
+    size_t e = 0;
+    for (uint32_t s = 0; s < alpha; ++s)
+      if (f[s]) put<uint32_t>(o, table_off + 4 * e++, s | (f[s] << 16));
+  } else {
+    for (uint32_t s = 0; s < alpha; ++s) put<uint16_t>(o, table_off + 2 * s, (uint16_t)f[s]);
+  }
   for (uint64_t t = 0; t <= tiles; ++t) put<uint32_t>(o, index_off + 4 * t, off[t]);
   for (uint64_t t = 0; t < tiles; ++t) o[ktab_off + t] = (uint8_t)enc[t].k;
   for (uint64_t t = 0; t < tiles; ++t) {
@@ -375,12 +399,16 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   in.total_bytes = get<uint64_t>(b, HeaderLayout::total);
   in.max_tile_words4 = get<uint32_t>(b, HeaderLayout::max_tile_words4);
   in.kmax = get<uint32_t>(b, HeaderLayout::kmax);
-  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_EXP) return DGT_E_FORMAT;
+  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_PAIR) return DGT_E_FORMAT;
   if (in.flags != 0) return DGT_E_FORMAT;
   if (in.total_bytes != size) return DGT_E_CORRUPT;
   if (!geometry_ok(in.fmt, in.n, in.k, in.tile_n, in.tile_k, in.lanes)) return DGT_E_CORRUPT;
   if (in.prob_bits < 8 || in.prob_bits > 15) return DGT_E_CORRUPT;
-  if (in.alphabet != dgt::alphabet_of(in.fmt)) return DGT_E_CORRUPT;
+  const bool sparse = dgt::sparse_table(in.fmt);
+  if (sparse ? (in.alphabet == 0 || in.alphabet > (1u << in.prob_bits))
+             : in.alphabet != dgt::alphabet_of(in.fmt))
+    return DGT_E_CORRUPT;
+  const uint64_t table_bytes = (sparse ? 4ull : 2ull) * in.alphabet;
   const uint64_t tiles = (uint64_t)(in.n / in.tile_n) * (in.k / in.tile_k);
   if (tiles != in.tiles) return DGT_E_CORRUPT;
   const uint64_t T = (uint64_t)in.tile_n * in.tile_k;
@@ -388,12 +416,22 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   if (in.kmax > 255) return DGT_E_CORRUPT;
   // section bounds and alignment
   if (in.table_off < dgt::kHeaderBytes || in.table_off % 16 ||
-      in.table_off + 2ull * in.alphabet > in.index_off || in.index_off % 16 ||
+      in.table_off + table_bytes > in.index_off || in.index_off % 16 ||
       in.index_off + 4 * (tiles + 1) > in.ktab_off || in.ktab_off % 16 ||
       in.ktab_off + tiles > in.streams_off || in.streams_off % 16 || in.streams_off > size)
     return DGT_E_CORRUPT;
   uint64_t fsum = 0;
-  for (uint32_t s = 0; s < in.alphabet; ++s) fsum += get<uint16_t>(b, in.table_off + 2 * s);
+  if (sparse) {
+    int64_t prev_sym = -1;
+    for (uint32_t e = 0; e < in.alphabet; ++e) {
+      const uint32_t v = get<uint32_t>(b, in.table_off + 4 * e);
+      if ((int64_t)(v & 0xFFFF) <= prev_sym || (v >> 16) == 0) return DGT_E_CORRUPT;
+      prev_sym = v & 0xFFFF;
+      fsum += v >> 16;
+    }
+  } else {
+    for (uint32_t s = 0; s < in.alphabet; ++s) fsum += get<uint16_t>(b, in.table_off + 2 * s);
+  }
   if (fsum != (1ull << in.prob_bits)) return DGT_E_CORRUPT;
   uint32_t prev = get<uint32_t>(b, in.index_off), maxlen = 0;
   if (prev != 0) return DGT_E_CORRUPT;

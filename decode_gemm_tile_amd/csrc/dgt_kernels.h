@@ -82,6 +82,8 @@ struct OperandTraits<INT4P> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<BF16E> { static constexpr int xbytes = 2; };
 template <>
+struct OperandTraits<BF16P> { static constexpr int xbytes = 2; };
+template <>
 struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<FP8> { static constexpr int xbytes = 2; };  // e4m3 widened to bf16
@@ -123,7 +125,7 @@ template <int FMT>
 __device__ __forceinline__ BOp finish_b(const uint32_t (&q)[4], u32x2 raw, float sc,
                                         float nsc8) {
   BOp b;
-  if constexpr (FMT == BF16) {
+  if constexpr (FMT == BF16 || FMT == BF16P) {  // q[i]: the high bytes of weights 2i, 2i+1
     b.v.x = __builtin_amdgcn_perm(q[0], raw.x, 0x05010400u);
     b.v.y = __builtin_amdgcn_perm(q[1], raw.x, 0x05030402u);
     b.v.z = __builtin_amdgcn_perm(q[2], raw.y, 0x05010400u);
@@ -492,7 +494,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         }
         if (i == kPrefetchStep) prefetch();
         uint32_t sy[ILP][NS];
-        step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
+        step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
   const Layer& L = a.L;
   constexpr uint32_t TPC = R == 32 ? 2 : 1;  // tiles per chain
 
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   Staged stg[2];   // whole streams
   Ring rg[2];      // ring: chunk 0 (c0) now, later chunks through the ring
   uint32_t c0[2][4];
-  const uint32_t fq = lut_load_freq(L.table, L.alphabet);
+  const uint32_t fq = table_issue<FMT>(L);
   const uint32_t sub_lane = R != 32 ? lane : half_lane, sub_size = R != 32 ? 64u : 32u;
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
   // 3) write the first words to LDS.  Both chain slots always load (a missing
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
 #pragma unroll
     for (int c = 0; c < 2; ++c) stage_load(stg[c], L.lanes, sub_lane, sub_size, kPreHalf, kPre);
   }
-  build_lut(fq, L.alphabet, lut, cum);
+  table_build<FMT>(fq, L, lut, cum);
   // the payload counts are read after the LUT build: a wait for them then
   // costs nothing (the staged streams are needed next anyway)
 #pragma unroll
@@ -608,7 +610,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     if (c < (int)nch) {
       const uint32_t ra = (cw + c) * TPC * L.region_words;
       if constexpr (RING) {
-        ring_start(rg[c], ch[c], smem, kLutBytes + kCumBytes + 2 * ra, lane, c0[c]);
+        ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * ra, lane, c0[c]);
       } else {
         const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
         cstart[c] = (R == 32 && upper) ? rb : ra;
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
         const uint32_t mine = 2 * stg[c].words4;
         const uint32_t na = uniform(mine);
         const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-        const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
+        const uint32_t ba = tab_bytes<FMT>() + 2 * ra, bb = tab_bytes<FMT>() + 2 * rb;
         ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
         ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
       }
@@ -795,7 +797,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   const Layer& L = a.L;
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
   uint8_t* xbuf = smem + x.xbuf_off;
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + x.xbuf_off - 16);
   const uint32_t lane = lane_id();
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   float out_scale = 1.f;
   if constexpr (FMT == FP8)
     out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
-  const uint32_t fq = lut_load_freq(L.table, L.alphabet);
+  const uint32_t fq = table_issue<FMT>(L);
   const uint32_t b0 = blockIdx.x * x.bpw, b1 = min(b0 + x.bpw, x.batches);
   floatx4 acc[FN][MTW];
 #pragma unroll
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       ch[c].x = L.streams[L.index[tj[c]] + lane];
       ch[c].x2 = (R == 128) ? L.streams[L.index[tj[c]] + 64 + lane] : 0u;
     }
-    if (b == b0) build_lut(fq, L.alphabet, lut, cum);
+    if (b == b0) table_build<FMT>(fq, L, lut, cum);
 #pragma unroll
     for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tj[c]];
     __syncthreads();  // LUT complete; the previous batch's fragment reads are done
@@ -839,7 +841,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t region = (wave * ILP + c) * L.region_words;
-      const uint32_t base = kLutBytes + kCumBytes + 2 * region;
+      const uint32_t base = tab_bytes<FMT>() + 2 * region;
       if constexpr (RING) {
         ring_start(rg[c], ch[c], smem, base, lane, c0[c]);
         ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
@@ -926,7 +928,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
             }
             if (i == kPrefetchStep) prefetch();
             uint32_t sy[ILP][NS];
-            step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, false, sy);
+            step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, false, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c)
 #pragma unroll
@@ -1003,7 +1005,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + kLutBytes + kCumBytes);
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
   const Layer& L = a.L;
   constexpr uint32_t TPC = R == 32 ? 2 : 1;
   constexpr int NS = states_per_lane(R);
@@ -1021,7 +1023,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   Ring rg[ILP];     // ring
   uint32_t c0[ILP][4];
   const uint32_t region0 = wave * ILP * TPC * L.region_words;
-  const uint32_t fq = lut_load_freq(L.table, L.alphabet);
+  const uint32_t fq = table_issue<FMT>(L);
   // every wave issues the same loads (an idle wave repeats the last id) so
   // the LUT build waits for the table alone
 #pragma unroll
@@ -1040,7 +1042,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     ch[c].x = L.streams[L.index[t_l] + (R == 32 ? half_lane : lane)];
     ch[c].x2 = (R == 128) ? L.streams[L.index[t_l] + 64 + lane] : 0u;
   }
-  build_lut(fq, L.alphabet, lut, cum);
+  table_build<FMT>(fq, L, lut, cum);
 #pragma unroll
   for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
   __syncthreads();  // LUT complete; each wave's staged stream is private to it
@@ -1049,7 +1051,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   for (int c = 0; c < ILP; ++c) {
     const uint32_t ra = region0 + c * TPC * L.region_words;
     if constexpr (RING) {
-      ring_start(rg[c], ch[c], smem, kLutBytes + kCumBytes + 2 * ra, lane, c0[c]);
+      ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * ra, lane, c0[c]);
       ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
       rg[c].cc = uniform(rg[c].cc);
       rg[c].nchunks = uniform(rg[c].nchunks);
@@ -1059,7 +1061,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
                                          R != 32 ? lane : half_lane, R != 32 ? 64u : 32u);
       const uint32_t na = uniform(mine);
       const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-      const uint32_t ba = kLutBytes + kCumBytes + 2 * ra, bb = kLutBytes + kCumBytes + 2 * rb;
+      const uint32_t ba = tab_bytes<FMT>() + 2 * ra, bb = tab_bytes<FMT>() + 2 * rb;
       ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
       ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
     }
@@ -1085,7 +1087,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
         }
       }
       uint32_t sy[ILP][NS];
-      step_all<R, decltype(careful)::value, ILP, RING>(ch, lut, smem, s0 + i, upper, sy);
+      step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
       for (int c = 0; c < ILP; ++c)
 #pragma unroll

@@ -37,16 +37,20 @@
  *     u32 flags, u32 N, K, tile_n, tile_k, lanes R, prob_bits, alphabet,
  *     tiles; u64 table, index, ktab, streams, raw offsets, u64 total size;
  *     u32 max tile length (4-byte units), u32 kmax (16); zero padding.
- *   table  u16 f[alphabet], sum f = 2^prob_bits (shared by all tiles).
+ *   table  u16 f[alphabet], sum f = 2^prob_bits (shared by all tiles);
+ *          BF16_PAIR (alphabet 65536): u32 symbol | f << 16 for each symbol
+ *          with f > 0, in increasing symbol order, and the header's alphabet
+ *          field holds the number of entries.
  *   index  u32 off[tiles+1]: tile t's stream starts at streams + 4*off[t].
  *   ktab   u8 k[tiles]: initial-state payload steps of each tile.
  *   streams per tile: R u32 lane states, u16 words in decode order, zero pad.
- *   raw    (BF16_SPLIT, BF16_EXP) T raw bytes per tile, lane-major.
+ *   raw    (BF16_SPLIT, BF16_EXP, BF16_PAIR) T raw bytes per tile, lane-major.
  * Tile t = bn*(K/tile_k) + bk covers W rows bn*tile_n.. and columns
  * bk*tile_k..  Inside a tile, symbol j = s*R + p (step s, lane p) with
  * s = 8g + e, fragment g = fk*(tile_n/16) + fn: lane p decodes row
  * 16fn + p%16, column fk*R/2 + 8*(p/16) + e.  rANS: state in [2^16, 2^32),
- * INT4_PAIR codes symbol c of a row for the weight pair (2c, 2c+1) and lays
+ * INT4_PAIR (and BF16_PAIR, whose symbol is the two weights' high bytes)
+ * codes symbol c of a row for the weight pair (2c, 2c+1) and lays
  * out a tile's tile_n*tile_k/2 symbols the same way with 4 symbols per lane
  * per fragment (s = 4g + e, pair column fk*R/4 + 4*(p/16) + e), so a lane's
  * 4 symbols are again its 8 consecutive weights of one row.
@@ -77,8 +81,11 @@ enum dgt_format {
   DGT_FMT_BF16_SPLIT = 4, /* bf16: high byte coded, low byte stored raw */
   DGT_FMT_INT4_PAIR = 5,  /* INT4 weights and scales, coded two per symbol:
                              q[n,2c] | q[n,2c+1] << 4 (alphabet 256) */
-  DGT_FMT_BF16_EXP = 6    /* bf16: exponent (bits 14..7) coded, sign and mantissa
+  DGT_FMT_BF16_EXP = 6,   /* bf16: exponent (bits 14..7) coded, sign and mantissa
                              stored raw as one byte (sign << 7 | mantissa) */
+  DGT_FMT_BF16_PAIR = 7   /* bf16 byte split with the high bytes of two weights
+                             adjacent along K coded as one 16-bit symbol
+                             hi[n,2c] | hi[n,2c+1] << 8; low bytes raw */
 };
 
 enum dgt_status {

@@ -6,6 +6,9 @@ import decode_gemm_tile_amd as dgt
 from oracle import gemm as ogemm
 
 
+BF16_FORMATS = (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP, dgt.DGT_FMT_BF16_PAIR)
+
+
 def to_dev(arr, dtype=None):
     import torch
     a = np.ascontiguousarray(arr)
@@ -27,14 +30,14 @@ def codes_as_u8_or_u16(fmt, codes):
     c = np.asarray(codes)
     if fmt == dgt.DGT_FMT_INT8:
         return c.astype(np.int8).view(np.uint8)
-    if fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
+    if fmt in BF16_FORMATS:
         return c.astype(np.uint16)
     return c.astype(np.uint8)
 
 
 def decoded_to_numpy(fmt, out):
     a = out.cpu().numpy()
-    if fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
+    if fmt in BF16_FORMATS:
         return a.view(np.uint16)
     return a
 

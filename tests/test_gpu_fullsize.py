@@ -20,13 +20,13 @@ from oracle import freq as ofreq
 from oracle import gemm as ogemm
 from oracle import order as oorder
 from oracle import rans as orans
-from tests.gpu_util import codes_as_u8_or_u16, to_dev, x_dev
+from tests.gpu_util import BF16_FORMATS, codes_as_u8_or_u16, to_dev, x_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 NAMES = ["int8_1024", "int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405",
          "int4_4096_pair", "int4_ffn405_pair", "bf16_mlp_exp", "int4_4096_r128",
-         "fp8_8192_r128", "bf16_mlp_r128"]
+         "fp8_8192_r128", "bf16_mlp_r128", "bf16_mlp_pair", "bf16_ffn405_pair"]
 _CACHE = {}
 
 
@@ -49,7 +49,7 @@ def test_fullsize_decode_bit_exact(name):
     status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
     out = dgt.dgt_decode_tiles(layer, status=status)
     ref = to_dev(codes_as_u8_or_u16(wl.fmt, d["codes"]))
-    if wl.fmt in (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP):
+    if wl.fmt in BF16_FORMATS:
         ref = ref.view(torch.int16)
     torch.cuda.synchronize()
     assert torch.equal(out.view(ref.dtype), ref)

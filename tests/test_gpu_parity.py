@@ -21,6 +21,7 @@ TOL = 1e-5
 
 F8, F4, FE, FB, FP, FX = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
                           dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_INT4_PAIR, dgt.DGT_FMT_BF16_EXP)
+FH = dgt.DGT_FMT_BF16_PAIR
 
 # (fmt, N, K, tile_n, tile_k, lanes, seed)
 CASES = [
@@ -46,6 +47,12 @@ CASES = [
     (FB, 256, 4096, 128, 64, 128, 19),    # several workgroups per strip
     (FP, 256, 1024, 128, 64, 128, 20),
     (FX, 384, 1024, 128, 64, 128, 22),
+    # bf16 byte split with high-byte pairs (16-bit symbols)
+    (FH, 384, 1024, 128, 64, 64, 23),
+    (FH, 512, 448, 256, 64, 64, 24),      # tile_n 256, 7 k-tiles
+    (FH, 256, 256, 128, 32, 32, 25),      # two tiles per wave
+    (FH, 256, 4096, 128, 64, 64, 26),     # several workgroups per strip
+    (FH, 384, 1024, 128, 64, 128, 27),    # two states per lane
 ]
 
 
@@ -128,6 +135,9 @@ XM_CASES = [
     (F4, 256, 2048, 128, 64, 128, 57),
     (FP, 512, 1024, 256, 64, 128, 58),
     (FX, 256, 2048, 128, 64, 128, 59),
+    (FH, 384, 2048, 128, 64, 64, 62),     # bf16 high-byte pairs
+    (FH, 512, 1024, 256, 64, 64, 63),
+    (FH, 256, 2048, 128, 64, 128, 64),
 ]
 
 
@@ -174,6 +184,7 @@ STAGING_CASES = [
     (FE, 512, 1024, 256, 64, 128, 74),
     (FP, 256, 2048, 128, 64, 128, 75),
     (F8, 256, 2048, 128, 64, 128, 76),
+    (FH, 384, 4096, 128, 64, 64, 77),
 ]
 
 
@@ -248,7 +259,7 @@ def test_exact_integer_case():
 
 
 @pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256),
-                                    (FP, 128), (FX, 128)])
+                                    (FP, 128), (FX, 128), (FH, 128)])
 @pytest.mark.parametrize("m", [1, 16, 64])
 def test_dense_baseline_matches_oracle(fmt, tn, m):
     import torch

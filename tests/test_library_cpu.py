@@ -53,6 +53,11 @@ CASES = [
     (dgt.DGT_FMT_BF16_SPLIT, 256, 128, 128, 64, 128, 17),
     (dgt.DGT_FMT_INT4_PAIR, 256, 256, 128, 64, 128, 18),
     (dgt.DGT_FMT_BF16_EXP, 256, 128, 128, 64, 128, 19),
+    # bf16 high-byte pairs (16-bit symbols, sparse table)
+    (dgt.DGT_FMT_BF16_PAIR, 256, 128, 128, 64, 64, 20),
+    (dgt.DGT_FMT_BF16_PAIR, 512, 128, 256, 64, 64, 21),
+    (dgt.DGT_FMT_BF16_PAIR, 128, 128, 128, 32, 32, 22),
+    (dgt.DGT_FMT_BF16_PAIR, 256, 128, 128, 64, 128, 23),
 ]
 
 
@@ -116,7 +121,16 @@ def test_layer_info_rejects_corruption():
     c = bytearray(b); io = info.index_off
     c[io + 4:io + 8] = (0).to_bytes(4, "little"); cases.append((c, -6))     # index order
     c = bytearray(b); c[info.ktab_off] = 200; cases.append((c, -6))         # ktab range
-    c = bytearray(b); c[8] = 7; cases.append((c, -5))                       # format id
+    c = bytearray(b); c[8] = 9; cases.append((c, -5))                       # format id
+    # sparse table (bf16 high-byte pairs): order, zero frequency, entry count
+    d7 = workloads.random_small(dgt.DGT_FMT_BF16_PAIR, 256, 128, seed=12)
+    b7 = bytearray(dgt.dgt_compress_layer(dgt.DGT_FMT_BF16_PAIR, d7["codes"], 128, 64, 64))
+    i7 = dgt.dgt_layer_info(bytes(b7))
+    t0 = i7.table_off
+    c = bytearray(b7); c[t0:t0 + 4], c[t0 + 4:t0 + 8] = b7[t0 + 4:t0 + 8], b7[t0:t0 + 4]
+    cases.append((c, -6))                                                   # symbol order
+    c = bytearray(b7); c[t0 + 2:t0 + 4] = (0).to_bytes(2, "little"); cases.append((c, -6))
+    c = bytearray(b7); c[40:44] = (5000).to_bytes(4, "little"); cases.append((c, -6))
     for blob, code in cases:
         with pytest.raises(dgt.DgtError) as e:
             dgt.dgt_layer_info(bytes(blob))
