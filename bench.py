@@ -122,7 +122,15 @@ def cpu_baseline(d, wl, blob):
                             h["raw_off"]).reshape(len(tiles), -1)
         from oracle import order
         rows = strips * wl.tile_n
-        hi = order.scatter_tiles(syms.astype(np.uint8), rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes)
+        if wl.fmt == 7:  # high-byte pairs: symbol = hi[2c] | hi[2c+1] << 8
+            pairs = order.scatter_tiles(syms.astype(np.uint16), rows, wl.k // 2, wl.tile_n,
+                                        wl.tile_k // 2, wl.lanes, epl=4)
+            hi = np.empty((rows, wl.k), np.uint16)
+            hi[:, 0::2] = pairs & 0xFF
+            hi[:, 1::2] = pairs >> 8
+        else:
+            hi = order.scatter_tiles(syms.astype(np.uint8), rows, wl.k, wl.tile_n, wl.tile_k,
+                                     wl.lanes)
         lo = order.scatter_tiles(raw, rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes, raw=True)
         w = (hi.astype(np.uint16) << 8) | lo
         y = ogemm.gemm_fp64(numerics.bf16_bits_to_f64(d["x"][:1]), numerics.bf16_bits_to_f64(w))
@@ -159,8 +167,8 @@ def main():
     blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
     encode_s = time.perf_counter() - t0
     info = dgt.dgt_layer_info(blob)
-    wide = wl.fmt in (4, 6)  # bf16 layers: one uint16 code per weight
-    sym = (np.asarray(d["codes"]) >> 8).astype(np.uint8) if wl.fmt == 4 else None
+    wide = wl.fmt in (4, 6, 7)  # bf16 layers: one uint16 code per weight
+    sym = (np.asarray(d["codes"]) >> 8).astype(np.uint8) if wl.fmt in (4, 7) else None
     h_hi = oentropy.empirical_entropy(sym, 256) if sym is not None else None
 
     copies = max(2, math.ceil(ROTATE_BYTES / len(blob)))
@@ -183,7 +191,7 @@ def main():
     dist = launch_distribution(fused, 50, stream)
     nk = wl.n * wl.k
     # decoded-weight bytes at the format's storage width (int4 half a byte)
-    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0}[wl.fmt]
+    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0, 7: 2.0}[wl.fmt]
     value = decoded_bytes / (ms * 1e-3) / 1e9
     alg_bytes = len(blob) + m * wl.k * 2 + m * wl.n * 4
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -291,21 +299,30 @@ def main():
                 ablation["m%d" % mm]["fused_speedup_vs_two_stage_vendor"] = round(ms_tv / ms_fused, 3)
         secondary["ablation"] = ablation
         del wd, dec
-        # the same layer with two rANS states per lane (R = 128): bits and time
+        # the same layer in the other codings of its family: bits and time
+        variants = []
+        if wl.fmt in (4, 7) and wl.lanes == 64:
+            other = 4 if wl.fmt == 7 else 7
+            variants.append(("one_high_byte_per_symbol" if other == 4 else "high_byte_pairs",
+                             other, 64))
         if wl.lanes == 64 and wl.tile_n % 32 == 0:
-            blob2 = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, 128)
+            variants.append(("two_states_per_lane", wl.fmt, 128))
+        for vname, vfmt, vlanes in variants:
+            blob2 = dgt.dgt_compress_layer(vfmt, d["codes"], wl.tile_n, wl.tile_k, vlanes)
             c2 = max(2, math.ceil(ROTATE_BYTES / len(blob2)))
             l2 = [dgt.DeviceLayer(blob2, dev) for _ in range(c2)]
-            r128 = {"bits_per_weight": round(dgt.dgt_layer_info(blob2).bits_per_weight, 4)}
+            var = {"fmt": vfmt, "lanes": vlanes,
+                   "bits_per_weight": round(dgt.dgt_layer_info(blob2).bits_per_weight, 4)}
             for mm, xm_ in ((1, x1), (m2, x2)):
                 wsr = dgt.alloc_workspace(dgt.dgt_gemm_workspace(l2[0], mm), dev)
                 yr = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
-                r128["fused_m%d_ms" % mm] = round(timed(
+                var["fused_m%d_ms" % mm] = round(timed(
                     lambda i: dgt.dgt_fused_decode_gemm(l2[i % c2], xm_, scales=scales,
                                                         w_scale=d["w_scale"], y=yr, ws=wsr,
                                                         stream=stream),
                     reps, 3, stream), 4)
-            secondary["two_states_per_lane"] = r128
+            var["decoded_gbs_m1"] = round(decoded_bytes / (var["fused_m1_ms"] * 1e-3) / 1e9, 3)
+            secondary[vname] = var
             del l2
     result["secondary"] = secondary
 
@@ -317,7 +334,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = a.numel()
 
-    if not args.no_cpu_baseline and wl.fmt == 4:
+    if not args.no_cpu_baseline and wl.fmt in (4, 7):
         result["cpu_baseline"] = cpu_baseline(d, wl, blob)
     print(json.dumps(result))
 
