@@ -13,6 +13,9 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "../../include/dgt.h"
 #include "dgt_format.h"
@@ -193,6 +196,7 @@ int device_supported(const dgt_info* in) {
 struct FusedPlan {
   uint32_t ring, region_words;
   uint32_t mt, mix, waves, threads, cpw, n2, chains, cps, wgs, slots, strips, red_cols, lds;
+  uint32_t rounds, red_off;
   uint32_t m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
   // large-M variant (fragments shared through LDS): used when xm != 0
@@ -214,6 +218,8 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
 // of rows that each decode the whole layer.  Needs R = 64 or 128 and k-tiles
 // per strip divisible by the workgroup's wave count.
 bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
+  p->rounds = 1;
+  p->red_off = 0;
   const uint32_t fn = in->tile_n / 16;
   if (in->lanes == 32 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
   const uint32_t ns = in->lanes == 128 ? 2 : 1;  // operands per wave and fragment
@@ -264,7 +270,38 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
 // one pass is handled in chunks of m_chunk rows.  Chains per workgroup C is
 // the layer's chains over the CUs (one round) when the wave cap allows it;
 // beyond the cap the first n2 waves take two chains each (MIX kernels).
-bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, bool* lds_bound) {
+// Workgroups of the multi-round kernel a CU holds at once (its registers and
+// LDS decide); 1 when the runtime cannot tell.  Cached per kernel and shape.
+uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, bool mix, uint32_t threads,
+                              uint32_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<uint32_t, uint32_t, uint32_t, bool, uint32_t, uint32_t>, uint32_t> memo;
+  const auto key = std::make_tuple(in->fmt, in->lanes, fn, mix, threads, lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  GemmArgs a{};
+  int n = 0, rc = DGT_E_ARG;
+  switch (in->fmt) {
+    case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    default: break;
+  }
+  const uint32_t v = (rc == DGT_OK && n > 0) ? (uint32_t)n : 1u;
+  std::lock_guard<std::mutex> g(mu);
+  memo[key] = v;
+  return v;
+}
+
+bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_env, FusedPlan* p,
+                    bool* lds_bound) {
   p->xm = 0;
   p->ring = ring ? 1 : 0;
   p->region_words = region_words_of(in, ring);
@@ -314,6 +351,8 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
   p->threads = 64 * std::max(p->waves, 4u);       // the LUT build uses >= 4 waves
   p->wgs = (p->chains + c - 1) / c;
   p->slots = (p->cps + c - 1) / c + 1;
+  p->rounds = 1;
+  p->red_off = 0;
   p->lds = tab + c * chain_lds;
   uint32_t rc = in->tile_n;
   while (rc > 16 && (uint64_t)p->waves * p->m_chunk * rc * 4 > p->lds) rc /= 2;
@@ -322,6 +361,31 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p, boo
     if (p->lds > kMaxLds) return false;
   }
   p->red_cols = rc;
+  // Layers that take several rounds of workgroups per CU run them inside
+  // each workgroup (k_fused_rounds): the LUT is built once and a strip's
+  // partial sums leave the workgroup once.  Ring staging, 16-row blocks of X,
+  // full rounds inside one strip (cpw divides the units per strip).  The
+  // reduction buffer then sits after the tables, over the rings.
+  if (ring && p->mt == 1 && R != 32 && p->cps % c == 0) {
+    uint32_t rc2 = in->tile_n;
+    while (rc2 > 16 && (uint64_t)p->waves * p->m_chunk * rc2 * 4 > c * chain_lds) rc2 /= 2;
+    const uint32_t lds2 = tab + std::max<uint32_t>(c * chain_lds, p->waves * p->m_chunk * rc2 * 4);
+    const uint32_t wg_rounds = p->wgs;
+    uint32_t rounds = rounds_env;
+    if (rounds == 0) {
+      const uint32_t per_cu = rounds_blocks_per_cu(in, fn, p->mix != 0, p->threads, lds2);
+      rounds = (wg_rounds + kCUs * per_cu - 1) / (kCUs * per_cu);
+    }
+    if (rounds > 1 && lds2 <= kMaxLds) {
+      const uint32_t cwg = c * rounds;
+      p->rounds = rounds;
+      p->wgs = (p->chains + cwg - 1) / cwg;
+      p->slots = (p->cps + cwg - 1) / cwg + 1;
+      p->red_off = tab;
+      p->lds = lds2;
+      p->red_cols = rc2;
+    }
+  }
   size_t off = dgt::align_up((size_t)p->strips * 4, 256);
   p->part_off = off;
   p->part_bytes = (size_t)p->strips * p->slots * p->m_chunk * in->tile_n * 4;
@@ -347,24 +411,35 @@ Staging staging_from_env() {
 // the ring when LDS would cap the chains per CU or workgroups come in several
 // rounds (each waits for one chunk instead of its whole streams to decode).
 // A forced staging that cannot serve the layer falls back to the choice.
-bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg) {
+// rounds: 0 = chosen per layer, else forced rounds per workgroup of the
+// register path (where cpw divides the units per strip).
+bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg, uint32_t rounds) {
   const bool r64 = in->lanes != 32;
   bool unused = false;
   if (sg == kRing && r64) {
     if (plan_fused_xm(in, m, true, p)) return true;
-    if (plan_fused_reg(in, m, true, p, &unused)) return true;
+    if (plan_fused_reg(in, m, true, rounds, p, &unused)) return true;
   }
   if (sg == kWhole) {
     if (plan_fused_xm(in, m, false, p)) return true;
-    if (plan_fused_reg(in, m, false, p, &unused)) return true;
+    if (plan_fused_reg(in, m, false, rounds, p, &unused)) return true;
   }
   if (plan_fused_xm(in, m, false, p)) return true;
   if (r64 && plan_fused_xm(in, m, true, p)) return true;
   bool lds_bound = false;
-  const bool whole = plan_fused_reg(in, m, false, p, &lds_bound);
+  const bool whole = plan_fused_reg(in, m, false, rounds, p, &lds_bound);
   if (!r64) return whole;
-  if (whole && !lds_bound && p->wgs <= kCUs) return true;
-  return plan_fused_reg(in, m, true, p, &unused);
+  if (whole && !lds_bound && p->wgs * p->rounds <= kCUs) return true;
+  return plan_fused_reg(in, m, true, rounds, p, &unused);
+}
+
+// Rounds per workgroup of the register path, forced by the environment
+// variable DGT_ROUNDS (a positive count; results are identical), else 0.
+uint32_t rounds_from_env() {
+  const char* v = std::getenv("DGT_ROUNDS");
+  if (!v) return 0;
+  const long r = std::strtol(v, nullptr, 10);
+  return (r > 0 && r < 65536) ? (uint32_t)r : 0u;
 }
 
 int launch_quant(const uint16_t* d_x, uint32_t count, uint8_t* ws_q, hipStream_t st,
@@ -407,16 +482,16 @@ struct CallPlan {
   size_t quant_off, ws_bytes;
 };
 
-bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c, Staging sg) {
+bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c, Staging sg, uint32_t rounds) {
   c->n_full = m / kPassRows;
   c->rest_rows = m % kPassRows;
   size_t q = 0;
   if (c->n_full) {
-    if (!plan_fused(in, kPassRows, &c->full, sg)) return false;
+    if (!plan_fused(in, kPassRows, &c->full, sg, rounds)) return false;
     q = std::max(q, c->full.quant_off);
   }
   if (c->rest_rows) {
-    if (!plan_fused(in, c->rest_rows, &c->rest, sg)) return false;
+    if (!plan_fused(in, c->rest_rows, &c->rest, sg, rounds)) return false;
     q = std::max(q, c->rest.quant_off);
   }
   c->quant_off = q;
@@ -456,6 +531,8 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     a.n2 = 0;
     a.slots = p.slots;
     a.red_cols = 0;
+    a.rounds = 1;
+    a.red_off = 0;
     x.bps = p.bps;
     x.bpw = p.bpw;
     x.batches = p.batches;
@@ -493,9 +570,25 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     a.n2 = p.n2;
     a.slots = p.slots;
     a.red_cols = p.red_cols;
+    a.rounds = p.rounds;
+    a.red_off = p.red_off;
     const uint32_t grid = p.wgs, threads = p.threads;
     const bool mix = p.mix != 0;
     int rc;
+    if (p.rounds > 1) {
+      switch (info->fmt) {
+        case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        default: return DGT_E_ARG;
+      }
+      if (rc) return rc;
+      continue;
+    }
     switch (info->fmt) {
       case DGT_FMT_INT8:
         rc = launch_fused<INT8>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
@@ -532,13 +625,15 @@ extern "C" {
 
 size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
   if (!info || m == 0 || m > kMaxRows) return 0;
-  // enough for every staging, so the environment may change between calls
+  // enough for every staging and for one round per workgroup (the most
+  // partial slots), so the environment may change between calls
   size_t ws = 0;
-  for (Staging sg : {kAuto, kWhole, kRing}) {
-    CallPlan c;
-    if (!plan_call(info, m, &c, sg)) return 0;
-    ws = std::max(ws, c.ws_bytes);
-  }
+  for (Staging sg : {kAuto, kWhole, kRing})
+    for (uint32_t rounds : {0u, 1u}) {
+      CallPlan c;
+      if (!plan_call(info, m, &c, sg, rounds)) return 0;
+      ws = std::max(ws, c.ws_bytes);
+    }
   return ws;
 }
 
@@ -557,7 +652,7 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
   if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
   if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
   CallPlan c;
-  if (!plan_call(info, m, &c, staging_from_env())) return DGT_E_UNSUPPORTED;
+  if (!plan_call(info, m, &c, staging_from_env(), rounds_from_env())) return DGT_E_UNSUPPORTED;
   if (ws_bytes < c.ws_bytes) return DGT_E_BUFSIZE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Layer L;
@@ -731,6 +826,8 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     uint32_t rc_cols = tile_n;
     while (rc_cols > 16 && (uint64_t)waves * a.m * rc_cols * 4 > lds) rc_cols /= 2;
     a.red_cols = rc_cols;
+    a.rounds = 1;
+    a.red_off = 0;
     d.w = static_cast<const uint8_t*>(d_w);
     d.n = n;
     d.k = k;

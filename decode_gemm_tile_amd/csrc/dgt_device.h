@@ -99,7 +99,8 @@ __device__ __forceinline__ uint32_t lut_load_freq(const uint16_t* table, uint32_
 
 __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32x2* lut,
                                  uint32_t* cum) {
-  const uint32_t t = threadIdx.x;
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));  // nothing derived from it is hoisted past a caller's loop
   const uint32_t lane = t & 63, wave = t >> 6;
   // inclusive scan of f over <= 256 symbols: wave scans plus wave totals
   uint32_t v = (t < alphabet) ? freq_of_thread : 0u;
@@ -151,7 +152,9 @@ __device__ inline void build_lut(uint32_t freq_of_thread, uint32_t alphabet, u32
 // per-wave sums before it is filled.  Caller synchronises.
 __device__ inline void build_lut_sparse(const uint32_t* table, uint32_t P, u32x2* lut,
                                         uint32_t* cum) {
-  const uint32_t t = threadIdx.x, B = blockDim.x;
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));  // nothing derived from it is hoisted past a caller's loop
+  const uint32_t B = blockDim.x;
   const uint32_t lane = t & 63, wave = t >> 6;
   uint32_t* wsum = reinterpret_cast<uint32_t*>(lut);
   const uint32_t q = (P + B - 1) / B;

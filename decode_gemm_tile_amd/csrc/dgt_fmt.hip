@@ -39,6 +39,23 @@ int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t th
   return DGT_E_UNSUPPORTED;
 }
 
+template <int R, int FN, bool MIX>
+int rounds_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st,
+             int* blocks_per_cu) {
+  auto k = k_fused_rounds<DGT_FMT, R, FN, 1, MIX>;
+  if (!set_lds(k, lds)) return DGT_E_HIP;
+  if (blocks_per_cu) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
+                                                     (int)threads, lds) != hipSuccess)
+      return DGT_E_HIP;
+    *blocks_per_cu = n;
+    return DGT_OK;
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, st, a);
+  return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
+}
+
 }  // namespace
 
 // Ring staging exists for R = 64 and 128 (one tile per chain).
@@ -58,6 +75,24 @@ int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32
   if (ring) return DGT_E_UNSUPPORTED;
   if (lanes == 32 && fn == 8) return fused_r<32, 8, false>(a, mt, mix, grid, threads, lds, st);
   if (lanes == 32 && fn == 16) return fused_r<32, 16, false>(a, mt, mix, grid, threads, lds, st);
+  return DGT_E_UNSUPPORTED;
+}
+
+// Multi-round register path (ring staging, 16-row blocks of X): launches, or
+// with blocks_per_cu set only reports how many workgroups a CU holds at once.
+template <>
+int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, bool mix,
+                                 uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st,
+                                 int* blocks_per_cu) {
+#define DGT_ROUNDS_CASE(RR, FNV)                                                          \
+  if (lanes == RR && fn == FNV)                                                           \
+    return mix ? rounds_t<RR, FNV, true>(a, grid, threads, lds, st, blocks_per_cu)        \
+               : rounds_t<RR, FNV, false>(a, grid, threads, lds, st, blocks_per_cu);
+  DGT_ROUNDS_CASE(64, 8)
+  DGT_ROUNDS_CASE(64, 16)
+  DGT_ROUNDS_CASE(128, 8)
+  DGT_ROUNDS_CASE(128, 16)
+#undef DGT_ROUNDS_CASE
   return DGT_E_UNSUPPORTED;
 }
 

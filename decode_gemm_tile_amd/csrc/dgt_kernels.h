@@ -46,6 +46,8 @@ struct GemmArgs {
   uint32_t n2;               // waves that take two units (the first n2 waves)
   uint32_t slots;            // partial slots per strip in the workspace
   uint32_t red_cols;         // tile_n columns reduced per LDS pass
+  uint32_t rounds;           // k_fused_rounds: rounds of cpw units per workgroup
+  uint32_t red_off;          // k_fused_rounds: LDS byte offset of the reduction buffer
 };
 
 // Static schedule: units (a chain of TPC consecutive k-tiles of one strip for
@@ -229,14 +231,17 @@ __device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t 
 // covered by one workgroup is written to Y directly; otherwise each workgroup
 // stores its partial in its slot and the last one to arrive (per-strip
 // counter) sums the slots in order, so results are deterministic.
+// Units [u0, u1) of workgroup blockIdx.x are reduced: C units per workgroup
+// in the strip numbering above; the waves holding units are those of the
+// first min(u1 - u0, cpw) units of a round.
 template <int FN, int MT>
-__device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
-                                                 float* red, float out_scale) {
-  const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t M = a.m, TN = FN * 16, C = a.cpw, RC = a.red_cols;
+__device__ __forceinline__ void reduce_range(const GemmArgs& a, floatx4 (&acc)[FN][MT],
+                                             float* red, float out_scale, uint32_t u0,
+                                             uint32_t u1, uint32_t C, uint32_t t) {
+  const uint32_t lane = t & 63, wave = t >> 6;
+  const uint32_t M = a.m, TN = FN * 16, RC = a.red_cols;
   const uint32_t wg = blockIdx.x;
-  const uint32_t u0 = wg * C, u1 = min(u0 + C, a.chains);
-  const uint32_t nw = waves_covering(u1 - u0, a.n2);           // active waves
+  const uint32_t nw = waves_covering(min(u1 - u0, a.cpw), a.n2);  // active waves
   const uint32_t sA = u0 / a.cps, sB = (u1 - 1) / a.cps;
   const uint32_t split =                                         // waves in strip A
       (sA == sB) ? nw : waves_covering((sA + 1) * a.cps - u0, a.n2);
@@ -314,6 +319,14 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&ac
     if (t == 0)
       __hip_atomic_store(&a.counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// One round per workgroup: units [b*C, b*C + C).
+template <int FN, int MT>
+__device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
+                                                 float* red, float out_scale) {
+  const uint32_t u0 = blockIdx.x * a.cpw;
+  reduce_range<FN, MT>(a, acc, red, out_scale, u0, min(u0 + a.cpw, a.chains), a.cpw, threadIdx.x);
 }
 
 // --------------------------------------------------------------- fused GEMM
@@ -654,6 +667,96 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   if constexpr (FMT == FP8)
     out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
   reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), out_scale);
+}
+
+// Layers with more chains than the CUs hold at once: a workgroup runs
+// a.rounds rounds of a.cpw units (a.cpw divides the units per strip and the
+// units of the layer, so every round is full and lies in one strip).  The LUT
+// is built once; a wave's accumulators carry over the rounds of a strip and
+// are reduced when the next round starts another strip or the range ends,
+// through a buffer at a.red_off that leaves the LUT intact.  Streams come
+// through the ring.  Each wave holds the same number of chains (ILP) in every
+// round, so its rounds are one loop with one decode path.
+template <int FMT, int R, int FN, int MT, int ILP>
+__device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, uint32_t fq,
+                                             uint32_t cw) {
+  const Layer& L = a.L;
+  const u32x2* lut = reinterpret_cast<const u32x2*>(smem);
+  uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
+  float* red = reinterpret_cast<float*>(smem + a.red_off);
+  const uint32_t C = a.cpw, CW = a.cpw * a.rounds;
+  const uint32_t U0 = blockIdx.x * CW, U1 = min(U0 + CW, a.chains);
+  floatx4 acc[FN][MT];
+  for (uint32_t u0 = U0; u0 < U1; u0 += C) {
+    const uint32_t lane = lane_id();
+    const bool first = u0 == U0;
+    const uint32_t chain0 = u0 + cw;
+    const uint32_t strip = chain0 / a.cps;
+    const uint32_t kt_first = chain0 % a.cps;
+    Chain ch[2];
+    Ring rg[2];
+    uint32_t tile_lane[2] = {0u, 0u};
+    uint32_t k0_lane[2] = {0u, 0u};
+    uint32_t c0[2][4];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      const uint32_t t = strip * L.kt + kt_first + c;
+      tile_lane[c] = t;
+      ring_issue(L, t, lane, rg[c], c0[c]);
+      ch[c].x = L.streams[L.index[t] + lane];
+      ch[c].x2 = (R == 128) ? L.streams[L.index[t] + 64 + lane] : 0u;
+      k0_lane[c] = (kt_first + c) * L.tile_k + 8 * (lane >> 4);
+    }
+    if (first) {
+      table_build<FMT>(fq, L, const_cast<u32x2*>(lut), cum);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) {
+      ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
+      ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * (cw + c) * L.region_words, lane, c0[c]);
+    }
+    if (first) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (ILP > 0)
+      fused_chains<FMT, R, FN, MT, ILP, true>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip,
+                                              acc, []() {});
+    // reduce at the end of the range or before a round in another strip
+    const uint32_t un = u0 + C;
+    if (un >= U1 || un / a.cps != u0 / a.cps) {
+      float out_scale = 1.f;
+      if constexpr (FMT == FP8)
+        out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
+      reduce_range<FN, MT>(a, acc, red, out_scale, max(U0, (u0 / a.cps) * a.cps), u0 + C, CW,
+                           threadIdx.x);
+      if (un < U1) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();  // the reduction buffer overlaps the next round's rings
+      }
+    }
+  }
+}
+
+template <int FMT, int R, int FN, int MT, bool MIX>
+__global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_fused_rounds(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const uint32_t cw = wave_first_unit(wave, a.n2);
+  const uint32_t fq = table_issue<FMT>(a.L);
+  // chains per wave: 2 for the first n2 waves, else 1; none past the round
+  if (MIX && wave < a.n2)
+    fused_rounds<FMT, R, FN, MT, 2>(a, smem, fq, cw);
+  else if (cw < a.cpw)
+    fused_rounds<FMT, R, FN, MT, 1>(a, smem, fq, cw);
+  else
+    fused_rounds<FMT, R, FN, MT, 0>(a, smem, fq, cw);
 }
 
 // ------------------------------------------------- fused GEMM, large M (LDS)

@@ -29,8 +29,11 @@
  *     little-endian.  Calls are thread-safe.
  *   - Environment: DGT_STAGING=whole|ring overrides the per-layer choice of
  *     how device kernels bring tile streams on chip (whole streams, or a
- *     two-chunk ring for one tile per wave); results are identical.  Read at
- *     every call; dgt_gemm_workspace covers every choice.
+ *     two-chunk ring for one tile per wave); DGT_ROUNDS=n forces n rounds of
+ *     chains per workgroup where the multi-round fused kernel applies (ring
+ *     staging, M <= 16 per launch, 64 or 128 lanes) instead of the per-layer
+ *     choice (1 = one round).  Results are identical.  Read at every call;
+ *     dgt_gemm_workspace covers every choice.
  *
  * Compressed layer ("blob") format, version 1 (all offsets in bytes):
  *   header (128 B): magic "DGT1", u16 version, u16 header size, u32 fmt,

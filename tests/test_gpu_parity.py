@@ -214,6 +214,41 @@ def test_forced_staging_matches_oracle(fmt, n, k, tn, tk, R, seed, staging, monk
         assert (status.cpu().numpy() == 0).all()
 
 
+ROUNDS_CASES = [
+    (FB, 256, 4096, 128, 64, 64, 81),     # two strips of 64 chains
+    (FH, 256, 4096, 128, 64, 64, 82),
+    (F8, 256, 1024, 128, 32, 32, 83),     # chains of two tiles
+    (FE, 512, 1024, 256, 64, 128, 84),    # tile_n 256, two states per lane
+    (FP, 384, 2048, 128, 64, 64, 85),     # int4 pairs with scales
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", ROUNDS_CASES)
+@pytest.mark.parametrize("rounds", [2, 3, 7])
+@pytest.mark.parametrize("staging", ["ring", "whole"])
+def test_rounds_per_workgroup_match_oracle(fmt, n, k, tn, tk, R, seed, rounds, staging,
+                                           monkeypatch):
+    """Workgroups that run several rounds of chains (one LUT build, partial
+    sums reduced when a round starts another strip) give the oracle's
+    results; forced here on small layers, where ranges straddle strips."""
+    import torch
+    monkeypatch.setenv("DGT_ROUNDS", str(rounds))
+    monkeypatch.setenv("DGT_STAGING", staging)
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=16)
+    layer = dgt.DeviceLayer(blob)
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, 16))
+    for m in (1, 5, 16):
+        xb = d["x"][:m]
+        status.fill_(-1)
+        y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), scales=scales, w_scale=d["w_scale"],
+                                      status=status, ws=ws)
+        torch.cuda.synchronize()
+        assert rel_err(y.cpu().numpy(), reference(fmt, d, xb)) <= TOL, m
+        assert (status.cpu().numpy() == 0).all()
+
+
 def test_fused_gemm_large_m_repeatable():
     import torch
     d, blob = _layer(FB, 384, 4096, 128, 64, 64, 48, m=256)
