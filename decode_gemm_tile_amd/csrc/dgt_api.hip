@@ -13,9 +13,6 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "../../include/dgt.h"
 #include "dgt_format.h"
@@ -271,17 +268,10 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
 // the layer's chains over the CUs (one round) when the wave cap allows it;
 // beyond the cap the first n2 waves take two chains each (MIX kernels).
 // Workgroups of the multi-round kernel a CU holds at once (its registers and
-// LDS decide); 1 when the runtime cannot tell.  Cached per kernel and shape.
+// LDS decide, as the runtime reports for the current device); 1 when the
+// runtime cannot tell.
 uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, bool mix, uint32_t threads,
                               uint32_t lds) {
-  static std::mutex mu;
-  static std::map<std::tuple<uint32_t, uint32_t, uint32_t, bool, uint32_t, uint32_t>, uint32_t> memo;
-  const auto key = std::make_tuple(in->fmt, in->lanes, fn, mix, threads, lds);
-  {
-    std::lock_guard<std::mutex> g(mu);
-    auto it = memo.find(key);
-    if (it != memo.end()) return it->second;
-  }
   GemmArgs a{};
   int n = 0, rc = DGT_E_ARG;
   switch (in->fmt) {
@@ -294,10 +284,7 @@ uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, bool mix, uint32_
     case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
     default: break;
   }
-  const uint32_t v = (rc == DGT_OK && n > 0) ? (uint32_t)n : 1u;
-  std::lock_guard<std::mutex> g(mu);
-  memo[key] = v;
-  return v;
+  return (rc == DGT_OK && n > 0) ? (uint32_t)n : 1u;
 }
 
 bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_env, FusedPlan* p,
