@@ -148,8 +148,8 @@ def cpu_baseline(d, wl, blob):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
-              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -15,7 +15,8 @@ ARCH = "gfx950"
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    # packed fp32 VALU forms stay off (hardware notes)
+    # no packed fp32 VALU instructions: the compiler would otherwise form them
+    # from scalar and float2 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]

@@ -176,7 +176,7 @@ const char* dgt_status_string(int status) {
     case DGT_E_FORMAT: return "unrecognised blob format";
     case DGT_E_CORRUPT: return "corrupt blob";
     case DGT_E_HIP: return "HIP runtime error";
-    case DGT_E_UNSUPPORTED: return "unsupported by this build";
+    case DGT_E_UNSUPPORTED: return "not supported by this library";
     default: return "unknown status";
   }
 }

@@ -100,7 +100,7 @@ enum dgt_status {
   DGT_E_FORMAT = -5,      /* blob header not recognised (magic, version, fmt) */
   DGT_E_CORRUPT = -6,     /* blob inconsistent (sizes, index, table, ktab) */
   DGT_E_HIP = -7,         /* a HIP runtime call or kernel launch failed */
-  DGT_E_UNSUPPORTED = -8  /* valid request this build does not implement */
+  DGT_E_UNSUPPORTED = -8  /* valid request this library does not implement */
 };
 
 /* Layer geometry for compression.  prob_bits: frequency precision n (12). */
