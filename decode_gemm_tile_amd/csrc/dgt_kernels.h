@@ -581,6 +581,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   Staged stg[2];   // whole streams
   Ring rg[2];      // ring: chunk 0 (c0) now, later chunks through the ring
   uint32_t c0[2][4];
+  uint32_t kq[2];  // payload step counts, loaded before the streams
   const uint32_t fq = table_issue<FMT>(L);
   const uint32_t sub_lane = R != 32 ? lane : half_lane, sub_size = R != 32 ? 64u : 32u;
   // 1) issue the stream loads, 2) build the LUT while they are in flight,
@@ -595,6 +596,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     const uint32_t ta = strip * L.kt + kt_first + cc * TPC;
     const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
     tile_lane[c] = t_l;
+    kq[c] = L.ktab[t_l];
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
@@ -611,11 +613,11 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     for (int c = 0; c < 2; ++c) stage_load(stg[c], L.lanes, sub_lane, sub_size, kPreHalf, kPre);
   }
   table_build<FMT>(fq, L, lut, cum);
-  // the payload counts are read after the LUT build: a wait for them then
-  // costs nothing (the staged streams are needed next anyway)
+  // the payload counts were loaded before the streams: waiting for them does
+  // not wait for the stream loads (the counter retires loads in order)
 #pragma unroll
   for (int c = 0; c < 2; ++c)
-    if (c < (int)nch) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
+    if (c < (int)nch) ch[c].lim = L.steps - kq[c];
   __syncthreads();  // LUT complete; each wave's staged streams are private to it
   uint32_t cstart[2] = {0u, 0u};  // this lane's tile region (u16 words)
 #pragma unroll
@@ -698,10 +700,12 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
     uint32_t tile_lane[2] = {0u, 0u};
     uint32_t k0_lane[2] = {0u, 0u};
     uint32_t c0[2][4];
+    uint32_t kq[2];  // payload step counts, loaded before the streams
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t t = strip * L.kt + kt_first + c;
       tile_lane[c] = t;
+      kq[c] = L.ktab[t];
       ring_issue(L, t, lane, rg[c], c0[c]);
       ch[c].x = L.streams[L.index[t] + lane];
       ch[c].x2 = (R == 128) ? L.streams[L.index[t] + 64 + lane] : 0u;
@@ -713,7 +717,7 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
     }
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
-      ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
+      ch[c].lim = L.steps - kq[c];
       ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * (cw + c) * L.region_words, lane, c0[c]);
     }
     if (first) {
@@ -926,9 +930,11 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     Ring rg[ILP];
     uint32_t c0[ILP][4];
     Staged stg[ILP];
+    uint32_t kq[ILP];  // payload step counts, loaded before the streams
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       tj[c] = strip * L.kt + kt0 + c * NW + wave;
+      kq[c] = L.ktab[tj[c]];
       if constexpr (RING)
         ring_issue(L, tj[c], lane, rg[c], c0[c]);
       else
@@ -938,7 +944,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
     }
     if (b == b0) table_build<FMT>(fq, L, lut, cum);
 #pragma unroll
-    for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tj[c]];
+    for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - kq[c];
     __syncthreads();  // LUT complete; the previous batch's fragment reads are done
     uint32_t lim_min = 0xFFFFFFFFu;
 #pragma unroll
@@ -1122,6 +1128,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
 
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
+  uint32_t kq[ILP];  // payload step counts, loaded before the streams
   Staged stg[ILP];  // whole streams
   Ring rg[ILP];     // ring
   uint32_t c0[ILP][4];
@@ -1138,6 +1145,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
     const uint32_t t_l = (R == 32 && upper) ? tb : ta;
     tile_lane[c] = t_l;
+    kq[c] = L.ktab[t_l];
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
@@ -1147,7 +1155,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   }
   table_build<FMT>(fq, L, lut, cum);
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
+  for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - kq[c];
   __syncthreads();  // LUT complete; each wave's staged stream is private to it
   if (!active) return;
 #pragma unroll
