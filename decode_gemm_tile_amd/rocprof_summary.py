@@ -2,10 +2,13 @@
 
 Usage:
   python -m decode_gemm_tile_amd.rocprof_summary trace <dir> [--title T] [--cmd C]
+  python -m decode_gemm_tile_amd.rocprof_summary counters <dir> --kernel k_fused [--cmd C]
   python -m decode_gemm_tile_amd.rocprof_summary traffic <fetch_dir> <write_dir>
         --kernel k_fused --workload bf16_mlp --alg-bytes N --source-hash H [--cmd C]
 
 `trace` lists kernel dispatch counts and durations (from --kernel-trace runs).
+`counters` lists, for the named kernel, the median per dispatch of every
+counter a --pmc run collected.
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch, from two --pmc
 runs) into HBM bytes per launch of the named kernel, each scaled by what the
 same counter reads for the plain 512 MiB device copy that bench.py
@@ -70,6 +73,21 @@ def cmd_trace(args):
                                                             mx / 1e3, tot / 1e3))
 
 
+def cmd_counters(args):
+    cur = _db(args.dir).cursor()
+    names = [r[0] for r in cur.execute("select distinct counter_name from pmc_events")]
+    print("# Counters of `%s`%s" % (args.kernel, (" (%s)" % args.title) if args.title else ""))
+    print()
+    if args.cmd:
+        print("Command: `%s`" % args.cmd)
+        print()
+    print("| counter | median per dispatch | dispatches |")
+    print("|---|---|---|")
+    for n in sorted(names):
+        _, med, cnt = _pick(counter_per_dispatch(args.dir, n), args.kernel)
+        print("| %s | %.6g | %d |" % (n, med, cnt))
+
+
 def cmd_traffic(args):
     f = counter_per_dispatch(args.fetch_dir, "FETCH_SIZE")
     w = counter_per_dispatch(args.write_dir, "WRITE_SIZE")
@@ -104,6 +122,11 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--title", default="")
     t.add_argument("--cmd", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--cmd", default="")
     r = sub.add_parser("traffic")
     r.add_argument("fetch_dir")
     r.add_argument("write_dir")
@@ -116,6 +139,8 @@ def main(argv=None):
     args = p.parse_args(argv)
     if args.mode == "trace":
         cmd_trace(args)
+    elif args.mode == "counters":
+        cmd_counters(args)
     else:
         cmd_traffic(args)
 
