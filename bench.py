@@ -281,6 +281,18 @@ def main():
                                     "two_stage_ms": round(ms_two, 4),
                                     "fused_ms": round(ms_fused, 4),
                                     "fused_speedup_vs_two_stage": round(ms_two / ms_fused, 3)}
+            if mm > 16 and wl.lanes == 64:
+                # the fused rung without ping-pong: one fragment buffer in the
+                # large-M kernel (the library reads the switch at every call)
+                os.environ["DGT_XM_SINGLE_BUFFER"] = "1"
+                try:
+                    ms_one = timed(lambda i: dgt.dgt_fused_decode_gemm(
+                        layers[i % copies], xm, scales=scales, w_scale=d["w_scale"], y=y2,
+                        ws=ws2, stream=stream), reps, 3, stream)
+                finally:
+                    del os.environ["DGT_XM_SINGLE_BUFFER"]
+                ablation["m%d" % mm]["fused_single_buffer_ms"] = round(ms_one, 4)
+                ablation["m%d" % mm]["ping_pong_speedup"] = round(ms_one / ms_fused, 3)
             # vendor GEMM on the uncompressed bf16 weight (reference point only),
             # alone and after the layer-level decode (the two-stage path with
             # the vendor library's GEMM on the decoded copy)

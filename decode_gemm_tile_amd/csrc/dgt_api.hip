@@ -420,6 +420,13 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg, uint32
   return plan_fused_reg(in, m, true, rounds, p, &unused);
 }
 
+// One fragment buffer instead of two in the large-M kernel (the ablation rung
+// without ping-pong), asked for by DGT_XM_SINGLE_BUFFER=1; results are identical.
+bool xm_single_buffer_from_env() {
+  const char* v = std::getenv("DGT_XM_SINGLE_BUFFER");
+  return v && std::strcmp(v, "1") == 0;
+}
+
 // Rounds per workgroup of the register path, forced by the environment
 // variable DGT_ROUNDS (a positive count; results are identical), else 0.
 uint32_t rounds_from_env() {
@@ -496,6 +503,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
   Layer L = L0;
   L.region_words = p.region_words;
   if (p.xm) {
+    const bool pp = !xm_single_buffer_from_env();
     XmArgs x;
     GemmArgs& a = x.g;
     a.L = L;
@@ -525,13 +533,13 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     x.batches = p.batches;
     x.xbuf_off = p.xbuf_off;
     switch (info->fmt) {
-      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, p.wgs, p.lds, st);
+      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
     }
   }

@@ -96,24 +96,29 @@ int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn,
   return DGT_E_UNSUPPORTED;
 }
 
+// pingpong = false: one fragment buffer (ablation; 64 lanes only).
 template <>
 int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring,
-                             uint32_t grid, uint32_t lds, hipStream_t st) {
-#define DGT_XM_CASE(RR, FNV, RG)                                                \
-  if (lanes == RR && fn == FNV && ring == RG) {                                 \
-    auto k = k_fused_xm<DGT_FMT, RR, FNV, RG>;                                  \
+                             bool pingpong, uint32_t grid, uint32_t lds, hipStream_t st) {
+#define DGT_XM_CASE(RR, FNV, RG, PPV)                                           \
+  if (lanes == RR && fn == FNV && ring == RG && pingpong == PPV) {              \
+    auto k = k_fused_xm<DGT_FMT, RR, FNV, RG, PPV>;                             \
     if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(FNV)), lds, st, x);    \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
   }
-  DGT_XM_CASE(64, 8, false)
-  DGT_XM_CASE(64, 8, true)
-  DGT_XM_CASE(64, 16, false)
-  DGT_XM_CASE(64, 16, true)
-  DGT_XM_CASE(128, 8, false)
-  DGT_XM_CASE(128, 8, true)
-  DGT_XM_CASE(128, 16, false)
-  DGT_XM_CASE(128, 16, true)
+  DGT_XM_CASE(64, 8, false, true)
+  DGT_XM_CASE(64, 8, true, true)
+  DGT_XM_CASE(64, 16, false, true)
+  DGT_XM_CASE(64, 16, true, true)
+  DGT_XM_CASE(128, 8, false, true)
+  DGT_XM_CASE(128, 8, true, true)
+  DGT_XM_CASE(128, 16, false, true)
+  DGT_XM_CASE(128, 16, true, true)
+  DGT_XM_CASE(64, 8, false, false)
+  DGT_XM_CASE(64, 8, true, false)
+  DGT_XM_CASE(64, 16, false, false)
+  DGT_XM_CASE(64, 16, true, false)
 #undef DGT_XM_CASE
   return DGT_E_UNSUPPORTED;
 }

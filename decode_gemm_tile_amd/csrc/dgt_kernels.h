@@ -890,7 +890,9 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
 // R = 64 or 128 (one tile per chain) and tile_k = 64 only.  With two states
 // per lane a wave publishes two operands per fragment (the tile's two row
 // halves at the same k), multiplied into the two halves' accumulators.
-template <int FMT, int R, int FN, bool RING>
+// PP = false keeps one fragment buffer (a barrier after the products, before
+// the next group is published): the rung without ping-pong of the ablation.
+template <int FMT, int R, int FN, bool RING, bool PP = true>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
@@ -999,7 +1001,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
 #pragma unroll
       for (int f0 = 0; f0 < FNH; f0 += FPB) {
         const uint32_t gq = (fk * FNH + f0) / FPB;
-        uint8_t* buf = xbuf + (gq & 1) * (FPB * NO * 1024);
+        uint8_t* buf = xbuf + (PP ? (gq & 1) : 0u) * (FPB * NO * 1024);
 #pragma unroll
         for (int d = 0; d < FPB; ++d) {
         const int fn = f0 + d;
@@ -1086,6 +1088,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
             __builtin_amdgcn_sched_group_barrier(0x008, kXB * MTW, 0);  // MFMA
           }
         }
+        if constexpr (!PP) __syncthreads();  // one buffer: every read done before the next publish
       }
     }
     if (a.status) {

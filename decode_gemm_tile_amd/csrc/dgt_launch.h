@@ -17,8 +17,8 @@ template <int FMT>
 int launch_fused_rounds(const GemmArgs& a, uint32_t lanes, uint32_t fn, bool mix, uint32_t grid,
                         uint32_t threads, uint32_t lds, hipStream_t st, int* blocks_per_cu);
 template <int FMT>
-int launch_fused_xm(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring, uint32_t grid,
-                    uint32_t lds, hipStream_t st);
+int launch_fused_xm(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring, bool pingpong,
+                    uint32_t grid, uint32_t lds, hipStream_t st);
 template <int FMT>
 int launch_decode(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bool ring, uint32_t grid,
                   uint32_t threads, uint32_t lds, hipStream_t st);

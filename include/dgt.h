@@ -32,7 +32,10 @@
  *     two-chunk ring for one tile per wave); DGT_ROUNDS=n forces n rounds of
  *     chains per workgroup where the multi-round fused kernel applies (ring
  *     staging, M <= 16 per launch, 64 or 128 lanes) instead of the per-layer
- *     choice (1 = one round).  Results are identical.  Read at every call;
+ *     choice (1 = one round); DGT_XM_SINGLE_BUFFER=1 makes the large-M fused
+ *     kernel (17 <= M <= 256 per pass, 64 lanes) keep one fragment buffer
+ *     instead of two (a comparison point; an error where no such kernel
+ *     exists).  Results are identical.  Read at every call;
  *     dgt_gemm_workspace covers every choice.
  *
  * Compressed layer ("blob") format, version 1 (all offsets in bytes):

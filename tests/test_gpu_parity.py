@@ -160,6 +160,30 @@ def test_fused_gemm_large_m_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     assert int(ws[:4 * strips].sum().item()) == 0   # strip counters returned to zero
 
 
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", [c for c in XM_CASES if c[5] == 64])
+@pytest.mark.parametrize("staging", ["ring", "whole"])
+def test_large_m_single_buffer_matches_oracle(fmt, n, k, tn, tk, R, seed, staging, monkeypatch):
+    """The large-M kernel with one fragment buffer (a barrier after every
+    group's products instead of ping-pong buffers) gives the oracle's results
+    and the same values as the two-buffer kernel."""
+    import torch
+    monkeypatch.setenv("DGT_STAGING", staging)
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=100)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, 100))
+    y2 = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"],
+                                   ws=ws).clone()
+    monkeypatch.setenv("DGT_XM_SINGLE_BUFFER", "1")
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    y1 = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"],
+                                   status=status, ws=ws)
+    torch.cuda.synchronize()
+    assert rel_err(y1.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
+    assert torch.equal(y1, y2)
+    assert (status.cpu().numpy() == 0).all()
+
+
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", [
     (FB, 384, 4096, 128, 64, 64, 52),
     (FE, 512, 1024, 256, 64, 64, 53),     # one fp8 activation scale across passes
