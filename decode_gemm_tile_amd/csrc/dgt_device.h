@@ -87,6 +87,17 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
+// Payload step count of tile t, t the same in every lane: a scalar load of
+// the dword holding byte t (the k table starts 16-aligned and is padded to 16
+// bytes, so the dword lies inside it).  A vector load of a value the code
+// then makes uniform would be read back at once, waiting for every load
+// issued before it.
+__device__ __forceinline__ uint32_t ktab_scalar(const uint8_t* ktab, uint32_t t) {
+  typedef __attribute__((address_space(4))) const uint32_t const_u32;
+  const const_u32* w = reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(ktab) + (t & ~3u));
+  return (*w >> (8u * (t & 3u))) & 0xFFu;
+}
+
 // Build the slot table in LDS from the shared frequency table: every slot r
 // maps to the symbol s with c_s <= r < c_s + f_s.  Caller synchronises.
 // The frequency load is split off so it can be issued before other loads

@@ -596,7 +596,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     const uint32_t ta = strip * L.kt + kt_first + cc * TPC;
     const uint32_t t_l = (R == 32 && upper) ? ta + 1 : ta;
     tile_lane[c] = t_l;
-    kq[c] = L.ktab[t_l];
+    kq[c] = (R == 32) ? (uint32_t)L.ktab[t_l] : ktab_scalar(L.ktab, t_l);
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
@@ -705,7 +705,7 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
     for (int c = 0; c < ILP; ++c) {
       const uint32_t t = strip * L.kt + kt_first + c;
       tile_lane[c] = t;
-      kq[c] = L.ktab[t];
+      kq[c] = ktab_scalar(L.ktab, t);
       ring_issue(L, t, lane, rg[c], c0[c]);
       ch[c].x = L.streams[L.index[t] + lane];
       ch[c].x2 = (R == 128) ? L.streams[L.index[t] + 64 + lane] : 0u;
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       tj[c] = strip * L.kt + kt0 + c * NW + wave;
-      kq[c] = L.ktab[tj[c]];
+      kq[c] = ktab_scalar(L.ktab, tj[c]);
       if constexpr (RING)
         ring_issue(L, tj[c], lane, rg[c], c0[c]);
       else
@@ -1131,7 +1131,6 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
 
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
-  uint32_t kq[ILP];  // payload step counts, loaded before the streams
   Staged stg[ILP];  // whole streams
   Ring rg[ILP];     // ring
   uint32_t c0[ILP][4];
@@ -1148,7 +1147,6 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
     const uint32_t t_l = (R == 32 && upper) ? tb : ta;
     tile_lane[c] = t_l;
-    kq[c] = L.ktab[t_l];
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
     else
@@ -1157,8 +1155,10 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     ch[c].x2 = (R == 128) ? L.streams[L.index[t_l] + 64 + lane] : 0u;
   }
   table_build<FMT>(fq, L, lut, cum);
+  // the payload counts are read after the LUT build (read before the
+  // streams they slowed this kernel down, 66 -> 76 us on the bf16 MLP layer)
 #pragma unroll
-  for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - kq[c];
+  for (int c = 0; c < ILP; ++c) ch[c].lim = L.steps - (uint32_t)L.ktab[tile_lane[c]];
   __syncthreads();  // LUT complete; each wave's staged stream is private to it
   if (!active) return;
 #pragma unroll
