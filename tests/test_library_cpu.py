@@ -161,3 +161,18 @@ def test_workspace_sizes_cover_every_pass():
     assert w513 >= w256 + (513 - 256) * 1024 * 2
     assert dgt.dgt_gemm_workspace(layer, 0) == 0
     assert dgt.dgt_gemm_workspace(layer, (1 << 16) + 1) == 0
+
+
+def test_size_within_a_tenth_of_a_bit_of_entropy_on_256x64_tiles():
+    """At 16384 weights per tile the per-lane state flush, less what the
+    initial-state payload recovers, stays under 0.1 bit/weight: the fp8 layer
+    (8-bit symbols) coded by the library's encoder against the oracle's
+    empirical entropy of the same symbols."""
+    from oracle import entropy as oent
+    d = workloads.make("fp8_8192")
+    wl = d["workload"]
+    b = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    sym, _ = oblob.symbolise(wl.fmt, d["codes"])
+    h = oent.empirical_entropy(sym, oblob.alphabet_of(wl.fmt))
+    bpw = 8.0 * len(b) / (wl.n * wl.k)
+    assert h <= bpw <= h + 0.1, (h, bpw)
