@@ -273,6 +273,29 @@ def test_rounds_per_workgroup_match_oracle(fmt, n, k, tn, tk, R, seed, rounds, s
         assert (status.cpu().numpy() == 0).all()
 
 
+@pytest.mark.parametrize("fmt,seed", [(F4, 86), (FB, 87)])
+def test_rounds_two_chains_per_wave_match_oracle(fmt, seed, monkeypatch):
+    """A layer large enough for 32 chains per workgroup (16 waves, two chains
+    each) through the ring, forced into 3 rounds so that workgroup ranges of
+    96 chains straddle the 256-chain strips: every output column against the
+    fp64 oracle."""
+    import torch
+    monkeypatch.setenv("DGT_STAGING", "ring")
+    monkeypatch.setenv("DGT_ROUNDS", "3")
+    d, blob = _layer(fmt, 4096, 16384, 128, 64, 64, seed, m=16)
+    layer = dgt.DeviceLayer(blob)
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    for m in (1, 16):
+        xb = d["x"][:m]
+        status.fill_(-1)
+        y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), scales=scales, w_scale=d["w_scale"],
+                                      status=status)
+        torch.cuda.synchronize()
+        assert rel_err(y.cpu().numpy(), reference(fmt, d, xb)) <= TOL, m
+        assert (status.cpu().numpy() == 0).all()
+
+
 def test_fused_gemm_large_m_repeatable():
     import torch
     d, blob = _layer(FB, 384, 4096, 128, 64, 64, 48, m=256)
