@@ -1,22 +1,25 @@
 """Benchmark of the fused rANS-decode GEMM on one MI355X.
 
 One step = one pass of the hot path over one batch: dgt_fused_decode_gemm on a
-resident compressed layer (LUT prologue, tile fetch, on-chip rANS decode,
-matrix-core product, split-K reduction and epilogue), here on the Llama-3-8B
-MLP projection shape W 14336x4096 stored as bf16 with its high byte coded
-(workload "bf16_mlp"), X of M = 1 row.  Several copies of the blob rotate so
-the 256 MB last-level cache cannot hold the working set.
+resident compressed layer (decode-table prologue, tile fetch, on-chip rANS
+decode, matrix-core product, split-K reduction and epilogue).  The default
+workload is the largest single-GPU configuration, the 405B-scale FFN weight
+W 53248x16384 stored as bf16 with its high byte rANS-coded and its low byte
+raw ("bf16_ffn405"), X of M = 1 row.  Copies of the blob rotate so the 256 MB
+last-level cache never holds the working set.
 
-Prints ONE JSON line: metric, value (decoded-weight GB/s at M = 1), roofline of
-the fused kernel (HBM bytes it must read / kernel time), the CPU oracle timed on
-the host cores, and secondary figures (bits/weight, TFLOP/s at M = 256, the
-uncompressed baseline).
+Prints ONE JSON line: metric, value (decoded-weight GB/s at M = 1), the
+roofline of the fused kernel (algorithmic bytes per launch / launch time), the
+CPU oracle timed on the host's cores, and secondary figures (bits/weight,
+TFLOP/s at M = 256, the library's own uncompressed GEMM, the vendor GEMM, the
+ablation ladder, the int4 405B-scale FFN and the Llama-3-8B MLP layer).
 """
 
 import argparse
 import hashlib
 import json
 import math
+import multiprocessing as mp
 import os
 import re
 import sys
@@ -31,6 +34,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20     # working set above the 256 MB last-level cache
 METRIC = "fused rANS-decode GEMM decoded-weight GB/s at M=1; TFLOP/s at M=256; bits/wt"
+# decoded-weight bytes per weight at the format's storage width (int4: half a byte)
+STORAGE_BYTES = {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0, 7: 2.0}
+CPU_SAMPLE_WEIGHTS = 96 << 20  # weights of W the CPU oracle decodes (whole strips)
 
 
 def parse_args():
@@ -38,10 +44,12 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="bf16_mlp")
+    p.add_argument("--workload", default="bf16_ffn405")
+    p.add_argument("--m", type=int, default=1,
+                   help="rows of X of the headline launches (the metric is quoted at M = 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true",
-                   help="time only the M=1 fused kernel (for profiler runs)")
+                   help="time only the headline launches (for profiler runs)")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run one plain device copy of 512 MiB (counter calibration)")
     return p.parse_args()
@@ -57,10 +65,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_prefix: str, workload: str, per_launch_ref: float):
+def traffic_from_profiles(workload: str, m: int):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_m%d.md" % (workload, m))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -71,7 +79,96 @@ def traffic_from_profiles(kernel_prefix: str, workload: str, per_launch_ref: flo
     return float(m_val.group(1))
 
 
+# ------------------------------------------------------------- CPU oracle
+_CPU = {}  # inherited by forked workers: blob, workload, codes, x row
+
+
+def _cpu_strips(bounds):
+    """Oracle decode of strips [s0, s1) of W plus the fp64 GEMV of X's first
+    row with those rows; returns (s0, y part, decoded rows equal the input)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import blob as oblob
+    from oracle import gemm as ogemm
+    from oracle import numerics, order
+    s0, s1 = bounds
+    blob, wl, codes, x1 = _CPU["blob"], _CPU["wl"], _CPU["codes"], _CPU["x1"]
+    kt = wl.k // wl.tile_k
+    tiles = list(range(s0 * kt, s1 * kt))
+    rows = (s1 - s0) * wl.tile_n
+    T = wl.tile_n * wl.tile_k
+    with threadpool_limits(limits=1):
+        h = oblob.parse(blob)
+        syms = oblob.decode_symbols(blob, tiles)
+        raw = np.frombuffer(blob, np.uint8, len(tiles) * T, h["raw_off"] + tiles[0] * T)
+        raw = raw.reshape(len(tiles), T)
+        if wl.fmt == 7:  # high-byte pairs: symbol = hi[2c] | hi[2c+1] << 8
+            pairs = order.scatter_tiles(syms.astype(np.uint16), rows, wl.k // 2, wl.tile_n,
+                                        wl.tile_k // 2, wl.lanes, epl=4)
+            hi = np.empty((rows, wl.k), np.uint16)
+            hi[:, 0::2] = pairs & 0xFF
+            hi[:, 1::2] = pairs >> 8
+        else:
+            hi = order.scatter_tiles(syms.astype(np.uint8), rows, wl.k, wl.tile_n, wl.tile_k,
+                                     wl.lanes)
+        lo = order.scatter_tiles(raw, rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes, raw=True)
+        w = (hi.astype(np.uint16) << 8) | lo
+        y = ogemm.gemm_fp64(numerics.bf16_bits_to_f64(x1), numerics.bf16_bits_to_f64(w))
+    r0 = s0 * wl.tile_n
+    return s0, y, bool(np.array_equal(w, codes[r0:r0 + rows]))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d, wl, blob):
+    """The CPU oracle (rANS decode of the compressed layer + fp64 GEMV at
+    M = 1) on a bounded sample: the first whole strips of the layer, about
+    CPU_SAMPLE_WEIGHTS weights.  Timed on one core, then split over every core
+    this process may run on (forked workers, one range of strips each)."""
+    strips = wl.n // wl.tile_n
+    s_count = max(1, min(strips, CPU_SAMPLE_WEIGHTS // (wl.tile_n * wl.k)))
+    _CPU.update(blob=blob, wl=wl, codes=np.asarray(d["codes"]), x1=d["x"][:1])
+    weights = s_count * wl.tile_n * wl.k
+    decoded = weights * STORAGE_BYTES[wl.fmt]
+    t0 = time.perf_counter()
+    _, y1, ok1 = _cpu_strips((0, s_count))
+    t1 = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    workers = min(cores, s_count)
+    cuts = np.linspace(0, s_count, workers + 1).astype(int)
+    parts = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(parts)) as pool:
+        res = pool.map(_cpu_strips, parts)
+    tn = time.perf_counter() - t0
+    yn = np.concatenate([r[1] for r in sorted(res, key=lambda r: r[0])], axis=1)
+    assert ok1 and all(r[2] for r in res), "oracle decode differs from the input weights"
+    assert np.array_equal(yn, y1)
+    _CPU.clear()
+    return {"value": round(decoded / tn / 1e9, 6), "unit": "GB/s", "cores": len(parts),
+            "kind": "oracle",
+            "sample": "strips 0..%d of %d (rows 0..%d, all K: %d tiles, %.1f M weights), "
+                      "rANS decode + fp64 GEMV at M=1; %d worker processes, numpy and BLAS "
+                      "at 1 thread each" % (s_count - 1, strips, s_count * wl.tile_n - 1,
+                                            s_count * (wl.k // wl.tile_k), weights / 1e6,
+                                            len(parts)),
+            "seconds": round(tn, 3), "single_core_value": round(decoded / t1 / 1e9, 6),
+            "single_core_seconds": round(t1, 3), "affinity_cores": cores,
+            "cpu_model": cpu_model(), "checksum": float(np.abs(y1).sum())}
+
+
+# ------------------------------------------------------------------- GPU
 def timed(fn, steps, warmup, stream):
+    """Average ms per call over `steps` calls, bracketed by events on `stream`
+    (the stream every library call is launched on)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -83,7 +180,7 @@ def timed(fn, steps, warmup, stream):
         fn(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per step
+    return start.elapsed_time(end) / steps
 
 
 def launch_distribution(fn, n, stream):
@@ -103,99 +200,121 @@ def launch_distribution(fn, n, stream):
             "p90_us": round(float(np.percentile(us, 90)), 3), "launches": n}
 
 
-def cpu_baseline(d, wl, blob):
-    """The CPU oracle (decode of the compressed layer + fp64 GEMV), timed on the
-    host on a bounded sample of the layer: every tile of the first strips."""
-    from threadpoolctl import threadpool_limits
+class Resident:
+    """A workload's blob in HBM (rotating copies), its X, scales and workspaces."""
 
+    def __init__(self, dgt, name, d, blob, dev):
+        import torch
+        self.dgt, self.d, self.dev = dgt, d, dev
+        self.wl = d["workload"]
+        self.blob = blob
+        self.info = dgt.dgt_layer_info(blob)
+        self.copies = max(2, math.ceil(ROTATE_BYTES / len(blob)))
+        self.layers = [dgt.DeviceLayer(blob, dev) for _ in range(self.copies)]
+        self.x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        self.scales = (torch.from_numpy(d["scales"].view(np.int16)).to(dev)
+                       if d["scales"] is not None else None)
+        self._ws = {}
+
+    def call(self, m, stream):
+        """A closure running one fused launch at M = m on copy i % copies."""
+        import torch
+        dgt = self.dgt
+        xm = self.x[:m].contiguous()
+        if m not in self._ws:
+            self._ws[m] = (dgt.alloc_workspace(dgt.dgt_gemm_workspace(self.layers[0], m),
+                                               self.dev),
+                           torch.empty((m, self.wl.n), dtype=torch.float32, device=self.dev))
+        ws, y = self._ws[m]
+
+        def run(i):
+            dgt.dgt_fused_decode_gemm(self.layers[i % self.copies], xm, scales=self.scales,
+                                      w_scale=self.d["w_scale"], y=y, ws=ws, stream=stream)
+        return run
+
+
+def compress(dgt, name):
+    import workloads
+    d = workloads.make(name)
+    wl = d["workload"]
+    t0 = time.perf_counter()
+    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    return d, blob, time.perf_counter() - t0
+
+
+def entropy_over(wl, d, info):
+    """Empirical entropy of the coded symbols per weight (+ raw bits) and the
+    blob's excess over it."""
     from oracle import blob as oblob
-    from oracle import gemm as ogemm
-    from oracle import numerics
-    h = oblob.parse(blob)
-    kt = wl.k // wl.tile_k
-    strips = wl.n // wl.tile_n
-    tiles = list(range(strips * kt))
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        syms = oblob.decode_symbols(blob, tiles)
-        raw = np.frombuffer(blob, np.uint8, len(tiles) * wl.tile_n * wl.tile_k,
-                            h["raw_off"]).reshape(len(tiles), -1)
-        from oracle import order
-        rows = strips * wl.tile_n
-        if wl.fmt == 7:  # high-byte pairs: symbol = hi[2c] | hi[2c+1] << 8
-            pairs = order.scatter_tiles(syms.astype(np.uint16), rows, wl.k // 2, wl.tile_n,
-                                        wl.tile_k // 2, wl.lanes, epl=4)
-            hi = np.empty((rows, wl.k), np.uint16)
-            hi[:, 0::2] = pairs & 0xFF
-            hi[:, 1::2] = pairs >> 8
+    from oracle import entropy as oentropy
+    sym, raw = oblob.symbolise(wl.fmt, d["codes"])
+    h = oentropy.empirical_entropy(sym, oblob.alphabet_of(wl.fmt)) / oblob.weights_per_symbol(wl.fmt)
+    raw_bits = 8.0 if raw is not None else 0.0
+    return round(h, 4), round(info.bits_per_weight - h - raw_bits, 4)
+
+
+def summary_line(dgt, name, dev, stream, reps, ms_list=(1, 256)):
+    """M = 1 and M = 256 figures of another workload (compressed on the spot)."""
+    d, blob, _ = compress(dgt, name)
+    r = Resident(dgt, name, d, blob, dev)
+    wl = r.wl
+    out = {"workload": "%s: W %dx%d %s, tiles %dx%d, R=%d" % (name, wl.n, wl.k, wl.note,
+                                                             wl.tile_n, wl.tile_k, wl.lanes),
+           "bits_per_weight": round(r.info.bits_per_weight, 4)}
+    h, over = entropy_over(wl, d, r.info)
+    out["entropy_bits"], out["bits_over_entropy"] = h, over
+    nk = wl.n * wl.k
+    for m in ms_list:
+        if m > d["x"].shape[0]:
+            continue
+        ms = timed(r.call(m, stream), reps, 3, stream)
+        out["fused_m%d_ms" % m] = round(ms, 4)
+        if m == 1:
+            out["decoded_gbs_m1"] = round(nk * STORAGE_BYTES[wl.fmt] / (ms * 1e-3) / 1e9, 3)
+            out["hbm_frac_m1"] = round((len(blob) + wl.k * 2 + wl.n * 4) / (ms * 1e-3) / 1e9
+                                       / HBM_PEAK_GBS, 4)
         else:
-            hi = order.scatter_tiles(syms.astype(np.uint8), rows, wl.k, wl.tile_n, wl.tile_k,
-                                     wl.lanes)
-        lo = order.scatter_tiles(raw, rows, wl.k, wl.tile_n, wl.tile_k, wl.lanes, raw=True)
-        w = (hi.astype(np.uint16) << 8) | lo
-        y = ogemm.gemm_fp64(numerics.bf16_bits_to_f64(d["x"][:1]), numerics.bf16_bits_to_f64(w))
-        dt = time.perf_counter() - t0
-    assert np.array_equal(w, d["codes"][:rows])
-    weights = rows * wl.k
-    return {"value": round(weights * 2 / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "%d of %d tiles (rows 0..%d, all K), decode + fp64 GEMV, %.1f s, "
-                      "1 thread (numpy, BLAS limited to 1)" % (len(tiles), wl.n // wl.tile_n * kt,
-                                                               rows - 1, dt),
-            "seconds": round(dt, 3), "checksum": float(np.abs(y).sum())}
+            out["fused_m%d_tflops" % m] = round(2.0 * m * nk / (ms * 1e-3) / 1e12, 3)
+    del r
+    return out
 
 
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path; "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would "
+              "hold its own shard of the layer); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import torch
-
     import decode_gemm_tile_amd as dgt
     import workloads
-    from oracle import entropy as oentropy
 
+    wl = workloads.WORKLOADS[args.workload]
+    d, blob, encode_s = compress(dgt, args.workload)
+    info = dgt.dgt_layer_info(blob)
+    cpu = None
+    if not args.no_cpu_baseline and wl.fmt in (4, 7):
+        cpu = cpu_baseline(d, wl, blob)  # before the GPU is touched (forked workers)
+
+    import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    wl = workloads.WORKLOADS[args.workload]
-    d = workloads.make(args.workload)
-    t0 = time.perf_counter()
-    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
-    encode_s = time.perf_counter() - t0
-    info = dgt.dgt_layer_info(blob)
-    wide = wl.fmt in (4, 6, 7)  # bf16 layers: one uint16 code per weight
-    sym = (np.asarray(d["codes"]) >> 8).astype(np.uint8) if wl.fmt in (4, 7) else None
-    h_hi = oentropy.empirical_entropy(sym, 256) if sym is not None else None
+    res = Resident(dgt, args.workload, d, blob, dev)
+    copies = res.copies
 
-    copies = max(2, math.ceil(ROTATE_BYTES / len(blob)))
-    layers = [dgt.DeviceLayer(blob, dev) for _ in range(copies)]
-    xall = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
-    scales = (torch.from_numpy(d["scales"].view(np.int16)).to(dev)
-              if d["scales"] is not None else None)
-
-    # ---- headline: fused kernel at M = 1
-    m = 1
-    x1 = xall[:m].contiguous()
-    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layers[0], m), dev)
-    y = torch.empty((m, wl.n), dtype=torch.float32, device=dev)
-
-    def fused(i, x=x1, y=y, ws=ws):
-        dgt.dgt_fused_decode_gemm(layers[i % copies], x, scales=scales, w_scale=d["w_scale"],
-                                  y=y, ws=ws, stream=stream)
-
+    # ---- headline: the fused kernel at M = args.m (1 for the metric)
+    m = args.m
+    fused = res.call(m, stream)
     ms = timed(fused, args.steps, args.warmup, stream)
     dist = launch_distribution(fused, 50, stream)
     nk = wl.n * wl.k
-    # decoded-weight bytes at the format's storage width (int4 half a byte)
-    decoded_bytes = nk * {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0, 7: 2.0}[wl.fmt]
+    decoded_bytes = nk * STORAGE_BYTES[wl.fmt]
     value = decoded_bytes / (ms * 1e-3) / 1e9
     alg_bytes = len(blob) + m * wl.k * 2 + m * wl.n * 4
+    if d["scales"] is not None:
+        alg_bytes += d["scales"].nbytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles("k_fused", args.workload, alg_bytes)
 
     result = {
         "metric": METRIC,
@@ -216,67 +335,59 @@ def main():
                    "m": m, "n": wl.n, "k": wl.k, "blob_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic_from_profiles(args.workload, m),
                      "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes": alg_bytes,
                      "per_launch": dist, "source_hash": source_hash()},
     }
+    h, over = entropy_over(wl, d, info)
+    secondary = {"bits_per_weight": round(info.bits_per_weight, 4), "entropy_bits": h,
+                 "bits_over_entropy": over, "compressed_bytes": len(blob),
+                 "encode_seconds": round(encode_s, 3)}
 
-    secondary = {"bits_per_weight": round(info.bits_per_weight, 4),
-                 "compressed_bytes": len(blob), "encode_seconds": round(encode_s, 3)}
-    if h_hi is not None:
-        secondary["entropy_hi_byte_bits"] = round(h_hi, 4)
-        secondary["bits_over_entropy"] = round(info.bits_per_weight - (h_hi + 8.0), 4)
     if not args.no_secondary:
-        # fused at M = 256 (TFLOP/s; the workload's largest M if smaller) and
-        # the uncompressed baseline at M = 1 and that M
-        m2 = min(256, xall.shape[0])
-        x2 = xall[:m2].contiguous()
-        ws2 = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layers[0], m2), dev)
-        y2 = torch.empty((m2, wl.n), dtype=torch.float32, device=dev)
-        ms2 = timed(lambda i: dgt.dgt_fused_decode_gemm(layers[i % copies], x2, scales=scales,
-                                                        w_scale=d["w_scale"], y=y2, ws=ws2,
-                                                        stream=stream),
-                    max(5, args.steps // 10), 3, stream)
+        reps = max(5, args.steps // 10)
+        m2 = min(256, d["x"].shape[0])
+        ms2 = timed(res.call(m2, stream), reps, 3, stream)
         flops = 2.0 * m2 * nk
         secondary["fused_m%d_ms" % m2] = round(ms2, 4)
         secondary["fused_m%d_tflops" % m2] = round(flops / (ms2 * 1e-3) / 1e12, 3)
         secondary["fused_m%d_mfma_frac" % m2] = round(
             flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        wide = wl.fmt in (4, 6, 7)
         codes = np.asarray(d["codes"])
         wraw = torch.from_numpy(codes.view(np.int16) if wide else codes.view(np.uint8)).to(dev)
         dcopies = max(2, math.ceil(ROTATE_BYTES / (nk * 2)))
         wd = [wraw.clone() for _ in range(dcopies)]
         del wraw
-        dec = torch.empty((wl.n, wl.k), dtype=torch.int16 if wide else torch.uint8,
-                          device=dev)
-        reps = max(5, args.steps // 10)
+        dec = torch.empty((wl.n, wl.k), dtype=torch.int16 if wide else torch.uint8, device=dev)
         ablation = {}
         for mm in sorted({1, m2}):
-            xm = xall[:mm].contiguous()
-            wsd = dgt.alloc_workspace(dgt.dgt_dense_workspace(wl.fmt, wl.n, wl.k, wl.tile_n, mm), dev)
+            xm = res.x[:mm].contiguous()
+            wsd = dgt.alloc_workspace(dgt.dgt_dense_workspace(wl.fmt, wl.n, wl.k, wl.tile_n, mm),
+                                      dev)
             yd = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
             msd = timed(lambda i: dgt.dgt_dense_gemm(wl.fmt, wd[i % dcopies], xm,
-                                                     tile_n=wl.tile_n, scales=scales,
+                                                     tile_n=wl.tile_n, scales=res.scales,
                                                      w_scale=d["w_scale"], y=yd, ws=wsd,
-                                                     stream=stream),
-                        reps, 3, stream)
+                                                     stream=stream), reps, 3, stream)
+            ms_fused = ms if mm == m else secondary["fused_m%d_ms" % mm] if mm == m2 else \
+                timed(res.call(mm, stream), reps, 3, stream)
             secondary["dense_m%d_ms" % mm] = round(msd, 4)
             if mm == 1:
                 secondary["dense_m1_weight_gbs"] = round(nk * 2 / (msd * 1e-3) / 1e9, 3)
-                secondary["fused_speedup_vs_dense_m1"] = round(msd / ms, 3)
+                secondary["fused_speedup_vs_dense_m1"] = round(msd / ms_fused, 3)
             else:
                 secondary["dense_m%d_tflops" % mm] = round(2.0 * mm * nk / (msd * 1e-3) / 1e12, 3)
             # ablation: layer-level decode to HBM, then the dense GEMM on the
             # decoded copy (two launches per step) against the fused kernel
-            ms_dec = timed(lambda i: dgt.dgt_decode_tiles(layers[i % copies], out=dec,
+            ms_dec = timed(lambda i: dgt.dgt_decode_tiles(res.layers[i % copies], out=dec,
                                                           stream=stream), reps, 3, stream)
 
             def two_stage(i, xm=xm, yd=yd, wsd=wsd):
-                dgt.dgt_decode_tiles(layers[i % copies], out=dec, stream=stream)
-                dgt.dgt_dense_gemm(wl.fmt, dec, xm, tile_n=wl.tile_n, scales=scales,
+                dgt.dgt_decode_tiles(res.layers[i % copies], out=dec, stream=stream)
+                dgt.dgt_dense_gemm(wl.fmt, dec, xm, tile_n=wl.tile_n, scales=res.scales,
                                    w_scale=d["w_scale"], y=yd, ws=wsd, stream=stream)
             ms_two = timed(two_stage, reps, 3, stream)
-            ms_fused = ms if mm == 1 else secondary["fused_m%d_ms" % mm]
             ablation["m%d" % mm] = {"decode_to_hbm_ms": round(ms_dec, 4),
                                     "two_stage_ms": round(ms_two, 4),
                                     "fused_ms": round(ms_fused, 4),
@@ -286,17 +397,14 @@ def main():
                 # large-M kernel (the library reads the switch at every call)
                 os.environ["DGT_XM_SINGLE_BUFFER"] = "1"
                 try:
-                    ms_one = timed(lambda i: dgt.dgt_fused_decode_gemm(
-                        layers[i % copies], xm, scales=scales, w_scale=d["w_scale"], y=y2,
-                        ws=ws2, stream=stream), reps, 3, stream)
+                    ms_one = timed(res.call(mm, stream), reps, 3, stream)
                 finally:
                     del os.environ["DGT_XM_SINGLE_BUFFER"]
                 ablation["m%d" % mm]["fused_single_buffer_ms"] = round(ms_one, 4)
                 ablation["m%d" % mm]["ping_pong_speedup"] = round(ms_one / ms_fused, 3)
-            # vendor GEMM on the uncompressed bf16 weight (reference point only),
-            # alone and after the layer-level decode (the two-stage path with
-            # the vendor library's GEMM on the decoded copy)
             if wide:
+                # vendor GEMM on the uncompressed bf16 weight (reference point
+                # only), alone and after the layer-level decode
                 wts = [w.view(torch.bfloat16).t().contiguous() for w in wd]
                 ms_lib = timed(lambda i: torch.matmul(xm, wts[i % len(wts)]), reps, 3, stream)
                 secondary["torch_matmul_bf16_m%d_ms" % mm] = round(ms_lib, 4)
@@ -304,11 +412,12 @@ def main():
                 decb = dec.view(torch.bfloat16)
 
                 def two_stage_vendor(i, xm=xm):
-                    dgt.dgt_decode_tiles(layers[i % copies], out=dec, stream=stream)
+                    dgt.dgt_decode_tiles(res.layers[i % copies], out=dec, stream=stream)
                     torch.nn.functional.linear(xm, decb)  # x @ W^T, W [N, K] as decoded
                 ms_tv = timed(two_stage_vendor, reps, 3, stream)
                 ablation["m%d" % mm]["two_stage_vendor_gemm_ms"] = round(ms_tv, 4)
-                ablation["m%d" % mm]["fused_speedup_vs_two_stage_vendor"] = round(ms_tv / ms_fused, 3)
+                ablation["m%d" % mm]["fused_speedup_vs_two_stage_vendor"] = round(
+                    ms_tv / ms_fused, 3)
         secondary["ablation"] = ablation
         del wd, dec
         # the same layer in the other codings of its family: bits and time
@@ -321,21 +430,22 @@ def main():
             variants.append(("two_states_per_lane", wl.fmt, 128))
         for vname, vfmt, vlanes in variants:
             blob2 = dgt.dgt_compress_layer(vfmt, d["codes"], wl.tile_n, wl.tile_k, vlanes)
-            c2 = max(2, math.ceil(ROTATE_BYTES / len(blob2)))
-            l2 = [dgt.DeviceLayer(blob2, dev) for _ in range(c2)]
-            var = {"fmt": vfmt, "lanes": vlanes,
-                   "bits_per_weight": round(dgt.dgt_layer_info(blob2).bits_per_weight, 4)}
-            for mm, xm_ in ((1, x1), (m2, x2)):
-                wsr = dgt.alloc_workspace(dgt.dgt_gemm_workspace(l2[0], mm), dev)
-                yr = torch.empty((mm, wl.n), dtype=torch.float32, device=dev)
-                var["fused_m%d_ms" % mm] = round(timed(
-                    lambda i: dgt.dgt_fused_decode_gemm(l2[i % c2], xm_, scales=scales,
-                                                        w_scale=d["w_scale"], y=yr, ws=wsr,
-                                                        stream=stream),
-                    reps, 3, stream), 4)
+            dv = dict(d)
+            dv["workload"] = workloads.Workload(wl.name, vfmt, wl.n, wl.k, wl.tile_n, wl.tile_k,
+                                                vlanes, wl.seed, wl.m_values, note=wl.note)
+            r2 = Resident(dgt, args.workload, dv, blob2, dev)
+            var = {"fmt": vfmt, "lanes": vlanes, "bits_per_weight": round(r2.info.bits_per_weight, 4)}
+            for mm in (1, m2):
+                var["fused_m%d_ms" % mm] = round(timed(r2.call(mm, stream), reps, 3, stream), 4)
             var["decoded_gbs_m1"] = round(decoded_bytes / (var["fused_m1_ms"] * 1e-3) / 1e9, 3)
             secondary[vname] = var
-            del l2
+            del r2
+        # the other configurations the metric is quoted on
+        others = {}
+        for other in ("int4_ffn405", "bf16_mlp"):
+            if other != args.workload:
+                others[other] = summary_line(dgt, other, dev, stream, reps)
+        secondary["other_workloads"] = others
     result["secondary"] = secondary
 
     if args.copy_calib:
@@ -346,8 +456,8 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = a.numel()
 
-    if not args.no_cpu_baseline and wl.fmt in (4, 7):
-        result["cpu_baseline"] = cpu_baseline(d, wl, blob)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 

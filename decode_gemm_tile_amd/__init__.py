@@ -102,6 +102,50 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Argument checks made before anything is launched: the C ABI receives raw
+# device pointers and cannot tell a tensor's shape, dtype, layout or device.
+_TWO_BYTE = ("torch.bfloat16", "torch.int16", "torch.uint16", "torch.float16")
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name, shape, dtypes, device):
+    """t must be a contiguous tensor of one of `dtypes` (by name), with
+    `shape` (None entries are free), on `device`."""
+    _need(t is not None, "%s is required" % name)
+    _need(hasattr(t, "data_ptr") and hasattr(t, "is_contiguous"), "%s must be a tensor" % name)
+    _need(str(t.dtype) in dtypes, "%s has dtype %s, expected one of %s"
+          % (name, t.dtype, ", ".join(dtypes)))
+    _need(t.dim() == len(shape) and all(s is None or s == d for s, d in zip(shape, t.shape)),
+          "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    _need(t.is_contiguous(), "%s must be contiguous" % name)
+    _need(t.device == device, "%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _check_gpu(device):
+    """Checked after every argument's shape and dtype: all of them live on
+    `device`, which must be a GPU."""
+    _need(device.type == "cuda", "arguments must be in GPU memory (the library has no CPU path)")
+
+
+def _check_status(status, tiles, device):
+    if status is not None:
+        _check_tensor(status, "status", (None,), ("torch.int32",), device)
+        _need(status.numel() >= tiles, "status holds %d entries, the layer has %d tiles"
+              % (status.numel(), tiles))
+
+
+def _check_scales(fmt, scales, n, k, device):
+    if fmt in (DGT_FMT_INT4, DGT_FMT_INT4_PAIR):
+        _need(k % 128 == 0, "int4 layers need K divisible by 128 (one scale per 128 columns)")
+        _check_tensor(scales, "scales", (n, k // 128), _TWO_BYTE, device)
+    else:
+        _need(scales is None, "scales are only taken by the int4 formats")
+
+
 # ----------------------------------------------------------------- host side
 def dgt_version() -> int:
     return lib().dgt_version()
@@ -160,15 +204,32 @@ def dgt_decode_tiles(layer: DeviceLayer, tile_ids=None, out=None, status=None, s
     import torch
     inf = layer.info
     dev = layer.blob.device
+    wide = inf.fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
     if out is None:
-        dt = (torch.int16 if inf.fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
-              else torch.uint8)
-        out = torch.zeros((inf.n, inf.k), dtype=dt, device=dev)
+        out = torch.zeros((inf.n, inf.k), dtype=torch.int16 if wide else torch.uint8, device=dev)
+    _check_tensor(out, "out", (inf.n, inf.k), _TWO_BYTE if wide else ("torch.uint8", "torch.int8"),
+                  dev)
+    _check_status(status, inf.tiles, dev)
     ids = None
     n_ids = 0
     if tile_ids is not None:
-        ids = torch.as_tensor(tile_ids, dtype=torch.int32).to(dev)
+        if isinstance(tile_ids, torch.Tensor):
+            ids = tile_ids
+        else:
+            a = np.asarray(tile_ids)
+            _need(a.dtype.kind in "iub" or a.size == 0, "tile_ids must be a 1-D integer list")
+            ids = torch.from_numpy(a.astype(np.int64).reshape(a.shape))
+        _need(ids.dim() == 1 and not ids.is_floating_point(), "tile_ids must be a 1-D integer list")
+        if ids.numel():
+            lo, hi = int(ids.min()), int(ids.max())
+            _need(0 <= lo and hi < inf.tiles, "tile ids must lie in [0, %d); got %d..%d"
+                  % (inf.tiles, lo, hi))
+        _check_gpu(dev)
+        ids = ids.to(dtype=torch.int32, device=dev).contiguous()
         n_ids = ids.numel()
+        if n_ids == 0:
+            return out
+    _check_gpu(dev)
     _check(lib().dgt_decode_tiles(_ptr(layer.blob), ctypes.byref(inf), _ptr(ids), n_ids,
                                   _ptr(out), _ptr(status), _stream(stream)),
            "dgt_decode_tiles")
@@ -189,11 +250,20 @@ def dgt_fused_decode_gemm(layer: DeviceLayer, x, scales=None, w_scale=1.0, y=Non
     """Y[m, n] = sum_k X[m, k] W[n, k] with W decoded on chip; x: bf16 [M, K]."""
     import torch
     inf = layer.info
+    dev = layer.blob.device
+    _check_tensor(x, "x", (None, inf.k), ("torch.bfloat16",), dev)
     m = x.shape[0]
+    _need(1 <= m, "x needs at least one row")
     if y is None:
-        y = torch.empty((m, inf.n), dtype=torch.float32, device=x.device)
+        y = torch.empty((m, inf.n), dtype=torch.float32, device=dev)
+    _check_tensor(y, "y", (m, inf.n), ("torch.float32",), dev)
+    _check_scales(inf.fmt, scales, inf.n, inf.k, dev)
+    _check_status(status, inf.tiles, dev)
+    if ws is not None:
+        _check_tensor(ws, "ws", (None,), ("torch.uint8",), dev)
+    _check_gpu(dev)
     if ws is None:
-        ws = alloc_workspace(dgt_gemm_workspace(layer, m), x.device)
+        ws = alloc_workspace(dgt_gemm_workspace(layer, m), dev)
     _check(lib().dgt_fused_decode_gemm(_ptr(layer.blob), ctypes.byref(inf), _ptr(x), m,
                                        _ptr(scales), float(w_scale), _ptr(y), _ptr(ws),
                                        ws.numel(), _ptr(status), _stream(stream)),
@@ -209,12 +279,22 @@ def dgt_dense_gemm(fmt, w, x, tile_n=128, scales=None, w_scale=1.0, y=None, ws=N
                    stream=None):
     """Uncompressed baseline; w: device [N, K] (uint8 codes or bf16 bits)."""
     import torch
+    wide = fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
+    _need(hasattr(w, "shape") and w.dim() == 2, "w must be a 2-D tensor [N, K]")
     n, k = w.shape
+    dev = w.device
+    _check_tensor(w, "w", (n, k), _TWO_BYTE if wide else ("torch.uint8", "torch.int8"), dev)
+    _check_tensor(x, "x", (None, k), ("torch.bfloat16",), dev)
     m = x.shape[0]
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    _check_tensor(y, "y", (m, n), ("torch.float32",), dev)
+    _check_scales(fmt, scales, n, k, dev)
+    if ws is not None:
+        _check_tensor(ws, "ws", (None,), ("torch.uint8",), dev)
+    _check_gpu(dev)
     if ws is None:
-        ws = alloc_workspace(dgt_dense_workspace(fmt, n, k, tile_n, m), x.device)
+        ws = alloc_workspace(dgt_dense_workspace(fmt, n, k, tile_n, m), dev)
     _check(lib().dgt_dense_gemm(fmt, n, k, tile_n, _ptr(w), _ptr(x), m, _ptr(scales),
                                 float(w_scale), _ptr(y), _ptr(ws), ws.numel(),
                                 _stream(stream)), "dgt_dense_gemm")

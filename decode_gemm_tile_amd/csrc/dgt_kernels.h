@@ -1131,6 +1131,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
 
   Chain ch[ILP];
   uint32_t tile_lane[ILP];
+  bool id_ok[ILP];  // the lane's tile id names a tile of the layer
   Staged stg[ILP];  // whole streams
   Ring rg[ILP];     // ring
   uint32_t c0[ILP][4];
@@ -1145,7 +1146,10 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     const uint32_t ib = min(first + c * TPC + 1, a.n_ids - 1);
     const uint32_t ta = a.ids ? a.ids[ia] : ia;
     const uint32_t tb = (R == 32) ? (a.ids ? a.ids[ib] : ib) : ta;
-    const uint32_t t_l = (R == 32 && upper) ? tb : ta;
+    const uint32_t t_id = (R == 32 && upper) ? tb : ta;
+    // an id past the layer decodes tile 0 in its place and writes nothing
+    id_ok[c] = t_id < L.tiles;
+    const uint32_t t_l = id_ok[c] ? t_id : 0u;
     tile_lane[c] = t_l;
     if constexpr (RING)
       ring_issue(L, t_l, lane, rg[c], c0[c]);
@@ -1220,6 +1224,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
     for (int c = 0; c < ILP; ++c)
 #pragma unroll
       for (int h = 0; h < NS; ++h) {
+        if (!id_ok[c]) continue;
         const uint32_t t = tile_lane[c];
         const uint32_t row = (t / L.kt) * L.tile_n + (h * FNH + fn) * 16 + (p & 15);
         const uint32_t col = (t % L.kt) * L.tile_k + fk * FW + 8 * (p >> 4);
@@ -1254,7 +1259,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t f = final_flags<R, RING>(ch[c], L.steps, upper);
-      if (R != 32 ? lane == 0 : half_lane == 0) a.status[tile_lane[c]] = (int32_t)f;
+      if ((R != 32 ? lane == 0 : half_lane == 0) && id_ok[c]) a.status[tile_lane[c]] = (int32_t)f;
     }
   }
 }

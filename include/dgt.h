@@ -151,6 +151,9 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out);
  * as what the fused path avoids).
  *   d_blob: device copy of the blob described by `info`.
  *   d_tile_ids: n_ids tile ids to decode, or NULL for all tiles (n_ids ignored).
+ *          An id >= the layer's tile count is skipped on the device: nothing
+ *          is written for it (neither d_out nor d_status), and the reads made
+ *          in its place stay inside the blob (tile 0's stream).
  *   d_out: the full W layout, row-major [N, K]: uint8 (INT8 bytes, INT4
  *          and INT4_PAIR codes, FP8 bytes) or uint16 bf16 bits (BF16_SPLIT,
  *          BF16_EXP);

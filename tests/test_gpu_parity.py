@@ -373,11 +373,63 @@ def test_corrupt_stream_sets_status_and_stays_in_bounds(R, staging, monkeypatch)
             b[start + 2 * j] ^= 0xA5
     layer = dgt.DeviceLayer(bytes(b))
     status = torch.full((info.tiles,), -1, dtype=torch.int32, device="cuda")
-    dgt.dgt_decode_tiles(layer, status=status)
+    # the output sits inside a larger buffer whose guard rows must stay untouched
+    buf = torch.full((info.n + 32, info.k), 0x5A, dtype=torch.uint8, device="cuda")
+    dgt.dgt_decode_tiles(layer, out=buf[16:16 + info.n], status=status)
     torch.cuda.synchronize()
     st = status.cpu().numpy()
     assert all(st[t] != 0 for t in bad_tiles)
     assert all(st[t] == 0 for t in range(info.tiles) if t not in bad_tiles)
+    host = buf.cpu().numpy()
+    assert (host[:16] == 0x5A).all() and (host[16 + info.n:] == 0x5A).all()
+    # tiles whose streams are intact still decode exactly
+    got = host[16:16 + info.n]
+    want = codes_as_u8_or_u16(F8, d["codes"])
+    kt = info.k // info.tile_k
+    for t in range(info.tiles):
+        if t in bad_tiles:
+            continue
+        r0, c0 = (t // kt) * info.tile_n, (t % kt) * info.tile_k
+        assert np.array_equal(got[r0:r0 + info.tile_n, c0:c0 + info.tile_k],
+                              want[r0:r0 + info.tile_n, c0:c0 + info.tile_k]), t
+
+
+@pytest.mark.parametrize("R", [32, 64, 128])
+def test_decode_tiles_skips_ids_past_the_layer(R):
+    """Tile ids >= the tile count reach the C ABI (the binding would refuse
+    them): the kernel decodes the valid ids and writes nothing for the others,
+    neither output nor status."""
+    import ctypes
+    import torch
+    d, blob = _layer(F8, 256, 512, 128, 64 if R != 32 else 32, R, 52)
+    layer = dgt.DeviceLayer(blob)
+    info = layer.info
+    valid = [info.tiles - 1, 2, 0]
+    raw_ids = valid[:1] + [info.tiles, 0xFFFFFFFF] + valid[1:] + [info.tiles + 7]
+    ids = torch.tensor(np.array(raw_ids, np.uint32).view(np.int32), device="cuda")
+    buf = torch.full((info.n + 32, info.k), 0x5A, dtype=torch.uint8, device="cuda")
+    status = torch.full((info.tiles + 8,), -1, dtype=torch.int32, device="cuda")
+    rc = dgt.lib().dgt_decode_tiles(ctypes.c_void_p(layer.blob.data_ptr()), ctypes.byref(info),
+                                    ctypes.c_void_p(ids.data_ptr()), len(raw_ids),
+                                    ctypes.c_void_p(buf[16:].data_ptr()),
+                                    ctypes.c_void_p(status.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    st = status.cpu().numpy()
+    assert (host[:16] == 0x5A).all() and (host[16 + info.n:] == 0x5A).all()
+    got = host[16:16 + info.n]
+    want = codes_as_u8_or_u16(F8, d["codes"])
+    kt = info.k // info.tile_k
+    mask = np.zeros(got.shape, bool)
+    for t in valid:
+        r0, c0 = (t // kt) * info.tile_n, (t % kt) * info.tile_k
+        mask[r0:r0 + info.tile_n, c0:c0 + info.tile_k] = True
+    assert np.array_equal(got[mask], want[mask])
+    assert (got[~mask] == 0x5A).all()
+    assert all(st[t] == 0 for t in valid)
+    assert all(st[t] == -1 for t in range(info.tiles + 8) if t not in valid)
 
 
 def test_argument_errors():
@@ -392,3 +444,68 @@ def test_argument_errors():
     with pytest.raises(dgt.DgtError) as e:
         dgt.dgt_fused_decode_gemm(layer, big)
     assert e.value.code == -1
+
+
+def _fp8_layer_from_codes(codes, tn, tk, R):
+    blob = dgt.dgt_compress_layer(FE, codes, tn, tk, R)
+    return dgt.DeviceLayer(blob)
+
+
+def _bf16_bits(values):
+    import torch
+    return torch.tensor(np.asarray(values, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("tn,tk,R", [(256, 64, 64), (128, 32, 32), (128, 64, 128)])
+@pytest.mark.parametrize("m", [3, 40, 200])
+def test_fp8_activation_quant_bit_exact(tn, tk, R, m):
+    """The device's per-tensor e4m3 quantisation of X, read through a layer
+    whose weights are the identity (e4m3 1.0 on the diagonal): Y[m, j] is
+    fl32(xq[m, j] * sx) exactly.  X's maximum is 0.5234375, and it holds values
+    whose product with inv rounds across an e4m3 boundary only in fp32, so the
+    device must round x * inv to fp32 before the e4m3 rounding, as the oracle
+    does.  M = 3 and 40 quantise in one workgroup, M = 200 in two launches."""
+    import torch
+    from oracle import numerics
+    n = k = 512
+    codes = np.zeros((n, k), np.uint8)
+    codes[np.arange(n), np.arange(k)] = 0x38
+    layer = _fp8_layer_from_codes(codes, tn, tk, R)
+    rng = np.random.default_rng(70 + m)
+    v = rng.uniform(-0.5, 0.5, (m, k)) * np.exp2(rng.integers(-14, 1, (m, k)))
+    v[0, :4] = [0.5234375, 2.396106719970703e-05, -4.792213439941406e-05, 2.0742416381835938e-05]
+    xb = _bf16_bits(v)
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), w_scale=1.0)
+    torch.cuda.synchronize()
+    xq, sx = numerics.fp8_quantize_activations(xb)
+    want = (numerics.e4m3_to_f64(xq) * sx).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("tn,tk,R", [(256, 64, 64), (128, 32, 32)])
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_fp8_exact_integer_gemm(tn, tk, R, m):
+    """amax|X| = 448 makes inv = sx = 1; X holds integers in [-16, 16] and e4m3
+    midpoints (1.0625 -> 1, 1.1875 -> 1.25 under ties-to-even), W small integers:
+    every partial sum is a multiple of 1/4 below 2^17, so Y is exact."""
+    import torch
+    from oracle import numerics
+    n, k = 512, 512
+    rng = np.random.default_rng(80 + m)
+    wv = rng.integers(-8, 9, (n, k)).astype(np.float64)
+    codes = numerics.f64_to_e4m3(wv)
+    xv = rng.integers(-16, 17, (m, k)).astype(np.float64)
+    xv[0, 0] = 448.0
+    xv[:, 1] = 1.0625
+    xv[:, 2] = -1.1875
+    xb = _bf16_bits(xv)
+    layer = _fp8_layer_from_codes(codes, tn, tk, R)
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), w_scale=1.0)
+    torch.cuda.synchronize()
+    xq = np.round(xv)  # the e4m3 values of X: integers, with the two midpoints below
+    xq[:, 1] = 1.0
+    xq[:, 2] = -1.25
+    want = ogemm.gemm_fp64(xq, wv)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
+    assert np.array_equal(ogemm.reference_output(FE, codes, xb, w_scale=1.0), want)

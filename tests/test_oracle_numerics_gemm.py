@@ -70,6 +70,66 @@ def test_int4_dequant_matches_torch():
     assert np.array_equal(ours, ref.view(torch.int16).numpy().view(np.uint16))
 
 
+def _torch_fp8_quant(bits):
+    """The same per-tensor quantisation in torch CPU float32: inv = 448 / amax
+    and sx = amax / 448 as fp32 divisions (correctly rounded), the product
+    x * inv in fp32, then torch's e4m3 cast (round to nearest even)."""
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).float()
+    amax = x.abs().max()
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    sx = amax / torch.tensor(448.0, dtype=torch.float32)
+    q = (x * inv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, float(sx)
+
+
+def _bf16_bits(values):
+    return torch.tensor(values, dtype=torch.float32).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("seed,scale", [(2, 1.0), (3, 1e-3), (4, 300.0), (5, 0.0)])
+def test_fp8_activation_quant_bit_exact_against_torch_float32(seed, scale):
+    rng = np.random.default_rng(seed)
+    if scale:
+        v = rng.normal(0, scale, (16, 512))
+    else:  # magnitudes spread over 2^-30 .. 2^8, so the e4m3 subnormals are hit
+        v = np.exp2(rng.uniform(-30, 8, (16, 512))) * rng.choice([-1.0, 1.0], (16, 512))
+    bits = _bf16_bits(v)
+    xq, sx = numerics.fp8_quantize_activations(bits)
+    rq, rsx = _torch_fp8_quant(bits)
+    assert np.array_equal(xq, rq)
+    assert sx == rsx
+
+
+def test_fp8_activation_quant_ties_round_to_even():
+    # amax = 448 makes inv = 1 exactly: these bf16 values are e4m3 midpoints
+    x = [448.0, 1.0625, 1.1875, -1.0625, 432.0, 2.0 ** -10, 3 * 2.0 ** -10, 0.0]
+    want = [0x7E, 0x38, 0x3A, 0xB8, 0x7E, 0x00, 0x02, 0x00]
+    bits = _bf16_bits(x)
+    xq, sx = numerics.fp8_quantize_activations(bits)
+    assert sx == 1.0 and xq.tolist() == want
+    assert _torch_fp8_quant(bits)[0].tolist() == want
+
+
+# (amax, x) where the exact x * inv and its fp32 rounding fall on different
+# sides of an e4m3 rounding boundary: only the fp32 product gives torch's code
+FP32_STEP_CASES = [(0.5234375, 2.396106719970703e-05), (0.5234375, 4.792213439941406e-05),
+                   (3.171875, 2.0742416381835938e-05), (29.125, 0.0004444122314453125),
+                   (0.0002269744873046875, 4.94765117764473e-10)]
+
+
+@pytest.mark.parametrize("amax,x", FP32_STEP_CASES)
+def test_fp8_activation_quant_rounds_the_product_to_fp32_first(amax, x):
+    bits = _bf16_bits([amax, x, -x])
+    xq, sx = numerics.fp8_quantize_activations(bits)
+    rq, rsx = _torch_fp8_quant(bits)
+    assert xq.tolist() == rq.tolist() and sx == rsx
+    # the product rounded straight from its exact value would give another code
+    inv = float(np.float32(448.0 / float(numerics.bf16_bits_to_f64(bits[:1])[0])))
+    exact = float(numerics.bf16_bits_to_f64(bits[1:2])[0]) * inv
+    assert int(numerics.f64_to_e4m3(np.array([exact]))[0]) != int(xq[1])
+
+
 def test_fp8_activation_quant_properties():
     rng = np.random.default_rng(2)
     x = torch.from_numpy(rng.normal(0, 1, (8, 512)).astype(np.float32)).to(torch.bfloat16)
@@ -136,3 +196,29 @@ def test_reference_output_fp8_exact_case():
     wq = numerics.f64_to_e4m3(np.array([[1.0, 2.0, 4.0, 8.0], [-1.0, 0.0, 0.0, 448.0]]))
     y = gemm.reference_output(gemm.FMT_FP8, wq, xb, w_scale=0.5)
     assert y.tolist() == [[0.5 * (448 - 2 + 2), 0.5 * (-448)]]
+
+
+# ------------------------------------------------------------ rel_frobenius
+def test_rel_frobenius_hand_computed():
+    y = np.array([[1.0, 2.0], [3.0, 4.0]])
+    ref = np.array([[1.0, 2.0], [3.0, 5.0]])
+    # |y - ref|_F = 1, |ref|_F = sqrt(1 + 4 + 9 + 25)
+    assert gemm.rel_frobenius(y, ref) == pytest.approx(1.0 / np.sqrt(39.0), rel=1e-15)
+    assert gemm.rel_frobenius(ref, ref) == 0.0
+    # a zero reference: the plain Frobenius norm of the difference
+    assert gemm.rel_frobenius(np.array([[3.0, 4.0]]), np.zeros((1, 2))) == 5.0
+
+
+def test_rel_frobenius_fails_a_perturbed_output():
+    """Negative control of the 1e-5 parity bound: one element off by 2e-5 of
+    the reference's norm, or one element never written (NaN), must fail it."""
+    rng = np.random.default_rng(9)
+    ref = rng.normal(size=(16, 256))
+    y = ref.copy()
+    y[3, 17] += 2e-5 * np.linalg.norm(ref)
+    err = gemm.rel_frobenius(y, ref)
+    assert err == pytest.approx(2e-5, rel=1e-6) and not err <= 1e-5
+    y = ref.astype(np.float32).astype(np.float64)
+    assert gemm.rel_frobenius(y, ref) <= 1e-7  # an fp32 rounding of every element passes
+    y[0, 0] = np.nan
+    assert not gemm.rel_frobenius(y, ref) <= 1e-5
