@@ -23,7 +23,8 @@ STATUS = {0: "DGT_OK", -1: "DGT_E_ARG", -2: "DGT_E_SHAPE", -3: "DGT_E_ALPHABET",
           -8: "DGT_E_UNSUPPORTED"}
 EXPORTS = ["dgt_version", "dgt_status_string", "dgt_compress_bound", "dgt_compress_layer",
            "dgt_layer_info", "dgt_decode_tiles", "dgt_gemm_workspace",
-           "dgt_fused_decode_gemm", "dgt_dense_workspace", "dgt_dense_gemm"]
+           "dgt_fused_decode_gemm", "dgt_dense_workspace", "dgt_dense_gemm",
+           "dgt_noalloc_scratch_bytes", "dgt_fused_decode_gemm_noalloc"]
 
 
 class DgtError(RuntimeError):
@@ -78,6 +79,11 @@ def lib():
         L.dgt_fused_decode_gemm.restype = ctypes.c_int
         L.dgt_fused_decode_gemm.argtypes = [vp, ctypes.POINTER(dgt_info), vp, u32, vp,
                                             ctypes.c_float, vp, vp, sz, vp, vp]
+        L.dgt_noalloc_scratch_bytes.restype = sz
+        L.dgt_noalloc_scratch_bytes.argtypes = []
+        L.dgt_fused_decode_gemm_noalloc.restype = ctypes.c_int
+        L.dgt_fused_decode_gemm_noalloc.argtypes = [vp, ctypes.POINTER(dgt_info), vp, u32, vp,
+                                                    ctypes.c_float, vp, vp, vp]
         L.dgt_dense_workspace.restype = sz
         L.dgt_dense_workspace.argtypes = [u32, u32, u32, u32, u32]
         L.dgt_dense_gemm.restype = ctypes.c_int
@@ -268,6 +274,30 @@ def dgt_fused_decode_gemm(layer: DeviceLayer, x, scales=None, w_scale=1.0, y=Non
                                        _ptr(scales), float(w_scale), _ptr(y), _ptr(ws),
                                        ws.numel(), _ptr(status), _stream(stream)),
            "dgt_fused_decode_gemm")
+    return y
+
+
+def dgt_noalloc_scratch_bytes() -> int:
+    return lib().dgt_noalloc_scratch_bytes()
+
+
+def dgt_fused_decode_gemm_noalloc(layer: DeviceLayer, x, y, scales=None, w_scale=1.0,
+                                  status=None, stream=None):
+    """dgt_fused_decode_gemm on the library's static scratch: no workspace and,
+    given y, no allocation at all."""
+    inf = layer.info
+    dev = layer.blob.device
+    _check_tensor(x, "x", (None, inf.k), ("torch.bfloat16",), dev)
+    m = x.shape[0]
+    _need(1 <= m, "x needs at least one row")
+    _check_tensor(y, "y", (m, inf.n), ("torch.float32",), dev)
+    _check_scales(inf.fmt, scales, inf.n, inf.k, dev)
+    _check_status(status, inf.tiles, dev)
+    _check_gpu(dev)
+    _check(lib().dgt_fused_decode_gemm_noalloc(_ptr(layer.blob), ctypes.byref(inf), _ptr(x), m,
+                                               _ptr(scales), float(w_scale), _ptr(y),
+                                               _ptr(status), _stream(stream)),
+           "dgt_fused_decode_gemm_noalloc")
     return y
 
 

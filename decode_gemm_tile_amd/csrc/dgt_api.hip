@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dgt.h"
 #include "dgt_format.h"
@@ -632,12 +633,15 @@ size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
   return ws;
 }
 
-int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
-                          uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
-                          void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
-  if (!d_blob || !info || !d_x || !d_y || !d_ws || m == 0 || m > kMaxRows) return DGT_E_ARG;
-  if (((uintptr_t)d_blob & 15) || ((uintptr_t)d_x & 15) || ((uintptr_t)d_ws & 255))
-    return DGT_E_ARG;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the fused entry points; fills the call's plan.
+int fused_prepare(const void* d_blob, const dgt_info* info, const uint16_t* d_x, uint32_t m,
+                  const uint16_t* d_scales, float* d_y, CallPlan* c) {
+  if (!d_blob || !info || !d_x || !d_y || m == 0 || m > kMaxRows) return DGT_E_ARG;
+  if (((uintptr_t)d_blob & 15) || ((uintptr_t)d_x & 15)) return DGT_E_ARG;
   int rc = device_supported(info);
   if (rc) return rc;
   if ((info->fmt == DGT_FMT_INT4 || info->fmt == DGT_FMT_INT4_PAIR) &&
@@ -646,13 +650,17 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
   const uint32_t fn = info->tile_n / 16;
   if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
   if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
-  CallPlan c;
-  if (!plan_call(info, m, &c, staging_from_env(), rounds_from_env())) return DGT_E_UNSUPPORTED;
-  if (ws_bytes < c.ws_bytes) return DGT_E_BUFSIZE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!plan_call(info, m, c, staging_from_env(), rounds_from_env())) return DGT_E_UNSUPPORTED;
+  return DGT_OK;
+}
+
+// The launches of one fused call with plan c on workspace ws (counters at zero).
+int fused_launch(const CallPlan& c, const void* d_blob, const dgt_info* info,
+                 const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
+                 float* d_y, uint8_t* ws, int32_t* d_status, hipStream_t st) {
+  int rc = DGT_OK;
   Layer L;
   layer_from_info(d_blob, info, &L);
-  uint8_t* ws = static_cast<uint8_t*>(d_ws);
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(d_x);
   const uint32_t xrow = info->k * 2;
   float* sxp = nullptr;
@@ -676,6 +684,82 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
     if (rc) return rc;
   }
   return DGT_OK;
+}
+
+// ------------------------------------------------ allocation-free workspace
+// The workspace of dgt_fused_decode_gemm_noalloc: a static device array (each
+// device holds its own copy from the library's load until the process ends).
+// In host code `scratch` names a host-side stand-in; its device address comes
+// from hipGetSymbolAddress, taken once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch (set up on first use).
+int scratch_of_current_device(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DGT_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DGT_E_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch[dev]);
+  return DGT_OK;
+}
+
+// Zero n dwords (a kernel rather than a memset node, so the call stays
+// correct when a caller captures it into a graph).
+__global__ __launch_bounds__(256) void k_zero(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
+                          uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
+                          void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
+  if (!d_ws || ((uintptr_t)d_ws & 255)) return DGT_E_ARG;
+  CallPlan c;
+  int rc = fused_prepare(d_blob, info, d_x, m, d_scales, d_y, &c);
+  if (rc) return rc;
+  if (ws_bytes < c.ws_bytes) return DGT_E_BUFSIZE;
+  return fused_launch(c, d_blob, info, d_x, m, d_scales, w_scale, d_y,
+                      static_cast<uint8_t*>(d_ws), d_status, static_cast<hipStream_t>(stream));
+}
+
+size_t dgt_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int dgt_fused_decode_gemm_noalloc(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
+                                  uint32_t m, const uint16_t* d_scales, float w_scale,
+                                  float* d_y, int32_t* d_status, void* stream) {
+  CallPlan c;
+  int rc = fused_prepare(d_blob, info, d_x, m, d_scales, d_y, &c);
+  if (rc) return rc;
+  if (c.ws_bytes > kScratchBytes) return DGT_E_BUFSIZE;
+  uint8_t* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the per-strip counters (and the fp8 quantisation's maximum and block
+  // counter) must start at zero; the array keeps whatever the last call left
+  const uint32_t strips = info->n / info->tile_n;
+  const uint32_t counter_words = (uint32_t)(dgt::align_up((size_t)strips * 4, 256) / 4);
+  hipLaunchKernelGGL(k_zero, dim3(std::min<uint32_t>((counter_words + 255) / 256, 64)),
+                     dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws), counter_words);
+  if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
+  if (info->fmt == DGT_FMT_FP8_E4M3) {
+    hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, st,
+                       reinterpret_cast<uint32_t*>(ws + c.quant_off), 64u);
+    if (hipGetLastError() != hipSuccess) return DGT_E_HIP;
+  }
+  return fused_launch(c, d_blob, info, d_x, m, d_scales, w_scale, d_y, ws, d_status, st);
 }
 
 int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d_tile_ids,

@@ -190,6 +190,23 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
                           uint32_t m, const uint16_t* d_scales, float w_scale, float* d_y,
                           void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream);
 
+/* Allocation-free variant of dgt_fused_decode_gemm, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, values and errors, but
+ * no workspace argument: the workspace is a static device array of
+ * dgt_noalloc_scratch_bytes() bytes (16 MiB) that every device the library
+ * runs on holds from the library's load until the process ends.  A call whose
+ * workspace (dgt_gemm_workspace) would exceed it returns DGT_E_BUFSIZE and
+ * enqueues nothing; M <= 16 fits every layer up to 53248 x 16384.  Each call
+ * first zeroes the array's counters with a small kernel on `stream`.  All
+ * calls on one device share the array: calls that overlap in time on one
+ * device (other streams, other threads) race and give wrong results.  Calls
+ * no hipMalloc, hipFree or allocating library routine. */
+size_t dgt_noalloc_scratch_bytes(void);
+int dgt_fused_decode_gemm_noalloc(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
+                                  uint32_t m, const uint16_t* d_scales, float w_scale,
+                                  float* d_y, int32_t* d_status, void* stream);
+
 /* Uncompressed baseline with the same tiling and epilogue, reading W from
  * global memory: d_w is [N, K] in the same element layout dgt_decode_tiles
  * writes (INT4_PAIR is read as INT4, BF16_EXP as BF16_SPLIT).  Workspace from dgt_dense_workspace
