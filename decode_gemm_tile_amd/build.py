@@ -38,8 +38,19 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = None) -> str:
-    """Compile every HIP/C++ source and link libdgt.so; returns its path."""
+def _stale(obj, src):
+    """True if obj is missing or older than its source or any header."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src, os.path.join(HERE, "..", "include", "dgt.h")]
+    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, jobs: int = None, incremental: bool = False) -> str:
+    """Compile every HIP/C++ source and link libdgt.so; returns its path.
+    incremental=True recompiles only objects older than their sources."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
@@ -56,6 +67,8 @@ def build(verbose: bool = False, jobs: int = None) -> str:
     api_obj = os.path.join(BUILD, "dgt_api.o")
     steps.append([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, "dgt_api.hip"), "-o", api_obj])
     objs.append(api_obj)
+    if incremental:
+        steps = [c for c in steps if _stale(c[-1], c[-3])]
     with cf.ThreadPoolExecutor(jobs) as ex:
         for out in ex.map(_run, steps):
             if verbose and out.strip():
@@ -67,4 +80,4 @@ def build(verbose: bool = False, jobs: int = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -30,6 +30,8 @@ int fused_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hi
 template <int R, int FN, bool RING>
 int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t threads,
             uint32_t lds, hipStream_t st) {
+  if (mt == 0 && !mix) return fused_t<R, FN, 0, false, RING>(a, grid, threads, lds, st);
+  if (mt == 0 && mix) return fused_t<R, FN, 0, true, RING>(a, grid, threads, lds, st);
   if (mt == 1 && !mix) return fused_t<R, FN, 1, false, RING>(a, grid, threads, lds, st);
   if (mt == 1 && mix) return fused_t<R, FN, 1, true, RING>(a, grid, threads, lds, st);
   if constexpr (FN <= 8) {
@@ -39,10 +41,10 @@ int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t th
   return DGT_E_UNSUPPORTED;
 }
 
-template <int R, int FN, bool MIX>
+template <int R, int FN, int MT, bool MIX>
 int rounds_t(const GemmArgs& a, uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st,
              int* blocks_per_cu) {
-  auto k = k_fused_rounds<DGT_FMT, R, FN, 1, MIX>;
+  auto k = k_fused_rounds<DGT_FMT, R, FN, MT, MIX>;
   if (!set_lds(k, lds)) return DGT_E_HIP;
   if (blocks_per_cu) {
     int n = 0;
@@ -78,16 +80,20 @@ int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32
   return DGT_E_UNSUPPORTED;
 }
 
-// Multi-round register path (ring staging, 16-row blocks of X): launches, or
-// with blocks_per_cu set only reports how many workgroups a CU holds at once.
+// Multi-round register path (ring staging, one 16-row block of X, or the
+// single-row mode mt = 0): launches, or with blocks_per_cu set only reports
+// how many workgroups a CU holds at once.
 template <>
-int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, bool mix,
-                                 uint32_t grid, uint32_t threads, uint32_t lds, hipStream_t st,
-                                 int* blocks_per_cu) {
-#define DGT_ROUNDS_CASE(RR, FNV)                                                          \
-  if (lanes == RR && fn == FNV)                                                           \
-    return mix ? rounds_t<RR, FNV, true>(a, grid, threads, lds, st, blocks_per_cu)        \
-               : rounds_t<RR, FNV, false>(a, grid, threads, lds, st, blocks_per_cu);
+int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t mt,
+                                 bool mix, uint32_t grid, uint32_t threads, uint32_t lds,
+                                 hipStream_t st, int* blocks_per_cu) {
+#define DGT_ROUNDS_CASE(RR, FNV)                                                              \
+  if (lanes == RR && fn == FNV && mt == 0)                                                    \
+    return mix ? rounds_t<RR, FNV, 0, true>(a, grid, threads, lds, st, blocks_per_cu)         \
+               : rounds_t<RR, FNV, 0, false>(a, grid, threads, lds, st, blocks_per_cu);       \
+  if (lanes == RR && fn == FNV && mt == 1)                                                    \
+    return mix ? rounds_t<RR, FNV, 1, true>(a, grid, threads, lds, st, blocks_per_cu)         \
+               : rounds_t<RR, FNV, 1, false>(a, grid, threads, lds, st, blocks_per_cu);
   DGT_ROUNDS_CASE(64, 8)
   DGT_ROUNDS_CASE(64, 16)
   DGT_ROUNDS_CASE(128, 8)

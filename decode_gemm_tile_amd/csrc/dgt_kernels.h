@@ -234,8 +234,16 @@ __device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t 
 // Units [u0, u1) of workgroup blockIdx.x are reduced: C units per workgroup
 // in the strip numbering above; the waves holding units are those of the
 // first min(u1 - u0, cpw) units of a round.
+// MT = 0 is the single-row mode (M = 1): instead of one accumulator per row
+// band, row band b of the tile is multiplied with an A operand holding X in
+// row b only, so accumulator row b collects band b and one 16x16 accumulator
+// holds all <= 16 bands (4 VGPRs instead of 4 per band).
+__host__ __device__ constexpr int acc_bands(int FN, int MT) { return MT == 0 ? 1 : FN; }
+__host__ __device__ constexpr int acc_blocks(int MT) { return MT == 0 ? 1 : MT; }
+
 template <int FN, int MT>
-__device__ __forceinline__ void reduce_range(const GemmArgs& a, floatx4 (&acc)[FN][MT],
+__device__ __forceinline__ void reduce_range(const GemmArgs& a,
+                                             floatx4 (&acc)[acc_bands(FN, MT)][acc_blocks(MT)],
                                              float* red, float out_scale, uint32_t u0,
                                              uint32_t u1, uint32_t C, uint32_t t) {
   const uint32_t lane = t & 63, wave = t >> 6;
@@ -248,17 +256,26 @@ __device__ __forceinline__ void reduce_range(const GemmArgs& a, floatx4 (&acc)[F
   const uint32_t nstrips = (sA == sB) ? 1u : 2u;
   __syncthreads();  // LUT / staged streams are no longer needed
   for (uint32_t c0 = 0; c0 < TN; c0 += RC) {
-    if (wave < nw) {
+    if (MT == 0 && wave < nw) {
+      // accumulator row 4 * (lane / 16) + i holds band 4 * (lane / 16) + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t band = 4 * (lane >> 4) + i;
+        const uint32_t col = band * 16 + (lane & 15);
+        if (band < (uint32_t)FN && col >= c0 && col < c0 + RC)
+          red[(size_t)wave * M * RC + (col - c0)] = acc[0][0][i];
+      }
+    } else if (wave < nw) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const uint32_t col = fn * 16 + (lane & 15);
         if (col >= c0 && col < c0 + RC) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
+          for (int mt = 0; mt < acc_blocks(MT); ++mt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t m = mt * 16 + 4 * (lane >> 4) + i;
-              if (m < M) red[((size_t)wave * M + m) * RC + (col - c0)] = acc[fn][mt][i];
+              if (m < M) red[((size_t)wave * M + m) * RC + (col - c0)] = acc[acc_bands(FN, MT) > 1 ? fn : 0][mt][i];
             }
           }
         }
@@ -323,7 +340,8 @@ __device__ __forceinline__ void reduce_range(const GemmArgs& a, floatx4 (&acc)[F
 
 // One round per workgroup: units [b*C, b*C + C).
 template <int FN, int MT>
-__device__ __forceinline__ void reduce_and_store(const GemmArgs& a, floatx4 (&acc)[FN][MT],
+__device__ __forceinline__ void reduce_and_store(const GemmArgs& a,
+                                                 floatx4 (&acc)[acc_bands(FN, MT)][acc_blocks(MT)],
                                                  float* red, float out_scale) {
   const uint32_t u0 = blockIdx.x * a.cpw;
   reduce_range<FN, MT>(a, acc, red, out_scale, u0, min(u0 + a.cpw, a.chains), a.cpw, threadIdx.x);
@@ -352,7 +370,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __host__ __device__ constexpr uint32_t fused_max_threads(int R, int FN, int MT, int ILP) {
-  return (MT == 1 && FN <= 8 && (R != 32 || ILP == 1)) ? 1024u : 512u;
+  return ((MT == 0 || (MT == 1 && FN <= 8)) && (R != 32 || ILP == 1)) ? 1024u : 512u;
 }
 __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
   return (MT == 1 && FN <= 8) ? 1024u : 512u;
@@ -368,7 +386,8 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
                                              Chain (&chs)[2], Ring (&rgs)[2],
                                              const uint32_t (&tile_lane)[2],
                                              const uint32_t (&k0_lane)[2], uint32_t strip,
-                                             floatx4 (&acc)[FN][MT], AfterFirst&& after_first) {
+                                             floatx4 (&acc)[acc_bands(FN, MT)][acc_blocks(MT)],
+                                             AfterFirst&& after_first) {
   const Layer& L = a.L;
   constexpr int NS = states_per_lane(R);
   constexpr uint32_t FW = (R == 128 ? 64 : R) / 2;  // fragment width (columns)
@@ -432,26 +451,29 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
       if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, 0, h);
       if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, 0, h);
     }
-  constexpr bool kPrefetchA = (MT == 1);
-  u32x4 A_n[ILP][MT];
+  constexpr bool kPrefetchA = (MT <= 1);
+  constexpr int MB = acc_blocks(MT);
+  // the X row of this lane (single-row mode: row 0 in every lane)
+  const uint32_t xrow = MT == 0 ? 0u : (lane & 15);
+  u32x4 A_n[ILP][MB];
   if constexpr (kPrefetchA) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + koff);
+      for (int mt = 0; mt < MB; ++mt)
+        A_n[c][mt] = load_a<FMT>(a, mt * 16 + xrow, kb[c] + koff);
   }
-  // A operands of column block fk (X is fetched one block ahead when MT == 1)
-  u32x4 A[ILP][MT];
+  // A operands of column block fk (X is fetched one block ahead when MT <= 1)
+  u32x4 A[ILP][MB];
   auto take_a = [&](uint32_t fk) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MB; ++mt) {
         if constexpr (kPrefetchA)
           A[c][mt] = A_n[c][mt];
         else
-          A[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + fk * FW + koff);
+          A[c][mt] = load_a<FMT>(a, mt * 16 + xrow, kb[c] + fk * FW + koff);
       }
   };
   auto prefetch_a = [&](uint32_t fk) __attribute__((always_inline)) {
@@ -460,8 +482,8 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
 #pragma unroll
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            A_n[c][mt] = load_a<FMT>(a, mt * 16 + (lane & 15), kb[c] + (fk + 1) * FW + koff);
+          for (int mt = 0; mt < MB; ++mt)
+            A_n[c][mt] = load_a<FMT>(a, mt * 16 + xrow, kb[c] + (fk + 1) * FW + koff);
       }
     }
   };
@@ -524,9 +546,20 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
 #pragma unroll
       for (int h = 0; h < NS; ++h) {
         const BOp b = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], nsc8[c][h]);
+        if constexpr (MT == 0) {
+          // band h * FNH + fn: X in that row of the A operand only
+          const bool row = (lane & 15) == (uint32_t)(h * FNH + fn);
+          u32x4 ap;
+          ap.x = row ? A[c][0].x : 0u;
+          ap.y = row ? A[c][0].y : 0u;
+          ap.z = row ? A[c][0].z : 0u;
+          ap.w = row ? A[c][0].w : 0u;
+          acc[0][0] = mfma<FMT>(ap, b, acc[0][0]);
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[h * FNH + fn][mt] = mfma<FMT>(A[c][mt], b, acc[h * FNH + fn][mt]);
+          for (int mt = 0; mt < MT; ++mt)
+            acc[h * FNH + fn][mt] = mfma<FMT>(A[c][mt], b, acc[h * FNH + fn][mt]);
+        }
       }
   };
   // The first fragment runs ahead of the loop, so that whatever after_first()
@@ -648,11 +681,11 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     }
   };
 
-  floatx4 acc[FN][MT];
+  floatx4 acc[acc_bands(FN, MT)][acc_blocks(MT)];
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
+  for (int fn = 0; fn < acc_bands(FN, MT); ++fn)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < acc_blocks(MT); ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MIX) {
     if (nch == 2)
       fused_chains<FMT, R, FN, MT, 2, RING>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip, acc,
@@ -688,7 +721,7 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
   float* red = reinterpret_cast<float*>(smem + a.red_off);
   const uint32_t C = a.cpw, CW = a.cpw * a.rounds;
   const uint32_t U0 = blockIdx.x * CW, U1 = min(U0 + CW, a.chains);
-  floatx4 acc[FN][MT];
+  floatx4 acc[acc_bands(FN, MT)][acc_blocks(MT)];
   for (uint32_t u0 = U0; u0 < U1; u0 += C) {
     const uint32_t lane = lane_id();
     const bool first = u0 == U0;
@@ -722,9 +755,9 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
     }
     if (first) {
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int fn = 0; fn < acc_bands(FN, MT); ++fn)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < acc_blocks(MT); ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     if constexpr (ILP > 0)
       fused_chains<FMT, R, FN, MT, ILP, true>(a, lut, smem, ch, rg, tile_lane, k0_lane, strip,
@@ -739,9 +772,9 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
                            threadIdx.x);
       if (un < U1) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < acc_bands(FN, MT); ++fn)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < acc_blocks(MT); ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();  // the reduction buffer overlaps the next round's rings
       }
     }

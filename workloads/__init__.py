@@ -96,6 +96,18 @@ for _base in ("bf16_mlp", "bf16_ffn405"):
         _base + "_pair", FMT_BF16_PAIR, _w.n, _w.k, _w.tile_n, _w.tile_k, _w.lanes, _w.seed,
         _w.m_values, w_sigma=_w.w_sigma, prob_bits=_w.prob_bits,
         note=_w.note + ", high bytes coded in pairs")
+# the same layers in other tile geometries (the configurations leave tile shape
+# or lane count free for these): 256x64 tiles, or 32 lanes per tile
+for _base, _tn, _tk, _r, _suffix in (("bf16_mlp", 256, 64, 64, "_t256"),
+                                     ("bf16_mlp", 128, 64, 32, "_r32"),
+                                     ("int4_ffn405", 256, 64, 64, "_t256"),
+                                     ("int4_ffn405", 128, 64, 32, "_r32"),
+                                     ("int4_4096", 128, 64, 32, "_r32")):
+    _w = WORKLOADS[_base]
+    WORKLOADS[_base + _suffix] = Workload(
+        _base + _suffix, _w.fmt, _w.n, _w.k, _tn, _tk, _r, _w.seed, _w.m_values,
+        w_sigma=_w.w_sigma, w_mean=_w.w_mean, prob_bits=_w.prob_bits,
+        note=_w.note + ", tiles %dx%d, R = %d" % (_tn, _tk, _r))
 # two states per lane: the same layers with R = 128
 for _base in ("int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405"):
     _w = WORKLOADS[_base]
