@@ -271,18 +271,18 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
 // Workgroups of the multi-round kernel a CU holds at once (its registers and
 // LDS decide, as the runtime reports for the current device); 1 when the
 // runtime cannot tell.
-uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, bool mix, uint32_t threads,
-                              uint32_t lds) {
+uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, uint32_t mt, bool mix,
+                              uint32_t threads, uint32_t lds) {
   GemmArgs a{};
   int n = 0, rc = DGT_E_ARG;
   switch (in->fmt) {
-    case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
-    case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, in->lanes, fn, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
     default: break;
   }
   return (rc == DGT_OK && n > 0) ? (uint32_t)n : 1u;
@@ -298,7 +298,8 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_e
   if (kt % tpc) return false;
   // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
   p->m_chunk = std::min<uint32_t>(m, in->tile_n == 256 ? 16 : 64);
-  p->mt = p->m_chunk <= 16 ? 1 : 4;
+  // one row: the single-row mode (row bands packed into one accumulator)
+  p->mt = p->m_chunk == 1 ? 0 : p->m_chunk <= 16 ? 1 : 4;
   p->strips = in->n / in->tile_n;
   p->chains = in->tiles / tpc;
   p->cps = kt / tpc;
@@ -354,14 +355,14 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_e
   // partial sums leave the workgroup once.  Ring staging, 16-row blocks of X,
   // full rounds inside one strip (cpw divides the units per strip).  The
   // reduction buffer then sits after the tables, over the rings.
-  if (ring && p->mt == 1 && R != 32 && p->cps % c == 0) {
+  if (ring && p->mt <= 1 && R != 32 && p->cps % c == 0) {
     uint32_t rc2 = in->tile_n;
     while (rc2 > 16 && (uint64_t)p->waves * p->m_chunk * rc2 * 4 > c * chain_lds) rc2 /= 2;
     const uint32_t lds2 = tab + std::max<uint32_t>(c * chain_lds, p->waves * p->m_chunk * rc2 * 4);
     const uint32_t wg_rounds = p->wgs;
     uint32_t rounds = rounds_env;
     if (rounds == 0) {
-      const uint32_t per_cu = rounds_blocks_per_cu(in, fn, p->mix != 0, p->threads, lds2);
+      const uint32_t per_cu = rounds_blocks_per_cu(in, fn, p->mt, p->mix != 0, p->threads, lds2);
       rounds = (wg_rounds + kCUs * per_cu - 1) / (kCUs * per_cu);
     }
     if (rounds > 1 && lds2 <= kMaxLds) {
@@ -573,13 +574,13 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     int rc;
     if (p.rounds > 1) {
       switch (info->fmt) {
-        case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
-        case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, info->lanes, fn, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_INT8: rc = launch_fused_rounds<INT8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_INT4: rc = launch_fused_rounds<INT4>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_INT4_PAIR: rc = launch_fused_rounds<INT4P>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_EXP: rc = launch_fused_rounds<BF16E>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
         default: return DGT_E_ARG;
       }
       if (rc) return rc;
@@ -691,7 +692,7 @@ int fused_launch(const CallPlan& c, const void* d_blob, const dgt_info* info,
 // device holds its own copy from the library's load until the process ends).
 // In host code `scratch` names a host-side stand-in; its device address comes
 // from hipGetSymbolAddress, taken once per device and kept in g_scratch.
-constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;

@@ -194,10 +194,11 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, values and errors, but
  * no workspace argument: the workspace is a static device array of
- * dgt_noalloc_scratch_bytes() bytes (16 MiB) that every device the library
+ * dgt_noalloc_scratch_bytes() bytes (64 MiB) that every device the library
  * runs on holds from the library's load until the process ends.  A call whose
  * workspace (dgt_gemm_workspace) would exceed it returns DGT_E_BUFSIZE and
- * enqueues nothing; M <= 16 fits every layer up to 53248 x 16384.  Each call
+ * enqueues nothing; M <= 16 fits every layer up to 53248 x 16384 (55 MiB at
+ * most), and so does M <= 256 up to 14336 x 4096 (42 MiB).  Each call
  * first zeroes the array's counters with a small kernel on `stream`.  All
  * calls on one device share the array: calls that overlap in time on one
  * device (other streams, other threads) race and give wrong results.  Calls

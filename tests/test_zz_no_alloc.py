@@ -46,9 +46,9 @@ def test_noalloc_matches_workspace_entry_point_twice(layer):
 
 def test_noalloc_refuses_oversize_workspace():
     import torch
-    fmt, n, k = dgt.DGT_FMT_BF16_SPLIT, 14336, 4096
-    d = workloads.random_small(fmt, n, 1024, seed=95, m=1)
-    codes = np.tile(d["codes"], (1, 4))
+    fmt, n, k = dgt.DGT_FMT_BF16_SPLIT, 28672, 4096
+    d = workloads.random_small(fmt, 1024, 1024, seed=95, m=1)
+    codes = np.tile(d["codes"], (n // 1024, k // 1024))
     layer = dgt.DeviceLayer(dgt.dgt_compress_layer(fmt, codes, 128, 64, 64))
     m = 256
     assert dgt.dgt_gemm_workspace(layer, m) > dgt.dgt_noalloc_scratch_bytes()
