@@ -35,7 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20     # working set above the 256 MB last-level cache
 METRIC = "fused rANS-decode GEMM decoded-weight GB/s at M=1; TFLOP/s at M=256; bits/wt"
 # decoded-weight bytes per weight at the format's storage width (int4: half a byte)
-STORAGE_BYTES = {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0, 7: 2.0}
+STORAGE_BYTES = {1: 1.0, 2: 0.5, 3: 1.0, 4: 2.0, 5: 0.5, 6: 2.0, 7: 2.0, 8: 2.0}
 CPU_SAMPLE_WEIGHTS = 96 << 20  # weights of W the CPU oracle decodes (whole strips)
 
 
@@ -63,6 +63,28 @@ def source_hash() -> str:
         with open(os.path.join(d, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+VALU_SIMDS = 1024            # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9
+VALU_CYCLES = 4              # a wave64 VALU instruction occupies a SIMD16 for 4 cycles
+
+
+def valu_from_profiles(workload: str, m: int, kernel_us: float):
+    """Fraction of the kernel time the SIMDs spend issuing VALU instructions,
+    from the committed SQ counter summary (SQ_INSTS_VALU per dispatch), if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "sq_counters_%s_m%d.md" % (workload, m))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source hash:\s*`?([0-9a-f]{16})", text)
+    m_val = re.search(r"\| SQ_INSTS_VALU \| ([0-9.eE+]+) \|", text)
+    if not m_hash or not m_val or m_hash.group(1) != source_hash():
+        return None
+    busy_s = float(m_val.group(1)) * VALU_CYCLES / VALU_SIMDS / CLOCK_HZ
+    return {"valu_instructions": float(m_val.group(1)),
+            "valu_issue_frac": round(busy_s / (kernel_us * 1e-6), 4)}
 
 
 def traffic_from_profiles(workload: str, m: int):
@@ -238,7 +260,7 @@ def compress(dgt, name):
     d = workloads.make(name)
     wl = d["workload"]
     t0 = time.perf_counter()
-    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes, wl.prob_bits)
     return d, blob, time.perf_counter() - t0
 
 
@@ -337,7 +359,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(args.workload, m),
                      "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes": alg_bytes,
-                     "per_launch": dist, "source_hash": source_hash()},
+                     "per_launch": dist, "source_hash": source_hash(),
+                     "valu": valu_from_profiles(args.workload, m, ms * 1e3)},
     }
     h, over = entropy_over(wl, d, info)
     secondary = {"bits_per_weight": round(info.bits_per_weight, 4), "entropy_bits": h,
@@ -353,7 +376,7 @@ def main():
         secondary["fused_m%d_tflops" % m2] = round(flops / (ms2 * 1e-3) / 1e12, 3)
         secondary["fused_m%d_mfma_frac" % m2] = round(
             flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
-        wide = wl.fmt in (4, 6, 7)
+        wide = wl.fmt in (4, 6, 7, 8)
         codes = np.asarray(d["codes"])
         wraw = torch.from_numpy(codes.view(np.int16) if wide else codes.view(np.uint8)).to(dev)
         dcopies = max(2, math.ceil(ROTATE_BYTES / (nk * 2)))
@@ -422,11 +445,10 @@ def main():
         del wd, dec
         # the same layer in the other codings of its family: bits and time
         variants = []
-        if wl.fmt in (4, 7) and wl.lanes == 64:
-            other = 4 if wl.fmt == 7 else 7
-            variants.append(("one_high_byte_per_symbol" if other == 4 else "high_byte_pairs",
-                             other, 64))
-        if wl.lanes == 64 and wl.tile_n % 32 == 0:
+        family = {4: "one_high_byte_per_symbol", 7: "high_byte_pairs", 8: "whole_words"}
+        if wl.fmt in family and wl.lanes == 64:
+            variants += [(nm, f, 64) for f, nm in family.items() if f != wl.fmt]
+        if wl.lanes == 64 and wl.tile_n % 32 == 0 and wl.fmt != 8:
             variants.append(("two_states_per_lane", wl.fmt, 128))
         for vname, vfmt, vlanes in variants:
             blob2 = dgt.dgt_compress_layer(vfmt, d["codes"], wl.tile_n, wl.tile_k, vlanes)
@@ -442,7 +464,7 @@ def main():
             del r2
         # the other configurations the metric is quoted on
         others = {}
-        for other in ("int4_ffn405", "bf16_mlp"):
+        for other in ("int4_ffn405", "int4_ffn405_pair", "bf16_mlp", "bf16_mlp_t128"):
             if other != args.workload:
                 others[other] = summary_line(dgt, other, dev, stream, reps)
         secondary["other_workloads"] = others

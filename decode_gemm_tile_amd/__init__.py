@@ -18,6 +18,8 @@ DGT_FMT_INT8, DGT_FMT_INT4, DGT_FMT_FP8_E4M3, DGT_FMT_BF16_SPLIT = 1, 2, 3, 4
 DGT_FMT_INT4_PAIR = 5
 DGT_FMT_BF16_EXP = 6
 DGT_FMT_BF16_PAIR = 7
+DGT_FMT_BF16_WORD = 8
+BF16_FORMATS = (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR, DGT_FMT_BF16_WORD)
 STATUS = {0: "DGT_OK", -1: "DGT_E_ARG", -2: "DGT_E_SHAPE", -3: "DGT_E_ALPHABET",
           -4: "DGT_E_BUFSIZE", -5: "DGT_E_FORMAT", -6: "DGT_E_CORRUPT", -7: "DGT_E_HIP",
           -8: "DGT_E_UNSUPPORTED"}
@@ -166,9 +168,12 @@ def dgt_compress_bound(fmt, n, k, tile_n, tile_k, lanes, prob_bits=12) -> int:
     return lib().dgt_compress_bound(ctypes.byref(p))
 
 
-def dgt_compress_layer(fmt, w, tile_n, tile_k, lanes, prob_bits=12) -> bytes:
+def dgt_compress_layer(fmt, w, tile_n, tile_k, lanes, prob_bits=None) -> bytes:
     """Offline encoder.  w: [N, K] numpy array (int8 / uint8 codes, or uint16
-    bf16 bit patterns for the bf16 split)."""
+    bf16 bit patterns for the bf16 formats).  prob_bits defaults to 12 (16 for
+    whole bf16 words)."""
+    if prob_bits is None:
+        prob_bits = 16 if fmt == DGT_FMT_BF16_WORD else 12
     w = np.ascontiguousarray(w)
     n, k = w.shape
     p = dgt_params(fmt, n, k, tile_n, tile_k, lanes, prob_bits, 0)
@@ -210,7 +215,7 @@ def dgt_decode_tiles(layer: DeviceLayer, tile_ids=None, out=None, status=None, s
     import torch
     inf = layer.info
     dev = layer.blob.device
-    wide = inf.fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
+    wide = inf.fmt in BF16_FORMATS
     if out is None:
         out = torch.zeros((inf.n, inf.k), dtype=torch.int16 if wide else torch.uint8, device=dev)
     _check_tensor(out, "out", (inf.n, inf.k), _TWO_BYTE if wide else ("torch.uint8", "torch.int8"),
@@ -309,7 +314,7 @@ def dgt_dense_gemm(fmt, w, x, tile_n=128, scales=None, w_scale=1.0, y=None, ws=N
                    stream=None):
     """Uncompressed baseline; w: device [N, K] (uint8 codes or bf16 bits)."""
     import torch
-    wide = fmt in (DGT_FMT_BF16_SPLIT, DGT_FMT_BF16_EXP, DGT_FMT_BF16_PAIR)
+    wide = fmt in BF16_FORMATS
     _need(hasattr(w, "shape") and w.dim() == 2, "w must be a 2-D tensor [N, K]")
     n, k = w.shape
     dev = w.device

@@ -20,7 +20,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-FORMATS = {"int8": 1, "int4": 2, "fp8": 3, "bf16": 4, "int4p": 5, "bf16e": 6, "bf16p": 7}
+FORMATS = {"int8": 1, "int4": 2, "fp8": 3, "bf16": 4, "int4p": 5, "bf16e": 6, "bf16p": 7,
+           "bf16w": 8}
 
 
 def _hipcc() -> str:

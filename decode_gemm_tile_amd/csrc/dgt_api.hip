@@ -181,11 +181,18 @@ bool layer_from_info(const void* d_blob, const dgt_info* in, Layer* L) {
   L->kt = in->k / in->tile_k;
   L->steps = in->tile_n * in->tile_k / dgt::weights_per_symbol(in->fmt) / in->lanes;
   L->region_words = region_words_of(in, false);  // a plan using the ring overrides it
+  L->tab = tab_bytes_layer((int)in->fmt, in->alphabet);
   return true;
 }
 
 int device_supported(const dgt_info* in) {
   if (!in) return DGT_E_ARG;
+  if (in->fmt == DGT_FMT_BF16_WORD) {
+    // whole words: 2^16 slots, 64 lanes, at most kWordSymbols distinct patterns
+    if (in->prob_bits != 16 || in->lanes != 64 || in->alphabet > kWordSymbols)
+      return DGT_E_UNSUPPORTED;
+    return DGT_OK;
+  }
   if (in->prob_bits != 12) return DGT_E_UNSUPPORTED;
   if (in->lanes != 32 && in->lanes != 64 && in->lanes != 128) return DGT_E_UNSUPPORTED;
   return DGT_OK;
@@ -211,6 +218,13 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
   return std::min(w, ups);
 }
 
+// One fragment buffer instead of two in the large-M kernel (the ablation rung
+// without ping-pong), asked for by DGT_XM_SINGLE_BUFFER=1; results are identical.
+bool xm_single_buffer_from_env() {
+  const char* v = std::getenv("DGT_XM_SINGLE_BUFFER");
+  return v && std::strcmp(v, "1") == 0;
+}
+
 // Large M: one launch in which every tile is decoded once and shared through
 // LDS by waves that own disjoint row blocks, instead of one launch per chunk
 // of rows that each decode the whole layer.  Needs R = 64 or 128 and k-tiles
@@ -230,8 +244,8 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   p->region_words = region_words_of(in, ring);
   const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
-      (uint32_t)dgt::align_up((size_t)tab_bytes_of((int)in->fmt) + nt * region_bytes + 16, 16);
-  const uint32_t fpb = in->lanes == 128 ? xm_fpb(128, fn) : xm_fpb(64, fn);
+      (uint32_t)dgt::align_up((size_t)tab_bytes_layer((int)in->fmt, in->alphabet) + nt * region_bytes + 16, 16);
+  const uint32_t fpb = xm_fpb(in->lanes == 128 ? 128 : 64, fn, (int)in->fmt);
   const uint32_t lds = xbuf_off + 2 * fpb * nt * ns * 1024;
   if (lds > kMaxLds) return false;
   p->xm = 1;
@@ -283,6 +297,7 @@ uint32_t rounds_blocks_per_cu(const dgt_info* in, uint32_t fn, uint32_t mt, bool
     case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
     case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
     case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
+    case DGT_FMT_BF16_WORD: rc = launch_fused_rounds<BF16W>(a, in->lanes, fn, mt, mix, 0, threads, lds, nullptr, &n); break;
     default: break;
   }
   return (rc == DGT_OK && n > 0) ? (uint32_t)n : 1u;
@@ -304,7 +319,7 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_e
   p->chains = in->tiles / tpc;
   p->cps = kt / tpc;
   const uint32_t chain_lds = tpc * p->region_words * 2;
-  const uint32_t tab = tab_bytes_of((int)in->fmt);
+  const uint32_t tab = tab_bytes_layer((int)in->fmt, in->alphabet);
   if (tab + chain_lds > kMaxLds) return false;
   const uint32_t lds_cap = (kMaxLds - tab) / chain_lds;
   const uint32_t fn = in->tile_n / 16 == 8 ? 8 : 16;
@@ -422,12 +437,6 @@ bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg, uint32
   return plan_fused_reg(in, m, true, rounds, p, &unused);
 }
 
-// One fragment buffer instead of two in the large-M kernel (the ablation rung
-// without ping-pong), asked for by DGT_XM_SINGLE_BUFFER=1; results are identical.
-bool xm_single_buffer_from_env() {
-  const char* v = std::getenv("DGT_XM_SINGLE_BUFFER");
-  return v && std::strcmp(v, "1") == 0;
-}
 
 // Rounds per workgroup of the register path, forced by the environment
 // variable DGT_ROUNDS (a positive count; results are identical), else 0.
@@ -542,6 +551,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
       case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
       case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
       case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_WORD: return launch_fused_xm<BF16W>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
     }
   }
@@ -581,6 +591,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
         case DGT_FMT_BF16_PAIR: rc = launch_fused_rounds<BF16P>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
         case DGT_FMT_FP8_E4M3: rc = launch_fused_rounds<FP8>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
         case DGT_FMT_BF16_SPLIT: rc = launch_fused_rounds<BF16>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
+        case DGT_FMT_BF16_WORD: rc = launch_fused_rounds<BF16W>(a, info->lanes, fn, p.mt, mix, grid, threads, p.lds, st, nullptr); break;
         default: return DGT_E_ARG;
       }
       if (rc) return rc;
@@ -607,6 +618,9 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
         break;
       case DGT_FMT_BF16_SPLIT:
         rc = launch_fused<BF16>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
+        break;
+      case DGT_FMT_BF16_WORD:
+        rc = launch_fused<BF16W>(a, info->lanes, fn, p.mt, mix, rg, grid, threads, p.lds, st);
         break;
       default:
         rc = DGT_E_ARG;
@@ -787,7 +801,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
   // whole streams when the workgroup's tiles fit LDS, else (R = 64, 128) the ring
   bool ring = false;
   auto lds_for = [&](uint32_t w) {
-    return tab_bytes_of((int)info->fmt) + w * ilp * tpc * a.L.region_words * 2;
+    return tab_bytes_layer((int)info->fmt, info->alphabet) + w * ilp * tpc * a.L.region_words * 2;
   };
   const Staging sg = staging_from_env();
   if (R != 32) {
@@ -811,6 +825,7 @@ int dgt_decode_tiles(const void* d_blob, const dgt_info* info, const uint32_t* d
     case DGT_FMT_BF16_PAIR: return launch_decode<BF16P>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_FP8_E4M3: return launch_decode<FP8>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     case DGT_FMT_BF16_SPLIT: return launch_decode<BF16>(a, R, ilp, ring, grid, 64 * waves, lds, st);
+    case DGT_FMT_BF16_WORD: return launch_decode<BF16W>(a, R, ilp, ring, grid, 64 * waves, lds, st);
     default: break;
   }
   return DGT_E_UNSUPPORTED;
@@ -853,10 +868,11 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
                    const uint16_t* d_x, uint32_t m, const uint16_t* d_scales, float w_scale,
                    float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_w || !d_x || !d_y || !d_ws || m == 0 || m > 256) return DGT_E_ARG;
-  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_PAIR) return DGT_E_ARG;
+  if (fmt < DGT_FMT_INT8 || fmt > DGT_FMT_BF16_WORD) return DGT_E_ARG;
   // same decoded layout and values as the one-symbol-per-weight formats
   if (fmt == DGT_FMT_INT4_PAIR) fmt = DGT_FMT_INT4;
-  if (fmt == DGT_FMT_BF16_EXP || fmt == DGT_FMT_BF16_PAIR) fmt = DGT_FMT_BF16_SPLIT;
+  if (fmt == DGT_FMT_BF16_EXP || fmt == DGT_FMT_BF16_PAIR || fmt == DGT_FMT_BF16_WORD)
+    fmt = DGT_FMT_BF16_SPLIT;
   if ((tile_n != 128 && tile_n != 256) || n % tile_n || k % 64 || (k / 64) % 2)
     return DGT_E_SHAPE;
   if (fmt == DGT_FMT_INT4 && (!d_scales || k % 128)) return DGT_E_ARG;

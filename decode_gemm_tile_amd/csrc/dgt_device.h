@@ -40,7 +40,8 @@ constexpr uint32_t kLutBytes = kSlots * 8;
 constexpr uint32_t kCumBytes = 1040;   // (256 + 1) u32, padded
 constexpr uint32_t kSlackWords = 64;   // u16 words of slack after each staged stream
 
-enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5, BF16E = 6, BF16P = 7 };
+enum Fmt : int { INT8 = 1, INT4 = 2, FP8 = 3, BF16 = 4, INT4P = 5, BF16E = 6, BF16P = 7,
+                 BF16W = 8 };
 
 // formats whose tiles carry one raw byte per weight next to the coded symbol
 template <int FMT>
@@ -58,12 +59,33 @@ __host__ __device__ constexpr int steps_per_frag() { return (FMT == INT4P || FMT
 template <int FMT>
 __host__ __device__ constexpr bool wide_symbols() { return FMT == BF16P; }
 constexpr uint32_t kCumBytesWide = 16400;  // (4096 + 1) u32 {c_s | symbol << 16}, padded
+// Whole bf16 words (BF16W, 2^16 slots): no slot table.  The LDS holds, per
+// 4 consecutive slots 4b .. 4b + 3, a 16-bit bucket word: the index of the
+// entry holding slot 4b (13 bits) and, in bit 13 + k - 1, whether an entry
+// starts at slot 4b + k (k = 1..3); after the buckets, the present symbols'
+// entries {c_s, symbol | (f_s - 1) << 16} (up to kWordSymbols, plus the end
+// entry {2^16, 0}), sized by the layer's alphabet.  The entry of slot 4b + j
+// is the bucket's index plus the starts at offsets 1..j: one bucket read
+// and one entry read per step.
+constexpr uint32_t kWordSymbols = 8191;
+constexpr uint32_t kWordEntryBytes = (kWordSymbols + 1) * 8;
+constexpr uint32_t kWordBuckets = 16384;
+constexpr uint32_t kWordBucketBytes = kWordBuckets * 2;
+constexpr uint32_t kWordTabBytes = kWordBucketBytes + kWordEntryBytes;  // largest alphabet
+// how a step finds its symbol: 0 the 12-bit slot table, 1 the slot table of
+// 16-bit symbols (BF16P), 2 the bucket lookup of whole words (BF16W)
+template <int FMT>
+__host__ __device__ constexpr int sym_mode() { return FMT == BF16P ? 1 : FMT == BF16W ? 2 : 0; }
 // LDS bytes of the decode table plus the cumulative table built with it
 __host__ __device__ constexpr uint32_t tab_bytes_of(int fmt) {
-  return kLutBytes + (fmt == BF16P ? kCumBytesWide : kCumBytes);
+  return fmt == BF16W ? kWordTabBytes : kLutBytes + (fmt == BF16P ? kCumBytesWide : kCumBytes);
 }
 template <int FMT>
 __host__ __device__ constexpr uint32_t tab_bytes() { return tab_bytes_of(FMT); }
+// LDS bytes of a layer's decode table (whole words: entries for its alphabet)
+__host__ __device__ constexpr uint32_t tab_bytes_layer(int fmt, uint32_t alphabet) {
+  return fmt == BF16W ? kWordBucketBytes + ((alphabet + 1) * 8 + 15) / 16 * 16 : tab_bytes_of(fmt);
+}
 // At most this many final steps of a tile decode the initial-state payload.
 constexpr uint32_t kPayloadMax = 16;
 // rANS states a wave lane holds for one chain: two when R = 128.
@@ -78,7 +100,15 @@ struct Layer {
   const uint8_t* raw;       // raw low bytes (BF16 split) or null
   uint32_t n, k, tile_n, tile_k, lanes, alphabet, tiles, kt, steps;
   uint32_t region_words;    // u16 capacity of one staged-stream region (even)
+  uint32_t tab;             // LDS bytes of the decode table (tab_bytes_layer)
 };
+
+// Where the staged words start in LDS: after the decode table.
+template <int FMT>
+__device__ __forceinline__ uint32_t tab_of(const Layer& L) {
+  if constexpr (FMT == BF16W) return L.tab;
+  else return tab_bytes<FMT>();
+}
 
 __device__ __forceinline__ uint32_t lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -209,17 +239,75 @@ __device__ inline void build_lut_sparse(const uint32_t* table, uint32_t P, u32x2
   }
 }
 
+// Entries and bucket starts of whole-word symbols from the sparse table of P
+// entries {symbol | (f - 1) << 16} in symbol order (see kWordSymbols): a
+// block scan of per-thread runs gives every entry's start c, then bucket b
+// (slots 16b .. 16b + 15) gets the last entry whose start is at most 16b.
+// The entry memory serves as scratch for the per-wave sums before it is
+// filled.  Caller synchronises.
+__device__ inline void build_word_table(const uint32_t* table, uint32_t P, u32x2* ent,
+                                        uint16_t* bucket) {
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));  // nothing derived from it is hoisted past a caller's loop
+  const uint32_t B = blockDim.x;
+  const uint32_t lane = t & 63, wave = t >> 6;
+  uint32_t* wsum = reinterpret_cast<uint32_t*>(bucket);  // before the buckets are written
+  const uint32_t q = (P + B - 1) / B;
+  const uint32_t e0 = min(t * q, P), e1 = min(e0 + q, P);
+  uint32_t run = 0;
+  for (uint32_t e = e0; e < e1; ++e) run += (table[e] >> 16) + 1;
+  uint32_t v = run;  // inclusive scan over the wave's threads
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  uint32_t c = v - run;
+  for (uint32_t w = 0; w < wave; ++w) c += wsum[w];
+  __syncthreads();  // the sums are read before the entries overwrite them
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t en = table[e];
+    u32x2 x;
+    x.x = c;
+    x.y = en;
+    ent[e] = x;
+    const uint32_t f = (en >> 16) + 1;
+    // the buckets whose first slot lies in [c, c + f) (each is written once)
+    for (uint32_t b = (c + 3) >> 2; 4 * b < c + f; ++b) bucket[b] = (uint16_t)e;
+    c += f;
+  }
+  if (t == 0) ent[P] = u32x2{1u << 16, 0u};
+  __syncthreads();
+  // starts inside each bucket: entries idx + 1, idx + 2, idx + 3 while they
+  // begin at or below its last slot (the end entry begins past every slot,
+  // so each read stays at or below entry P)
+  for (uint32_t b = t; b < kWordBuckets; b += B) {
+    const uint32_t idx = bucket[b], last = 4 * b + 3;
+    uint32_t mask = 0;
+    for (uint32_t j = 1; j <= 3; ++j) {
+      const uint32_t cj = ent[idx + j].x;
+      if (cj > last) break;
+      mask |= 1u << (cj - 4 * b - 1);
+    }
+    bucket[b] = (uint16_t)(idx | (mask << 13));
+  }
+}
+
 // Table load and decode-table build of a format: the dense table's
 // frequency load is issued early (table_issue) and used by table_build.
 template <int FMT>
 __device__ __forceinline__ uint32_t table_issue(const Layer& L) {
-  if constexpr (wide_symbols<FMT>()) return 0u;
+  if constexpr (sym_mode<FMT>() != 0) return 0u;
   else return lut_load_freq(L.table, L.alphabet);
 }
 template <int FMT>
 __device__ __forceinline__ void table_build(uint32_t fq, const Layer& L, u32x2* lut,
                                             uint32_t* cum) {
-  if constexpr (wide_symbols<FMT>())
+  if constexpr (sym_mode<FMT>() == 2)
+    build_word_table(reinterpret_cast<const uint32_t*>(L.table), L.alphabet,
+                     lut + kWordBucketBytes / 8, reinterpret_cast<uint16_t*>(lut));
+  else if constexpr (sym_mode<FMT>() == 1)
     build_lut_sparse(reinterpret_cast<const uint32_t*>(L.table), L.alphabet, lut, cum);
   else
     build_lut(fq, L.alphabet, lut, cum);
@@ -269,22 +357,39 @@ __host__ __device__ constexpr int ring_group_steps(int R) { return (int)kChunkWo
 // second states' (interleaving order j = s*128 + p).  CAREFUL also handles the
 // payload switch (x -= L at step == lim, no reads from then on).
 // Returns the table words (decoded symbol in the top byte) per state, or for
-// 16-bit symbols (SYM16) the symbol's two bytes in the low half.
-template <int R, bool CAREFUL, int ILP, bool RING, bool SYM16 = false>
+// 16-bit symbols (MODE 1, and the whole words of MODE 2) the symbol in the
+// low half.  MODE 2 (2^16 slots): the bucket lookup of kWordBuckets.
+template <int R, bool CAREFUL, int ILP, bool RING, int MODE = 0>
 __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restrict__ lut,
                                          const uint8_t* __restrict__ lds, uint32_t s,
                                          bool upper_half,
                                          uint32_t (&sym)[ILP][states_per_lane(R)]) {
   constexpr int NS = states_per_lane(R);
+  constexpr bool SYM16 = MODE == 1;
+  constexpr uint32_t NB = MODE == 2 ? 16u : 12u;  // frequency precision
   uint32_t x[ILP][NS];
   u32x2 e[ILP][NS];
+  uint32_t wsym[ILP][NS];  // MODE 2: the whole word
 #pragma unroll
   for (int i = 0; i < ILP; ++i)
 #pragma unroll
     for (int h = 0; h < NS; ++h) {
       x[i][h] = h ? c[i].x2 : c[i].x;
       if (CAREFUL) x[i][h] = (s == c[i].lim) ? x[i][h] - kL : x[i][h];
-      e[i][h] = lut[x[i][h] & (kSlots - 1)];
+      if constexpr (MODE == 2) {
+        const uint32_t slot = x[i][h] & 0xFFFFu;
+        const uint16_t* bucket = reinterpret_cast<const uint16_t*>(lut);
+        const uint32_t bv = bucket[slot >> 2];
+        const uint32_t starts = (bv >> 13) & ((1u << (slot & 3u)) - 1u);
+        const u32x2 en =
+            lut[kWordBucketBytes / 8 + (bv & 0x1FFFu) + (uint32_t)__builtin_popcount(starts)];
+        // the step's operands: f, slot - c_s and the symbol
+        e[i][h].x = (en.y >> 16) + 1u;
+        e[i][h].y = slot - en.x;
+        wsym[i][h] = en.y & 0xFFFFu;
+      } else {
+        e[i][h] = lut[x[i][h] & (kSlots - 1)];
+      }
     }
   uint32_t xn[ILP][NS], w[ILP][NS];
   bool need[ILP][NS];
@@ -294,7 +399,7 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
 #pragma unroll
     for (int h = 0; h < NS; ++h) {
       const uint32_t bias = SYM16 ? (e[i][h].y & 0xFFFu) : e[i][h].y;
-      xn[i][h] = (e[i][h].x & 0xFFFFFFu) * (x[i][h] >> 12) + bias;  // v_mad_u32_u24
+      xn[i][h] = (e[i][h].x & 0xFFFFFFu) * (x[i][h] >> NB) + bias;  // v_mad_u32_u24
       need[i][h] = xn[i][h] < kL;
       if (CAREFUL) need[i][h] = need[i][h] && (s < c[i].lim);
       const uint64_t m = __builtin_amdgcn_ballot_w64(need[i][h]);
@@ -328,7 +433,8 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
       const uint32_t v = need[i][h] ? ((xn[i][h] << 16) | w[i][h]) : xn[i][h];
       if (h) c[i].x2 = v; else c[i].x = v;
       // 16-bit symbols: [low byte, high byte, 0, 0] from the entry's top bytes
-      sym[i][h] = SYM16 ? __builtin_amdgcn_perm(e[i][h].y, e[i][h].x, 0x0c0c0703u) : e[i][h].x;
+      sym[i][h] = SYM16 ? __builtin_amdgcn_perm(e[i][h].y, e[i][h].x, 0x0c0c0703u)
+                  : MODE == 2 ? wsym[i][h] : e[i][h].x;
     }
 }
 

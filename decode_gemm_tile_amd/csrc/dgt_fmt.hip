@@ -71,12 +71,14 @@ int launch_fused<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32
                 : fused_r<RR, FNV, false>(a, mt, mix, grid, threads, lds, st);
   DGT_FUSED_CASE(64, 8)
   DGT_FUSED_CASE(64, 16)
-  DGT_FUSED_CASE(128, 8)
-  DGT_FUSED_CASE(128, 16)
+  if constexpr (DGT_FMT != BF16W) {  // whole bf16 words: 64 lanes only
+    DGT_FUSED_CASE(128, 8)
+    DGT_FUSED_CASE(128, 16)
+    if (ring) return DGT_E_UNSUPPORTED;
+    if (lanes == 32 && fn == 8) return fused_r<32, 8, false>(a, mt, mix, grid, threads, lds, st);
+    if (lanes == 32 && fn == 16) return fused_r<32, 16, false>(a, mt, mix, grid, threads, lds, st);
+  }
 #undef DGT_FUSED_CASE
-  if (ring) return DGT_E_UNSUPPORTED;
-  if (lanes == 32 && fn == 8) return fused_r<32, 8, false>(a, mt, mix, grid, threads, lds, st);
-  if (lanes == 32 && fn == 16) return fused_r<32, 16, false>(a, mt, mix, grid, threads, lds, st);
   return DGT_E_UNSUPPORTED;
 }
 
@@ -96,8 +98,10 @@ int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn,
                : rounds_t<RR, FNV, 1, false>(a, grid, threads, lds, st, blocks_per_cu);
   DGT_ROUNDS_CASE(64, 8)
   DGT_ROUNDS_CASE(64, 16)
-  DGT_ROUNDS_CASE(128, 8)
-  DGT_ROUNDS_CASE(128, 16)
+  if constexpr (DGT_FMT != BF16W) {
+    DGT_ROUNDS_CASE(128, 8)
+    DGT_ROUNDS_CASE(128, 16)
+  }
 #undef DGT_ROUNDS_CASE
   return DGT_E_UNSUPPORTED;
 }
@@ -117,14 +121,16 @@ int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t lanes, uint32_t fn, bool 
   DGT_XM_CASE(64, 8, true, true)
   DGT_XM_CASE(64, 16, false, true)
   DGT_XM_CASE(64, 16, true, true)
-  DGT_XM_CASE(128, 8, false, true)
-  DGT_XM_CASE(128, 8, true, true)
-  DGT_XM_CASE(128, 16, false, true)
-  DGT_XM_CASE(128, 16, true, true)
   DGT_XM_CASE(64, 8, false, false)
   DGT_XM_CASE(64, 8, true, false)
   DGT_XM_CASE(64, 16, false, false)
   DGT_XM_CASE(64, 16, true, false)
+  if constexpr (DGT_FMT != BF16W) {  // whole bf16 words: 64 lanes only
+    DGT_XM_CASE(128, 8, false, true)
+    DGT_XM_CASE(128, 8, true, true)
+    DGT_XM_CASE(128, 16, false, true)
+    DGT_XM_CASE(128, 16, true, true)
+  }
 #undef DGT_XM_CASE
   return DGT_E_UNSUPPORTED;
 }
@@ -143,12 +149,14 @@ int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bo
   DGT_DECODE_CASE(64, 2, false)
   DGT_DECODE_CASE(64, 1, true)
   DGT_DECODE_CASE(64, 2, true)
-  DGT_DECODE_CASE(128, 1, false)
-  DGT_DECODE_CASE(128, 2, false)
-  DGT_DECODE_CASE(128, 1, true)
-  DGT_DECODE_CASE(128, 2, true)
-  DGT_DECODE_CASE(32, 1, false)
-  DGT_DECODE_CASE(32, 2, false)
+  if constexpr (DGT_FMT != BF16W) {
+    DGT_DECODE_CASE(128, 1, false)
+    DGT_DECODE_CASE(128, 2, false)
+    DGT_DECODE_CASE(128, 1, true)
+    DGT_DECODE_CASE(128, 2, true)
+    DGT_DECODE_CASE(32, 1, false)
+    DGT_DECODE_CASE(32, 2, false)
+  }
 #undef DGT_DECODE_CASE
   return DGT_E_UNSUPPORTED;
 }
@@ -156,7 +164,7 @@ int launch_decode<DGT_FMT>(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bo
 template <>
 int launch_dense<DGT_FMT>(const DenseArgs& d, uint32_t fn, uint32_t mt, uint32_t grid,
                           uint32_t threads, uint32_t lds, hipStream_t st) {
-  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E || DGT_FMT == BF16P) {
+  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E || DGT_FMT == BF16P || DGT_FMT == BF16W) {
     return DGT_E_UNSUPPORTED;  // their decoded weights are read as INT4 / BF16_SPLIT
   } else {
 #define DGT_DENSE_CASE(FNV, MTV)                                                        \

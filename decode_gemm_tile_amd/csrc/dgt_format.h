@@ -27,9 +27,13 @@ struct HeaderLayout {
                           total = 88, max_tile_words4 = 96, kmax = 100;
 };
 
-inline uint32_t alphabet_of(uint32_t fmt) { return fmt == 2 ? 16u : fmt == 7 ? 65536u : 256u; }
-// formats whose table lists the present symbols only: u32 symbol | f << 16
-inline bool sparse_table(uint32_t fmt) { return fmt == 7; }
+inline uint32_t alphabet_of(uint32_t fmt) {
+  return fmt == 2 ? 16u : (fmt == 7 || fmt == 8) ? 65536u : 256u;
+}
+// formats whose table lists the present symbols only: u32 symbol | (f - bias) << 16
+inline bool sparse_table(uint32_t fmt) { return fmt == 7 || fmt == 8; }
+// BF16_WORD (frequency precision 16 bits) stores f - 1, so that f = 2^16 fits
+inline uint32_t sparse_f_bias(uint32_t fmt) { return fmt == 8 ? 1u : 0u; }
 // weights coded per symbol (INT4_PAIR and BF16_PAIR pack two along K)
 inline uint32_t weights_per_symbol(uint32_t fmt) { return (fmt == 5 || fmt == 7) ? 2u : 1u; }
 // symbols per lane per 16-row fragment (8 weights either way)

@@ -49,11 +49,17 @@ bool geometry_ok(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tn, uint32_t tk,
   return true;
 }
 
+// frequency precision a format allows: 8..15 bits, or exactly 16 for whole
+// bf16 words (a u16 dense entry cannot hold f = 2^16)
+bool prob_bits_ok(uint32_t fmt, uint32_t prob_bits) {
+  if (fmt == DGT_FMT_BF16_WORD) return prob_bits >= 12 && prob_bits <= 16;
+  return prob_bits >= 8 && prob_bits <= 15;
+}
+
 bool params_ok(const dgt_params* p) {
   if (!p) return false;
-  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_PAIR) return false;
-  if (p->prob_bits < 8 || p->prob_bits > 15) return false;
-  return true;
+  if (p->fmt < DGT_FMT_INT8 || p->fmt > DGT_FMT_BF16_WORD) return false;
+  return prob_bits_ok(p->fmt, p->prob_bits);
 }
 
 // Integer frequency quantisation to M = 2^prob_bits (largest remainder, ties
@@ -223,6 +229,9 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
       if (a > 15 || b > 15) return DGT_E_ALPHABET;
       sym[i] = (uint8_t)(a | (b << 4));
     }
+  } else if (fmt == DGT_FMT_BF16_WORD) {
+    const uint16_t* b = static_cast<const uint16_t*>(w);
+    for (uint64_t i = 0; i < NS; ++i) sym[i] = b[i];
   } else if (fmt == DGT_FMT_BF16_SPLIT) {
     raw.resize(NK);
     const uint16_t* b = static_cast<const uint16_t*>(w);
@@ -348,7 +357,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
   if (dgt::sparse_table(fmt)) {
     size_t e = 0;
     for (uint32_t s = 0; s < alpha; ++s)
-      if (f[s]) put<uint32_t>(o, table_off + 4 * e++, s | (f[s] << 16));
+      if (f[s]) put<uint32_t>(o, table_off + 4 * e++, s | ((f[s] - dgt::sparse_f_bias(fmt)) << 16));
   } else {
     for (uint32_t s = 0; s < alpha; ++s) put<uint16_t>(o, table_off + 2 * s, (uint16_t)f[s]);
   }
@@ -399,11 +408,11 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
   in.total_bytes = get<uint64_t>(b, HeaderLayout::total);
   in.max_tile_words4 = get<uint32_t>(b, HeaderLayout::max_tile_words4);
   in.kmax = get<uint32_t>(b, HeaderLayout::kmax);
-  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_PAIR) return DGT_E_FORMAT;
+  if (in.fmt < DGT_FMT_INT8 || in.fmt > DGT_FMT_BF16_WORD) return DGT_E_FORMAT;
   if (in.flags != 0) return DGT_E_FORMAT;
   if (in.total_bytes != size) return DGT_E_CORRUPT;
   if (!geometry_ok(in.fmt, in.n, in.k, in.tile_n, in.tile_k, in.lanes)) return DGT_E_CORRUPT;
-  if (in.prob_bits < 8 || in.prob_bits > 15) return DGT_E_CORRUPT;
+  if (!prob_bits_ok(in.fmt, in.prob_bits)) return DGT_E_CORRUPT;
   const bool sparse = dgt::sparse_table(in.fmt);
   if (sparse ? (in.alphabet == 0 || in.alphabet > (1u << in.prob_bits))
              : in.alphabet != dgt::alphabet_of(in.fmt))
@@ -425,9 +434,10 @@ int dgt_layer_info(const void* blob, size_t size, dgt_info* out) {
     int64_t prev_sym = -1;
     for (uint32_t e = 0; e < in.alphabet; ++e) {
       const uint32_t v = get<uint32_t>(b, in.table_off + 4 * e);
-      if ((int64_t)(v & 0xFFFF) <= prev_sym || (v >> 16) == 0) return DGT_E_CORRUPT;
+      const uint32_t fv = (v >> 16) + dgt::sparse_f_bias(in.fmt);
+      if ((int64_t)(v & 0xFFFF) <= prev_sym || fv == 0) return DGT_E_CORRUPT;
       prev_sym = v & 0xFFFF;
-      fsum += v >> 16;
+      fsum += fv;
     }
   } else {
     for (uint32_t s = 0; s < in.alphabet; ++s) fsum += get<uint16_t>(b, in.table_off + 2 * s);

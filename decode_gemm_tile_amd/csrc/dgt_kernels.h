@@ -89,6 +89,8 @@ template <>
 struct OperandTraits<BF16> { static constexpr int xbytes = 2; };
 template <>
 struct OperandTraits<FP8> { static constexpr int xbytes = 2; };  // e4m3 widened to bf16
+template <>
+struct OperandTraits<BF16W> { static constexpr int xbytes = 2; };
 
 // B operand of one fragment from 8 decoded LUT words (+ raw bytes / scales).
 struct BOp {
@@ -118,6 +120,8 @@ __device__ __forceinline__ uint32_t pair_b(uint32_t e0, uint32_t e1) {
     return __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // two bf16 (exact integers)
   } else if constexpr (FMT == FP8) {
     return __builtin_amdgcn_perm(e1, e0, 0x07030c0cu);  // e4m3 bytes in the high half
+  } else if constexpr (FMT == BF16W) {
+    return e0 | (e1 << 16);  // the two weights' bf16 patterns
   } else {
     return e0;
   }
@@ -143,7 +147,7 @@ __device__ __forceinline__ BOp finish_b(const uint32_t (&q)[4], u32x2 raw, float
       o[i] = (sm & 0x807F807Fu) | (q[i] & ~0x807F807Fu);
     }
     b.v.x = o[0]; b.v.y = o[1]; b.v.z = o[2]; b.v.w = o[3];
-  } else if constexpr (FMT == INT8) {
+  } else if constexpr (FMT == INT8 || FMT == BF16W) {
     b.v.x = q[0]; b.v.y = q[1]; b.v.z = q[2]; b.v.w = q[3];
   } else if constexpr (FMT == INT4) {
     uint32_t o[4];
@@ -529,7 +533,7 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
         }
         if (i == kPrefetchStep) prefetch();
         uint32_t sy[ILP][NS];
-        step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
+        step_all<R, decltype(careful)::value, ILP, RING, sym_mode<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_of<FMT>(a.L));
   const Layer& L = a.L;
   constexpr uint32_t TPC = R == 32 ? 2 : 1;  // tiles per chain
 
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
     if (c < (int)nch) {
       const uint32_t ra = (cw + c) * TPC * L.region_words;
       if constexpr (RING) {
-        ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * ra, lane, c0[c]);
+        ring_start(rg[c], ch[c], smem, tab_of<FMT>(a.L) + 2 * ra, lane, c0[c]);
       } else {
         const uint32_t rb = (R == 32) ? ra + L.region_words : ra;
         cstart[c] = (R == 32 && upper) ? rb : ra;
@@ -666,7 +670,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
         const uint32_t mine = 2 * stg[c].words4;
         const uint32_t na = uniform(mine);
         const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-        const uint32_t ba = tab_bytes<FMT>() + 2 * ra, bb = tab_bytes<FMT>() + 2 * rb;
+        const uint32_t ba = tab_of<FMT>(a.L) + 2 * ra, bb = tab_of<FMT>(a.L) + 2 * rb;
         ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
         ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
       }
@@ -751,7 +755,7 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       ch[c].lim = L.steps - kq[c];
-      ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * (cw + c) * L.region_words, lane, c0[c]);
+      ring_start(rg[c], ch[c], smem, tab_of<FMT>(a.L) + 2 * (cw + c) * L.region_words, lane, c0[c]);
     }
     if (first) {
 #pragma unroll
@@ -828,21 +832,21 @@ __host__ __device__ constexpr int xm_ilp(int FN) { return 1; }
 __host__ __device__ constexpr int xm_tiles(int FN) { return xm_waves(FN) * xm_ilp(FN); }
 // fragments published per barrier: the most (4, 2 or 1) whose doubled buffers
 // stay within 64 KiB of LDS (operands of 1 KiB: tiles x states per lane per
-// fragment)
-__host__ __device__ constexpr int xm_fpb(int R, int FN) {
-  return 2 * 4 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024   ? 4
-         : 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= 64 * 1024 ? 2
-                                                                          : 1;
+// fragment), 32 KiB beside the larger table of whole bf16 words
+__host__ __device__ constexpr int xm_fpb(int R, int FN, int fmt) {
+  const int budget = (fmt == BF16W ? 32 : 64) * 1024;
+  return 2 * 4 * xm_tiles(FN) * states_per_lane(R) * 1024 <= budget   ? 4
+         : 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= budget ? 2
+                                                                       : 1;
 }
 
 // Partials of a strip shared by several workgroups are kept in the
 // accumulators' register layout (slot, wave, row block, fragment, float pair,
 // lane), so every 8-byte store and load of a wave covers 512 contiguous bytes.
 // A slot holds the full NW * MTW * 16 rows.
-template <int FN, int MTW>
+template <int FN, int MTW, int NW = xm_waves(FN)>
 __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW],
                                          uint32_t strip, uint32_t* flag, float out_scale) {
-  constexpr int NW = xm_waves(FN);
   constexpr uint32_t kSlotPairs = NW * MTW * FN * 2 * 64;  // float pairs per slot
   const GemmArgs& a = x.g;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -929,7 +933,7 @@ template <int FMT, int R, int FN, bool RING, bool PP = true>
 __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
   constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
-  constexpr int FPB = xm_fpb(R, FN);
+  constexpr int FPB = xm_fpb(R, FN, FMT);
   static_assert(FNH % FPB == 0 && (NO * FPB) % 4 == 0, "fragment groups");
   constexpr uint32_t FW = 32, TK = 64, FK = TK / FW, G = FK * FNH;
   constexpr int SPF = steps_per_frag<FMT>();
@@ -939,7 +943,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   const Layer& L = a.L;
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_of<FMT>(a.L));
   uint8_t* xbuf = smem + x.xbuf_off;
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + x.xbuf_off - 16);
   const uint32_t lane = lane_id();
@@ -985,7 +989,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
 #pragma unroll
     for (int c = 0; c < ILP; ++c) {
       const uint32_t region = (wave * ILP + c) * L.region_words;
-      const uint32_t base = tab_bytes<FMT>() + 2 * region;
+      const uint32_t base = tab_of<FMT>(a.L) + 2 * region;
       if constexpr (RING) {
         ring_start(rg[c], ch[c], smem, base, lane, c0[c]);
         ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
@@ -1072,7 +1076,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
             }
             if (i == kPrefetchStep) prefetch();
             uint32_t sy[ILP][NS];
-            step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, false, sy);
+            step_all<R, decltype(careful)::value, ILP, RING, sym_mode<FMT>()>(ch, lut, smem, s0 + i, false, sy);
 #pragma unroll
             for (int c = 0; c < ILP; ++c)
 #pragma unroll
@@ -1150,7 +1154,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   u32x2* lut = reinterpret_cast<u32x2*>(smem);
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
-  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_bytes<FMT>());
+  uint16_t* words = reinterpret_cast<uint16_t*>(smem + tab_of<FMT>(a.L));
   const Layer& L = a.L;
   constexpr uint32_t TPC = R == 32 ? 2 : 1;
   constexpr int NS = states_per_lane(R);
@@ -1202,7 +1206,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
   for (int c = 0; c < ILP; ++c) {
     const uint32_t ra = region0 + c * TPC * L.region_words;
     if constexpr (RING) {
-      ring_start(rg[c], ch[c], smem, tab_bytes<FMT>() + 2 * ra, lane, c0[c]);
+      ring_start(rg[c], ch[c], smem, tab_of<FMT>(a.L) + 2 * ra, lane, c0[c]);
       ch[c].p0 = uniform(ch[c].p0); ch[c].s0 = uniform(ch[c].s0); ch[c].e0 = uniform(ch[c].e0);
       rg[c].cc = uniform(rg[c].cc);
       rg[c].nchunks = uniform(rg[c].nchunks);
@@ -1212,7 +1216,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
                                          R != 32 ? lane : half_lane, R != 32 ? 64u : 32u);
       const uint32_t na = uniform(mine);
       const uint32_t nb = (R == 32) ? (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) : na;
-      const uint32_t ba = tab_bytes<FMT>() + 2 * ra, bb = tab_bytes<FMT>() + 2 * rb;
+      const uint32_t ba = tab_of<FMT>(a.L) + 2 * ra, bb = tab_of<FMT>(a.L) + 2 * rb;
       ch[c].p0 = ba; ch[c].s0 = ba; ch[c].e0 = ba + 2 * na;
       ch[c].p1 = bb; ch[c].s1 = bb; ch[c].e1 = bb + 2 * nb;
     }
@@ -1238,7 +1242,7 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
         }
       }
       uint32_t sy[ILP][NS];
-      step_all<R, decltype(careful)::value, ILP, RING, wide_symbols<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
+      step_all<R, decltype(careful)::value, ILP, RING, sym_mode<FMT>()>(ch, lut, smem, s0 + i, upper, sy);
 #pragma unroll
       for (int c = 0; c < ILP; ++c)
 #pragma unroll
@@ -1261,7 +1265,10 @@ __global__ __launch_bounds__(1024) void k_decode(DecodeArgs a) {
         const uint32_t t = tile_lane[c];
         const uint32_t row = (t / L.kt) * L.tile_n + (h * FNH + fn) * 16 + (p & 15);
         const uint32_t col = (t % L.kt) * L.tile_k + fk * FW + 8 * (p >> 4);
-        if constexpr (has_raw_bytes<FMT>()) {
+        if constexpr (FMT == BF16W) {
+          const BOp b = make_b<FMT>(e[c][h], u32x2{0u, 0u}, 0.f, 0.f);
+          *reinterpret_cast<u32x4*>(a.out + ((size_t)row * L.k + col) * 2) = b.v;
+        } else if constexpr (has_raw_bytes<FMT>()) {
           const uint8_t* rp = L.raw + (size_t)t * L.tile_n * L.tile_k + (size_t)g * 8 * R +
                               (64 * h + p) * 8;
           const u32x2 raw = *reinterpret_cast<const u32x2*>(rp);

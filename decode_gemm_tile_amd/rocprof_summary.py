@@ -66,6 +66,9 @@ def cmd_trace(args):
     if args.cmd:
         print("Command: `%s`" % args.cmd)
         print()
+    if args.source_hash:
+        print("- source hash: `%s`" % args.source_hash)
+        print()
     print("| kernel | dispatches | avg us | min us | max us | total us |")
     print("|---|---|---|---|---|---|")
     for name, n, avg, mn, mx, tot in st[:12]:
@@ -80,6 +83,9 @@ def cmd_counters(args):
     print()
     if args.cmd:
         print("Command: `%s`" % args.cmd)
+        print()
+    if args.source_hash:
+        print("- source hash: `%s`" % args.source_hash)
         print()
     print("| counter | median per dispatch | dispatches |")
     print("|---|---|---|")
@@ -122,11 +128,13 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--title", default="")
     t.add_argument("--cmd", default="")
+    t.add_argument("--source-hash", default="")
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--kernel", required=True)
     c.add_argument("--title", default="")
     c.add_argument("--cmd", default="")
+    c.add_argument("--source-hash", default="")
     r = sub.add_parser("traffic")
     r.add_argument("fetch_dir")
     r.add_argument("write_dir")

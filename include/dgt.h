@@ -44,9 +44,10 @@
  *     tiles; u64 table, index, ktab, streams, raw offsets, u64 total size;
  *     u32 max tile length (4-byte units), u32 kmax (16); zero padding.
  *   table  u16 f[alphabet], sum f = 2^prob_bits (shared by all tiles);
- *          BF16_PAIR (alphabet 65536): u32 symbol | f << 16 for each symbol
- *          with f > 0, in increasing symbol order, and the header's alphabet
- *          field holds the number of entries.
+ *          BF16_PAIR and BF16_WORD (alphabet 65536): u32 symbol | f << 16
+ *          (BF16_WORD: symbol | (f - 1) << 16) for each symbol with f > 0, in
+ *          increasing symbol order, and the header's alphabet field holds the
+ *          number of entries.
  *   index  u32 off[tiles+1]: tile t's stream starts at streams + 4*off[t].
  *   ktab   u8 k[tiles]: initial-state payload steps of each tile.
  *   streams per tile: R u32 lane states, u16 words in decode order, zero pad.
@@ -89,9 +90,12 @@ enum dgt_format {
                              q[n,2c] | q[n,2c+1] << 4 (alphabet 256) */
   DGT_FMT_BF16_EXP = 6,   /* bf16: exponent (bits 14..7) coded, sign and mantissa
                              stored raw as one byte (sign << 7 | mantissa) */
-  DGT_FMT_BF16_PAIR = 7   /* bf16 byte split with the high bytes of two weights
+  DGT_FMT_BF16_PAIR = 7,  /* bf16 byte split with the high bytes of two weights
                              adjacent along K coded as one 16-bit symbol
                              hi[n,2c] | hi[n,2c+1] << 8; low bytes raw */
+  DGT_FMT_BF16_WORD = 8   /* bf16 whole words: the 16-bit pattern is the symbol,
+                             frequency precision prob_bits = 16 ([P §4.1]:
+                             16-bit symbols need a precise table), nothing raw */
 };
 
 enum dgt_status {
@@ -106,7 +110,8 @@ enum dgt_status {
   DGT_E_UNSUPPORTED = -8  /* valid request this library does not implement */
 };
 
-/* Layer geometry for compression.  prob_bits: frequency precision n (12). */
+/* Layer geometry for compression.  prob_bits: frequency precision n (12;
+ * BF16_WORD: 16, which the device kernels require for it). */
 typedef struct dgt_params {
   uint32_t fmt, n, k, tile_n, tile_k, lanes, prob_bits, flags;
 } dgt_params;
@@ -134,7 +139,7 @@ size_t dgt_compress_bound(const dgt_params* p);
  *   w: N*K weights row-major: one byte per weight for INT8 (two's
  *      complement), INT4 and INT4_PAIR (values 0..15; INT4_PAIR needs even
  *      K and tile_k) and FP8_E4M3; one uint16 bf16 bit pattern per weight
- *      for BF16_SPLIT and BF16_EXP.
+ *      for BF16_SPLIT, BF16_EXP, BF16_PAIR and BF16_WORD.
  *   out/cap: caller buffer of `cap` bytes; *out_size receives the blob size.
  * Errors: E_ARG, E_SHAPE, E_ALPHABET (INT4 code > 15), E_BUFSIZE.
  * Deterministic: the same input always gives the same bytes. */

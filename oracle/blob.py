@@ -9,18 +9,21 @@ pages give none); all integers are little-endian.
 header (128 bytes)
    0 magic  b"DGT1"              4 u16 version = 1     6 u16 header bytes = 128
    8 u32 fmt (1 int8, 2 int4, 3 fp8 e4m3, 4 bf16 byte split, 5 int4 pairs,
-              6 bf16 exponent split, 7 bf16 byte split with high-byte pairs)
+              6 bf16 exponent split, 7 bf16 byte split with high-byte pairs,
+              8 bf16 whole words)
   12 u32 flags = 0              16 u32 N     20 u32 K
   24 u32 tile_n  28 u32 tile_k  32 u32 lanes R  36 u32 prob_bits n
-  40 u32 alphabet (16 for int4, 256 for the other dense tables; format 7:
-         the number P of table entries)            44 u32 tiles
+  40 u32 alphabet (16 for int4, 256 for the other dense tables; formats 7
+         and 8: the number P of table entries)     44 u32 tiles
   48 u64 table_off   56 u64 index_off   64 u64 ktab_off   72 u64 streams_off
   80 u64 raw_off (0 when the format stores no raw bytes)   88 u64 total bytes
   96 u32 max tile stream length in 4-byte units
  100 u32 kmax (payload-step cap, 16)    104..127 zero
-table   u16 f[alphabet]; format 7 (alphabet 65536, at most 2**n symbols
-        present): u32 entry[P] = symbol | f << 16 for the symbols with f > 0,
-        in increasing symbol order                        (16-byte aligned)
+table   u16 f[alphabet]; formats 7 and 8 (alphabet 65536, at most 2**n
+        symbols present): u32 entry[P] for the symbols with f > 0, in
+        increasing symbol order, entry = symbol | f << 16 (format 7) or
+        symbol | (f - 1) << 16 (format 8, whose n = 16 allows f = 2**16)
+                                                          (16-byte aligned)
 index   u32 off[tiles + 1], 4-byte units from streams_off, off[0] = 0 (aligned)
 ktab    u8 k[tiles]: payload steps of each tile (see ``oracle.rans``) (aligned)
 streams tile t at streams_off + 4*off[t]: R u32 states (lane order) then the
@@ -38,7 +41,11 @@ symbol, alphabet 256; tile_n and tile_k stay in weights, a tile holds
 tile_n*tile_k/2 symbols laid out by ``oracle.order`` with epl = 4); bf16
 high-byte pairs (format 7): the bf16 byte split with the high bytes of two
 weights adjacent along K coded as one 16-bit symbol hi[n, 2c] | hi[n, 2c+1] << 8
-(the same pair geometry as int4 pairs), the low bytes raw as in format 4.
+(the same pair geometry as int4 pairs), the low bytes raw as in format 4;
+bf16 whole words (format 8): the 16-bit pattern itself is the symbol, nothing
+is stored raw, and the table has 2**16 slots (n = 16), the precision the
+pages' 16-bit coding needs ([P1 §4.1] puts the table-precision cost of
+16-bit symbols at 0.1-0.2 bit).
 """
 
 import struct
@@ -52,6 +59,7 @@ VERSION = 1
 HEADER_BYTES = 128
 FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
 FMT_BF16_PAIR = 7
+FMT_BF16_WORD = 8
 _PAIR_FORMATS = (FMT_INT4_PAIR, FMT_BF16_PAIR)
 _HDR = struct.Struct("<4sHHIIIIIIIIII QQQQQQ II 24x")
 assert _HDR.size == HEADER_BYTES
@@ -66,14 +74,19 @@ def alphabet_of(fmt: int) -> int:
         return 16
     if fmt in (FMT_INT8, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP):
         return 256
-    if fmt == FMT_BF16_PAIR:
+    if fmt in (FMT_BF16_PAIR, FMT_BF16_WORD):
         return 65536
     raise ValueError("unknown format")
 
 
 def sparse_table(fmt: int) -> bool:
     """Formats whose table lists only the present symbols (symbol, f)."""
-    return fmt == FMT_BF16_PAIR
+    return fmt in (FMT_BF16_PAIR, FMT_BF16_WORD)
+
+
+def sparse_f_bias(fmt: int) -> int:
+    """A sparse entry stores f - bias in its top 16 bits (format 8: f may be 2**16)."""
+    return 1 if fmt == FMT_BF16_WORD else 0
 
 
 def weights_per_symbol(fmt: int) -> int:
@@ -123,6 +136,8 @@ def symbolise(fmt: int, w):
             raise ValueError("bf16 pairs need an even K")
         hi = (b >> 8).astype(np.uint16)
         return (hi[:, 0::2] | (hi[:, 1::2] << 8)).astype(np.uint16), (b & 0xFF).astype(np.uint8)
+    if fmt == FMT_BF16_WORD:
+        return w.astype(np.uint16), None
     raise ValueError("unknown format")
 
 
@@ -153,7 +168,8 @@ def compress_layer(fmt: int, w, tile_n: int, tile_k: int, lanes: int,
     table_off = HEADER_BYTES
     if sparse_table(fmt):
         present = np.nonzero(f)[0]
-        table = (present.astype(np.uint32) | (f[present].astype(np.uint32) << 16)).astype("<u4")
+        fv = f[present].astype(np.uint32) - sparse_f_bias(fmt)
+        table = (present.astype(np.uint32) | (fv << 16)).astype("<u4")
         table_bytes, alpha_field = table.tobytes(), int(present.size)
     else:
         table_bytes, alpha_field = f.astype("<u2").tobytes(), alpha
@@ -212,7 +228,7 @@ def parse(blob) -> dict:
     a, t = h["alphabet"], h["tiles"]
     if sparse_table(h["fmt"]):
         ent = np.frombuffer(b, "<u4", a, h["table_off"]).astype(np.int64)
-        syms, fs = ent & 0xFFFF, ent >> 16
+        syms, fs = ent & 0xFFFF, (ent >> 16) + sparse_f_bias(h["fmt"])
         if (fs == 0).any() or (np.diff(syms) <= 0).any():
             raise ValueError("bad sparse table")
         h["freq"] = np.zeros(alphabet_of(h["fmt"]), np.int64)
@@ -283,6 +299,8 @@ def decompress_layer(blob) -> np.ndarray:
         raw = np.frombuffer(blob, np.uint8, h["tiles"] * T, h["raw_off"]).reshape(h["tiles"], T)
         lo = order.scatter_tiles(raw, n, k, tn, tk, R, raw=True).astype(np.uint16)
         return (hi << 8) | lo
+    if fmt == FMT_BF16_WORD:
+        return order.scatter_tiles(syms.astype(np.uint16), n, k, tn, tk, R)
     if fmt == FMT_INT4_PAIR:
         pairs = order.scatter_tiles(syms.astype(np.uint8), n, k // 2, tn, tk // 2, R, epl=4)
         out = np.empty((n, k), np.uint8)

@@ -14,6 +14,7 @@ from . import numerics
 
 FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
 FMT_BF16_PAIR = 7
+FMT_BF16_WORD = 8
 
 
 def gemm_fp64(x, w) -> np.ndarray:
@@ -45,7 +46,7 @@ def weight_values(fmt: int, codes, scales_bf16_bits=None) -> np.ndarray:
     int8: the signed code; int4 (single or pair symbols: the same codes and
     values, only the coding differs): bf16_RNE((q-8)*scale); fp8: the e4m3 value
     (the per-tensor weight scale is applied to the product, not here);
-    bf16 (any of the three codings): the bf16 value of the 16-bit pattern.
+    bf16 (any of the four codings): the bf16 value of the 16-bit pattern.
     """
     if fmt == FMT_INT8:
         return np.asarray(codes).astype(np.int8).astype(np.float64)
@@ -54,7 +55,7 @@ def weight_values(fmt: int, codes, scales_bf16_bits=None) -> np.ndarray:
         return numerics.bf16_bits_to_f64(bits)
     if fmt == FMT_FP8:
         return numerics.e4m3_to_f64(codes)
-    if fmt in (FMT_BF16, FMT_BF16_EXP, FMT_BF16_PAIR):
+    if fmt in (FMT_BF16, FMT_BF16_EXP, FMT_BF16_PAIR, FMT_BF16_WORD):
         return numerics.bf16_bits_to_f64(codes)
     raise ValueError("unknown format")
 

@@ -6,7 +6,7 @@ import decode_gemm_tile_amd as dgt
 from oracle import gemm as ogemm
 
 
-BF16_FORMATS = (dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_BF16_EXP, dgt.DGT_FMT_BF16_PAIR)
+BF16_FORMATS = dgt.BF16_FORMATS
 
 
 def to_dev(arr, dtype=None):

@@ -4,8 +4,9 @@
   zero-bit step and a tile's streams are its R states alone;
 - one rare symbol among a constant field (f = 1 for it);
 - full 8-bit alphabets (every int8 byte; every finite e4m3 code);
-- constant bf16 layers in the three bf16 codings (one high byte, one
-  exponent, one high-byte pair) and a two-valued one (four high-byte pairs).
+- constant bf16 layers in the four bf16 codings (one high byte, one
+  exponent, one high-byte pair, one whole word: f = 2^16) and a two-valued
+  one (four high-byte pairs); one rare whole word (f = 1).
 
 Each layer decodes bit-exactly (every tile status 0) and the fused GEMM is
 within 1e-5 relative Frobenius of the fp64 oracle at M = 1 and 16; for the
@@ -57,8 +58,18 @@ def _layer(name, rng):
         d["w_scale"] = 0.01
     elif name.startswith("bf16_constant"):
         fmt = {"split": dgt.DGT_FMT_BF16_SPLIT, "exp": dgt.DGT_FMT_BF16_EXP,
-               "pair": dgt.DGT_FMT_BF16_PAIR}[name.split("_")[-1]]
+               "pair": dgt.DGT_FMT_BF16_PAIR, "word": dgt.DGT_FMT_BF16_WORD}[name.split("_")[-1]]
         codes = np.full((N, K), 0x3F80, np.uint16)  # 1.0
+    elif name == "bf16_rare_word":
+        # one word among 2^17 (f = 1) and copies of another (f = 2^16 - 1)
+        fmt, codes = dgt.DGT_FMT_BF16_WORD, np.full((N, K), 0x3C24, np.uint16)
+        codes[77, 401] = 0xC2F0
+    elif name == "bf16_many_rare_words":
+        # 6000 words once each (f = 1, runs of starts inside every 4-slot
+        # bucket) around one common word
+        fmt, codes = dgt.DGT_FMT_BF16_WORD, np.full((N, K), 0x3F80, np.uint16)
+        words = np.array([w for w in range(0x3000, 0x3000 + 6001) if w != 0x3F80], np.uint16)
+        codes.flat[rng.permutation(N * K)[:words.size]] = words
     elif name == "bf16_two_values_pair":
         fmt = dgt.DGT_FMT_BF16_PAIR
         codes = np.where(rng.random((N, K)) < 0.3, 0xBC24, 0x3C24).astype(np.uint16)
@@ -76,8 +87,11 @@ NAMES = ["int4_constant", "int4_rare_symbol", "int4_pair_constant", "int8_all_by
          "bf16_constant_pair", "bf16_two_values_pair"]
 
 
-@pytest.mark.parametrize("name", NAMES)
-@pytest.mark.parametrize("R", [32, 64, 128])
+WORD_NAMES = ["bf16_constant_word", "bf16_rare_word", "bf16_many_rare_words"]
+
+
+@pytest.mark.parametrize("name,R", [(n, r) for n in NAMES for r in (32, 64, 128)] +
+                         [(n, 64) for n in WORD_NAMES])  # whole words: 64 lanes
 def test_degenerate_layer_decodes_and_multiplies(name, R):
     import torch
     rng = np.random.default_rng(zlib.crc32(("%s/%d" % (name, R)).encode()))
@@ -99,7 +113,7 @@ def test_degenerate_layer_decodes_and_multiplies(name, R):
                                       status=status)
         torch.cuda.synchronize()
         ref = reference(fmt, d, xb)
-        if name == "bf16_constant_split":
+        if name in ("bf16_constant_split", "bf16_constant_word"):
             closed = numerics.bf16_bits_to_f64(xb).sum(axis=1, keepdims=True) * np.ones((1, N))
             assert np.allclose(ref, closed, rtol=0, atol=1e-9)
         assert rel_err(y.cpu().numpy(), ref) <= TOL, (name, R, m)

@@ -30,6 +30,7 @@ TOL = 1e-5
 # codings of the same weights are adjacent, so they share one oracle output
 NAMES = ["int8_1024", "int4_4096", "int4_4096_pair", "int4_4096_r128", "fp8_8192",
          "fp8_8192_r128", "bf16_mlp", "bf16_mlp_exp", "bf16_mlp_r128", "bf16_mlp_pair",
+         "bf16_mlp_word",
          "int4_ffn405", "int4_ffn405_pair", "bf16_ffn405", "bf16_ffn405_pair"]
 _CACHE = {}
 
@@ -40,7 +41,7 @@ def _setup(name):
     _CACHE.clear()  # keep one full-size layer in memory at a time
     d = workloads.make(name)
     wl = d["workload"]
-    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    blob = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes, wl.prob_bits)
     layer = dgt.DeviceLayer(blob)
     _CACHE[name] = (d, wl, blob, layer)
     return _CACHE[name]
@@ -91,7 +92,8 @@ _REF = {}  # oracle outputs of the first rows, shared by codings of the same wei
 def _family(wl):
     """Key of the weight values a workload multiplies (codings of one layer share it)."""
     fam = {dgt.DGT_FMT_INT4_PAIR: dgt.DGT_FMT_INT4, dgt.DGT_FMT_BF16_EXP: dgt.DGT_FMT_BF16_SPLIT,
-           dgt.DGT_FMT_BF16_PAIR: dgt.DGT_FMT_BF16_SPLIT}.get(wl.fmt, wl.fmt)
+           dgt.DGT_FMT_BF16_PAIR: dgt.DGT_FMT_BF16_SPLIT,
+           dgt.DGT_FMT_BF16_WORD: dgt.DGT_FMT_BF16_SPLIT}.get(wl.fmt, wl.fmt)
     return (fam, wl.n, wl.k, wl.seed)
 
 

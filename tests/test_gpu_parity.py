@@ -22,6 +22,7 @@ TOL = 1e-5
 F8, F4, FE, FB, FP, FX = (dgt.DGT_FMT_INT8, dgt.DGT_FMT_INT4, dgt.DGT_FMT_FP8_E4M3,
                           dgt.DGT_FMT_BF16_SPLIT, dgt.DGT_FMT_INT4_PAIR, dgt.DGT_FMT_BF16_EXP)
 FH = dgt.DGT_FMT_BF16_PAIR
+FW = dgt.DGT_FMT_BF16_WORD
 
 # (fmt, N, K, tile_n, tile_k, lanes, seed)
 CASES = [
@@ -53,6 +54,10 @@ CASES = [
     (FH, 256, 256, 128, 32, 32, 25),      # two tiles per wave
     (FH, 256, 4096, 128, 64, 64, 26),     # several workgroups per strip
     (FH, 384, 1024, 128, 64, 128, 27),    # two states per lane
+    # bf16 whole words (16-bit symbols at 16-bit precision, 64 lanes)
+    (FW, 384, 1024, 128, 64, 64, 28),
+    (FW, 512, 448, 256, 64, 64, 29),      # tile_n 256, 7 k-tiles
+    (FW, 256, 4096, 128, 64, 64, 30),     # several workgroups per strip
 ]
 
 
@@ -130,6 +135,11 @@ XM_CASES = [
     (FP, 384, 2048, 128, 64, 64, 49),     # int4 pairs
     (FP, 512, 1024, 256, 64, 64, 50),
     (FX, 256, 2048, 128, 64, 64, 51),     # bf16 exponent split
+    (FH, 384, 1024, 128, 64, 64, 57),     # bf16 high-byte pairs (16-bit symbols)
+    (FH, 512, 1024, 256, 64, 64, 58),
+    (FB, 256, 8192, 256, 64, 64, 59),     # tile_n 256, eight batches per strip
+    (FW, 384, 2048, 128, 64, 64, 60),     # bf16 whole words
+    (FW, 512, 1024, 256, 64, 64, 61),
     (FB, 384, 4096, 128, 64, 128, 55),    # two states per lane: two operands per fragment
     (FE, 512, 1024, 256, 64, 128, 56),
     (F4, 256, 2048, 128, 64, 128, 57),
@@ -209,6 +219,7 @@ STAGING_CASES = [
     (FP, 256, 2048, 128, 64, 128, 75),
     (F8, 256, 2048, 128, 64, 128, 76),
     (FH, 384, 4096, 128, 64, 64, 77),
+    (FW, 384, 4096, 128, 64, 64, 78),
 ]
 
 
@@ -244,6 +255,7 @@ ROUNDS_CASES = [
     (F8, 256, 1024, 128, 32, 32, 83),     # chains of two tiles
     (FE, 512, 1024, 256, 64, 128, 84),    # tile_n 256, two states per lane
     (FP, 384, 2048, 128, 64, 64, 85),     # int4 pairs with scales
+    (FW, 256, 4096, 128, 64, 64, 86),     # bf16 whole words
 ]
 
 

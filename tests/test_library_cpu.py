@@ -58,14 +58,19 @@ CASES = [
     (dgt.DGT_FMT_BF16_PAIR, 512, 128, 256, 64, 64, 21),
     (dgt.DGT_FMT_BF16_PAIR, 128, 128, 128, 32, 32, 22),
     (dgt.DGT_FMT_BF16_PAIR, 256, 128, 128, 64, 128, 23),
+    # bf16 whole words (16-bit precision, f - 1 in the table)
+    (dgt.DGT_FMT_BF16_WORD, 256, 128, 128, 64, 64, 24),
+    (dgt.DGT_FMT_BF16_WORD, 512, 256, 256, 64, 64, 25),
+    (dgt.DGT_FMT_BF16_WORD, 128, 128, 128, 32, 32, 26),
 ]
 
 
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES)
 def test_cpp_encoder_matches_oracle_bytes(fmt, n, k, tn, tk, R, seed):
     d = workloads.random_small(fmt, n, k, seed=seed)
-    ours = dgt.dgt_compress_layer(fmt, d["codes"], tn, tk, R)
-    ref = oblob.compress_layer(fmt, d["codes"], tn, tk, R)
+    pb = 16 if fmt == dgt.DGT_FMT_BF16_WORD else 12
+    ours = dgt.dgt_compress_layer(fmt, d["codes"], tn, tk, R, pb)
+    ref = oblob.compress_layer(fmt, d["codes"], tn, tk, R, prob_bits=pb)
     assert len(ours) == len(ref)
     assert ours == ref
     info = dgt.dgt_layer_info(ours)
@@ -82,7 +87,7 @@ def test_cpp_encoder_matches_oracle_on_small_workloads():
     for name in ("int8_1024", "int4_4096", "int4_4096_pair"):
         d = workloads.make(name)
         wl = d["workload"]
-        ours = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+        ours = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes, wl.prob_bits)
         ref = oblob.compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
         assert ours == ref, name
 
@@ -95,6 +100,13 @@ def test_cpp_encoder_special_tables():
         ref = oblob.compress_layer(oblob.FMT_INT4, codes, 128, 64, 64)
         assert ours == ref
         assert np.array_equal(oblob.decompress_layer(ours), codes)
+    # whole bf16 words: a constant layer (f = 2^16) and a rare word (f = 1)
+    r = np.full((256, 512), 0x4000, np.uint16)
+    r[5, 7] = 1
+    for codes in (np.full((128, 64), 0x3C00, np.uint16), r):
+        ours = dgt.dgt_compress_layer(dgt.DGT_FMT_BF16_WORD, codes, 128, 64, 64, 16)
+        assert ours == oblob.compress_layer(oblob.FMT_BF16_WORD, codes, 128, 64, 64, prob_bits=16)
+        assert dgt.dgt_layer_info(ours).prob_bits == 16
 
 
 def test_compress_errors():
@@ -171,7 +183,7 @@ def test_size_within_a_tenth_of_a_bit_of_entropy_on_256x64_tiles():
     from oracle import entropy as oent
     d = workloads.make("fp8_8192")
     wl = d["workload"]
-    b = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    b = dgt.dgt_compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes, wl.prob_bits)
     sym, _ = oblob.symbolise(wl.fmt, d["codes"])
     h = oent.empirical_entropy(sym, oblob.alphabet_of(wl.fmt))
     bpw = 8.0 * len(b) / (wl.n * wl.k)

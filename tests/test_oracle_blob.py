@@ -34,13 +34,22 @@ CASES = [
     (blob.FMT_BF16_PAIR, 128, 128, 128, 32, 32),
     (blob.FMT_BF16_PAIR, 256, 128, 128, 64, 128),
     (blob.FMT_BF16_PAIR, 32, 32, 16, 16, 16),
+    # bf16 whole words (16-bit symbols at 16-bit precision)
+    (blob.FMT_BF16_WORD, 256, 128, 128, 64, 64),
+    (blob.FMT_BF16_WORD, 512, 128, 256, 64, 64),
+    (blob.FMT_BF16_WORD, 128, 128, 128, 32, 32),
+    (blob.FMT_BF16_WORD, 256, 128, 128, 64, 128),
 ]
+
+
+def _pb(fmt):
+    return 16 if fmt == blob.FMT_BF16_WORD else 12
 
 
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R", CASES)
 def test_round_trip_is_lossless(fmt, n, k, tn, tk, R):
     d = workloads.random_small(fmt, n, k, seed=n + k + fmt)
-    b = blob.compress_layer(fmt, d["codes"], tn, tk, R)
+    b = blob.compress_layer(fmt, d["codes"], tn, tk, R, prob_bits=_pb(fmt))
     out = blob.decompress_layer(b)
     assert out.dtype == np.asarray(d["codes"]).dtype
     assert np.array_equal(out, d["codes"])
@@ -68,16 +77,23 @@ def test_header_layout_and_alignment():
     assert list(raw0) == [int(codes[0, e]) & 0xFF for e in range(8)]
 
 
-def test_bits_per_weight_bounds_on_small_configs():
-    for name in ("int8_1024", "int4_4096"):
-        d = workloads.make(name)
-        wl = d["workload"]
-        b = blob.compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
-        sym, _ = blob.symbolise(wl.fmt, d["codes"])
-        h = entropy.empirical_entropy(sym, blob.alphabet_of(wl.fmt))
-        bpw = blob.bits_per_weight(b, wl.n, wl.k)
-        assert bpw >= h               # Gibbs: a static code cannot beat H_emp
-        assert bpw <= h + 0.15        # per-lane state flush dominates the excess
+@pytest.mark.parametrize("name,excess", [
+    # the int8 layer's geometry is fixed (128x32 tiles, 32 lanes): 4096 weights
+    # per tile leave the per-lane state flush at about 0.13 bit
+    ("int8_1024", 0.15),
+    # where the geometry is free it meets the 0.1-bit target
+    ("int4_4096", 0.1),
+    ("int4_4096_pair", 0.1),
+])
+def test_bits_per_weight_bounds_on_small_configs(name, excess):
+    d = workloads.make(name)
+    wl = d["workload"]
+    b = blob.compress_layer(wl.fmt, d["codes"], wl.tile_n, wl.tile_k, wl.lanes)
+    sym, _ = blob.symbolise(wl.fmt, d["codes"])
+    h = entropy.empirical_entropy(sym, blob.alphabet_of(wl.fmt)) / blob.weights_per_symbol(wl.fmt)
+    bpw = blob.bits_per_weight(b, wl.n, wl.k)
+    assert bpw >= h               # Gibbs: a static code cannot beat H_emp
+    assert bpw <= h + excess      # per-lane state flush dominates the excess
 
 
 def test_int8_config_entropy_is_about_5_bits():
@@ -208,3 +224,42 @@ def test_bf16_pair_symbols_sparse_table_and_size():
     b4 = blob.compress_layer(blob.FMT_BF16, d["codes"], 128, 64, 64)
     extra = blob.bits_per_weight(b7, 256, 1024) - blob.bits_per_weight(b4, 256, 1024)
     assert -0.05 < extra < 0.12
+
+
+def test_bf16_word_symbols_table_and_size():
+    """bf16 whole words: the 16-bit pattern is the symbol, nothing raw, the
+    table holds symbol | (f - 1) << 16 for the present symbols in symbol order
+    (so a constant layer's f = 2^16 fits), with sum f = 2^16; the blob is at
+    least the empirical entropy of the words (Gibbs) and, beside the table,
+    within the per-lane state flush of it."""
+    w = np.array([[0x3F80, 0xBF80, 0x0001, 0x3F80]], np.uint16)
+    sym, raw = blob.symbolise(blob.FMT_BF16_WORD, w)
+    assert raw is None and sym.dtype == np.uint16 and sym.tolist() == w.tolist()
+    # constant layer: one entry, f = 2^16 stored as 0xFFFF
+    c = np.full((128, 64), 0x3C00, np.uint16)
+    bc = blob.compress_layer(blob.FMT_BF16_WORD, c, 128, 64, 64, prob_bits=16)
+    hc = blob.parse(bc)
+    assert hc["alphabet"] == 1 and hc["raw_off"] == 0 and hc["prob_bits"] == 16
+    assert int(np.frombuffer(bc, "<u4", 1, hc["table_off"])[0]) == 0x3C00 | (0xFFFF << 16)
+    assert hc["freq"][0x3C00] == 1 << 16
+    assert np.array_equal(blob.decompress_layer(bc), c)
+    # a rare word among 2^17 weights: f = 1 stored as 0, the other f = 2^16 - 1
+    r = np.full((256, 512), 0x4000, np.uint16)
+    r[5, 7] = 0x0001
+    br = blob.compress_layer(blob.FMT_BF16_WORD, r, 128, 64, 64, prob_bits=16)
+    hr = blob.parse(br)
+    ent = np.frombuffer(br, "<u4", 2, hr["table_off"])
+    assert ent.tolist() == [0x0001 | (0 << 16), 0x4000 | (0xFFFE << 16)]
+    assert np.array_equal(blob.decompress_layer(br), r)
+    # a Gaussian layer: table of the quantised histogram, size bounds
+    d = workloads.random_small(blob.FMT_BF16_WORD, 512, 1024, seed=19)
+    b = blob.compress_layer(blob.FMT_BF16_WORD, d["codes"], 256, 64, 64, prob_bits=16)
+    h = blob.parse(b)
+    f_ref = freq.quantize_freqs(entropy.histogram(d["codes"], 65536), 16)
+    assert np.array_equal(h["freq"], f_ref) and h["alphabet"] == (f_ref > 0).sum()
+    hw = entropy.empirical_entropy(d["codes"], 65536)
+    bpw = blob.bits_per_weight(b, 512, 1024)
+    table_bits = 8.0 * 4 * h["alphabet"] / (512 * 1024)
+    assert bpw >= hw
+    assert bpw - table_bits <= hw + 0.15
+    assert np.array_equal(blob.decompress_layer(b), d["codes"])

@@ -11,21 +11,29 @@ Recipe (numpy.random.default_rng(seed); W first, then scales, then X):
                 X bf16 [16, 1024] N(0, 1).  Tiles 128x32, 32 lanes.
   int4_4096     W 4096x4096 codes rint(N(8, 1.2)) clipped to [0, 15]; scales
                 bf16 [4096, 32] N(0.01, 0.002) redrawn while <= 0 (one per 128
-                columns); X bf16 [16, 4096] N(0, 1).  Tiles 128x64, 64 lanes.
+                columns); X bf16 [16, 4096] N(0, 1).  Tiles 128x64, 32 lanes.
   fp8_8192      W 8192x8192 bf16 N(0, 0.02), per-tensor scale
                 sw = fl32(amax|W| / 448), codes = e4m3(fl32(W / sw)) (torch's
                 cast); X bf16 [64, 8192] N(0, 1).  Tiles 256x64, 64 lanes.
   bf16_mlp      W 14336x4096 bf16 N(0, 0.02) (Llama-3-8B MLP projection shape);
-                X bf16 [256, 4096] N(0, 1).  Tiles 128x64, 64 lanes.
+                X bf16 [256, 4096] N(0, 1).  Tiles 256x64, 64 lanes.
   int4_ffn405   W 53248x16384 int4 rint(N(8, 1.0)) clipped, scales as int4_4096;
-                X bf16 [256, 16384].  Tiles 128x64, 64 lanes.
+                X bf16 [256, 16384].  Tiles 256x64, 64 lanes.
   int4_4096_pair, int4_ffn405_pair: the two int4 layers above (same seeds,
                 same draws) in the pair-symbol format.
   bf16_mlp_exp  the bf16_mlp layer (same seed, same draws) in the exponent split.
   bf16_mlp_pair, bf16_ffn405_pair: the two bf16 layers (same seeds, same draws)
                 in the byte split with the high bytes coded in pairs.
+  bf16_mlp_word, bf16_ffn405_word: the same layers coded as whole 16-bit
+                words, frequency precision 16 bits.
   *_r128        the named layer (same seed, same draws) coded with two rANS
                 states per lane (R = 128: tile halves of tile_n/2 rows).
+  bf16_mlp_t128, int4_ffn405_t128, bf16_mlp_r32, int4_ffn405_r32,
+  int4_4096_r64 the named layer (same draws) in another tile geometry
+                (128x64 tiles; 32 or 64 lanes).
+Where the configuration leaves the tile geometry or the lane count free, the
+default is one whose compressed size stays within 0.1 bit per weight of the
+empirical entropy (256x64 tiles, or 32 lanes at 128x64).
   bf16_ffn405   W 53248x16384 bf16 N(0, 0.01); X bf16 [256, 16384].
                 Tiles 256x64, 64 lanes.
 rint is numpy's (ties to even); clipping follows rounding.  Casts to bf16 and
@@ -38,7 +46,8 @@ import numpy as np
 
 FMT_INT8, FMT_INT4, FMT_FP8, FMT_BF16, FMT_INT4_PAIR, FMT_BF16_EXP = 1, 2, 3, 4, 5, 6
 FMT_BF16_PAIR = 7
-_BF16_FORMATS = (FMT_BF16, FMT_BF16_EXP, FMT_BF16_PAIR)
+FMT_BF16_WORD = 8
+_BF16_FORMATS = (FMT_BF16, FMT_BF16_EXP, FMT_BF16_PAIR, FMT_BF16_WORD)
 _CHUNK = 1 << 24
 
 
@@ -66,26 +75,26 @@ class Workload:
 WORKLOADS = {
     "int8_1024": Workload("int8_1024", FMT_INT8, 1024, 1024, 128, 32, 32, 101, (16,),
                           w_sigma=8.0, note="int8 codes, H ~ 5 bits"),
-    "int4_4096": Workload("int4_4096", FMT_INT4, 4096, 4096, 128, 64, 64, 202, (1, 16),
+    "int4_4096": Workload("int4_4096", FMT_INT4, 4096, 4096, 128, 64, 32, 202, (1, 16),
                           w_sigma=1.2, w_mean=8.0, note="AWQ-style int4 + group-128 scales"),
     "fp8_8192": Workload("fp8_8192", FMT_FP8, 8192, 8192, 256, 64, 64, 303, (1, 16, 64),
                          w_sigma=0.02, note="e4m3 with per-tensor scale"),
-    "bf16_mlp": Workload("bf16_mlp", FMT_BF16, 14336, 4096, 128, 64, 64, 404, (1, 8, 64, 256),
+    "bf16_mlp": Workload("bf16_mlp", FMT_BF16, 14336, 4096, 256, 64, 64, 404, (1, 8, 64, 256),
                          w_sigma=0.02, note="bf16 N(0,0.02) byte split, Llama-3-8B MLP shape"),
-    "int4_ffn405": Workload("int4_ffn405", FMT_INT4, 53248, 16384, 128, 64, 64, 505,
+    "int4_ffn405": Workload("int4_ffn405", FMT_INT4, 53248, 16384, 256, 64, 64, 505,
                             (1, 8, 64, 256), w_sigma=1.0, w_mean=8.0,
                             note="405B-scale FFN, int4"),
     "bf16_ffn405": Workload("bf16_ffn405", FMT_BF16, 53248, 16384, 256, 64, 64, 506,
                             (1, 8, 64, 256), w_sigma=0.01, note="405B-scale FFN, bf16"),
     # the same int4 layers (same seeds, codes and scales) coded two weights per symbol
-    "int4_4096_pair": Workload("int4_4096_pair", FMT_INT4_PAIR, 4096, 4096, 128, 64, 64, 202,
+    "int4_4096_pair": Workload("int4_4096_pair", FMT_INT4_PAIR, 4096, 4096, 128, 64, 32, 202,
                                (1, 16), w_sigma=1.2, w_mean=8.0,
                                note="int4_4096 coded as int4 pairs"),
-    "int4_ffn405_pair": Workload("int4_ffn405_pair", FMT_INT4_PAIR, 53248, 16384, 128, 64, 64,
+    "int4_ffn405_pair": Workload("int4_ffn405_pair", FMT_INT4_PAIR, 53248, 16384, 256, 64, 64,
                                  505, (1, 8, 64, 256), w_sigma=1.0, w_mean=8.0,
                                  note="int4_ffn405 coded as int4 pairs"),
     # the bf16 MLP layer (same draws) with its exponent coded, sign + mantissa raw
-    "bf16_mlp_exp": Workload("bf16_mlp_exp", FMT_BF16_EXP, 14336, 4096, 128, 64, 64, 404,
+    "bf16_mlp_exp": Workload("bf16_mlp_exp", FMT_BF16_EXP, 14336, 4096, 256, 64, 64, 404,
                              (1, 8, 64, 256), w_sigma=0.02,
                              note="bf16 N(0,0.02) exponent split, Llama-3-8B MLP shape"),
 }
@@ -98,16 +107,23 @@ for _base in ("bf16_mlp", "bf16_ffn405"):
         note=_w.note + ", high bytes coded in pairs")
 # the same layers in other tile geometries (the configurations leave tile shape
 # or lane count free for these): 256x64 tiles, or 32 lanes per tile
-for _base, _tn, _tk, _r, _suffix in (("bf16_mlp", 256, 64, 64, "_t256"),
+for _base, _tn, _tk, _r, _suffix in (("bf16_mlp", 128, 64, 64, "_t128"),
                                      ("bf16_mlp", 128, 64, 32, "_r32"),
-                                     ("int4_ffn405", 256, 64, 64, "_t256"),
+                                     ("int4_ffn405", 128, 64, 64, "_t128"),
                                      ("int4_ffn405", 128, 64, 32, "_r32"),
-                                     ("int4_4096", 128, 64, 32, "_r32")):
+                                     ("int4_4096", 128, 64, 64, "_r64")):
     _w = WORKLOADS[_base]
     WORKLOADS[_base + _suffix] = Workload(
         _base + _suffix, _w.fmt, _w.n, _w.k, _tn, _tk, _r, _w.seed, _w.m_values,
         w_sigma=_w.w_sigma, w_mean=_w.w_mean, prob_bits=_w.prob_bits,
         note=_w.note + ", tiles %dx%d, R = %d" % (_tn, _tk, _r))
+# the bf16 layers (same draws) coded as whole 16-bit words at 16-bit precision
+for _base in ("bf16_mlp", "bf16_ffn405"):
+    _w = WORKLOADS[_base]
+    WORKLOADS[_base + "_word"] = Workload(
+        _base + "_word", FMT_BF16_WORD, _w.n, _w.k, _w.tile_n, _w.tile_k, _w.lanes, _w.seed,
+        _w.m_values, w_sigma=_w.w_sigma, prob_bits=16,
+        note=_w.note.replace("byte split", "whole 16-bit words"))
 # two states per lane: the same layers with R = 128
 for _base in ("int4_4096", "fp8_8192", "bf16_mlp", "int4_ffn405", "bf16_ffn405"):
     _w = WORKLOADS[_base]
