@@ -218,6 +218,13 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
   return std::min(w, ups);
 }
 
+// Workgroups of the fused kernels take their work in XCD-major order
+// (xcd_tile) when DGT_XCD_ORDER=1; results are identical.
+bool xcd_order_from_env() {
+  const char* v = std::getenv("DGT_XCD_ORDER");
+  return v && std::strcmp(v, "1") == 0;
+}
+
 // One fragment buffer instead of two in the large-M kernel (the ablation rung
 // without ping-pong), asked for by DGT_XM_SINGLE_BUFFER=1; results are identical.
 bool xm_single_buffer_from_env() {
@@ -539,6 +546,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     a.red_cols = 0;
     a.rounds = 1;
     a.red_off = 0;
+    a.swz = xcd_order_from_env() ? 1u : 0u;
     x.bps = p.bps;
     x.bpw = p.bpw;
     x.batches = p.batches;
@@ -579,6 +587,7 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     a.red_cols = p.red_cols;
     a.rounds = p.rounds;
     a.red_off = p.red_off;
+    a.swz = xcd_order_from_env() ? 1u : 0u;
     const uint32_t grid = p.wgs, threads = p.threads;
     const bool mix = p.mix != 0;
     int rc;
@@ -896,6 +905,50 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     xsrc = reinterpret_cast<const uint8_t*>(xq);
     sxp = sx;
   }
+  // one row: the streaming GEMV (X staged whole in LDS)
+  if (m == 1 && (size_t)k * 2 <= 64 * 1024) {
+    GemvArgs g;
+    g.w = static_cast<const uint8_t*>(d_w);
+    g.x = reinterpret_cast<const uint16_t*>(xsrc);
+    g.scales = d_scales;
+    g.xscale = sxp;
+    g.w_scale = w_scale;
+    g.y = d_y;
+    g.n = n;
+    g.k = k;
+    switch (fmt) {
+      case DGT_FMT_INT8: return launch_gemv<INT8>(g, st);
+      case DGT_FMT_INT4: return launch_gemv<INT4>(g, st);
+      case DGT_FMT_FP8_E4M3: return launch_gemv<FP8>(g, st);
+      case DGT_FMT_BF16_SPLIT: return launch_gemv<BF16>(g, st);
+      default: return DGT_E_UNSUPPORTED;
+    }
+  }
+  // 32 rows and more: the LDS-tiled GEMM, all rows in one launch
+  if (m >= 32) {
+    DenseTiledArgs t;
+    t.w = static_cast<const uint8_t*>(d_w);
+    t.x = xsrc;
+    t.scales = d_scales;
+    t.xscale = sxp;
+    t.w_scale = w_scale;
+    t.y = d_y;
+    t.m = m;
+    t.n = n;
+    t.k = k;
+    t.x_row_bytes = xrow;
+    t.nmb = (m + kDtRows - 1) / kDtRows;
+    // 64-row blocks of W when 128-row ones would not give every CU two
+    const uint32_t bn = t.nmb * (n / 128) >= 2 * kCUs ? 128u : 64u;
+    t.nnb = n / bn;
+    switch (fmt) {
+      case DGT_FMT_INT8: return launch_dense_tiled<INT8>(t, bn, st);
+      case DGT_FMT_INT4: return launch_dense_tiled<INT4>(t, bn, st);
+      case DGT_FMT_FP8_E4M3: return launch_dense_tiled<FP8>(t, bn, st);
+      case DGT_FMT_BF16_SPLIT: return launch_dense_tiled<BF16>(t, bn, st);
+      default: return DGT_E_UNSUPPORTED;
+    }
+  }
   const uint32_t lds = 64 * 1024;
   for (uint32_t m0 = 0; m0 < m; m0 += mc) {
     DenseArgs d;
@@ -924,6 +977,7 @@ int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const 
     a.red_cols = rc_cols;
     a.rounds = 1;
     a.red_off = 0;
+    a.swz = 0;
     d.w = static_cast<const uint8_t*>(d_w);
     d.n = n;
     d.k = k;

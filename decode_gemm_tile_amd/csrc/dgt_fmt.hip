@@ -182,5 +182,35 @@ int launch_dense<DGT_FMT>(const DenseArgs& d, uint32_t fn, uint32_t mt, uint32_t
   }
 }
 
+template <>
+int launch_dense_tiled<DGT_FMT>(const DenseTiledArgs& d, uint32_t bn, hipStream_t st) {
+  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E || DGT_FMT == BF16P || DGT_FMT == BF16W) {
+    return DGT_E_UNSUPPORTED;
+  } else {
+    auto run = [&](auto k, uint32_t lds) {
+      if (!set_lds(k, lds)) return DGT_E_HIP;
+      hipLaunchKernelGGL(k, dim3(d.nmb * d.nnb), dim3(256), lds, st, d);
+      return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
+    };
+    if (bn == 128) return run(k_dense_tiled<DGT_FMT, 128>, dense_tiled_lds(128));
+    if (bn == 64) return run(k_dense_tiled<DGT_FMT, 64>, dense_tiled_lds(64));
+    return DGT_E_UNSUPPORTED;
+  }
+}
+
+template <>
+int launch_gemv<DGT_FMT>(const GemvArgs& g, hipStream_t st) {
+  if constexpr (DGT_FMT == INT4P || DGT_FMT == BF16E || DGT_FMT == BF16P || DGT_FMT == BF16W) {
+    return DGT_E_UNSUPPORTED;
+  } else {
+    auto k = k_gemv<DGT_FMT>;
+    const uint32_t lds = g.k * 2;
+    if (!set_lds(k, lds)) return DGT_E_HIP;
+    const uint32_t rows = kGvRows * kGvWaves;
+    hipLaunchKernelGGL(k, dim3((g.n + rows - 1) / rows), dim3(64 * kGvWaves), lds, st, g);
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;
+  }
+}
+
 }  // namespace dev
 }  // namespace dgt

@@ -48,7 +48,20 @@ struct GemmArgs {
   uint32_t red_cols;         // tile_n columns reduced per LDS pass
   uint32_t rounds;           // k_fused_rounds: rounds of cpw units per workgroup
   uint32_t red_off;          // k_fused_rounds: LDS byte offset of the reduction buffer
+  uint32_t swz;              // 1: workgroups take their work in XCD-major order (wg_of)
 };
+
+// Workgroup g of T runs on XCD g mod 8 under round-robin dispatch.  xcd_tile
+// numbers the workgroups XCD-major, so that consecutive numbers (work that
+// shares data: the row blocks of one block of Y, the workgroups of one strip)
+// run on one XCD and share its L2.  A bijection of [0, T) for any T.
+__host__ __device__ constexpr uint32_t xcd_tile(uint32_t g, uint32_t T) {
+  return (g % 8) < T % 8 ? (g % 8) * (T / 8 + 1) + g / 8
+                         : (T % 8) * (T / 8 + 1) + ((g % 8) - T % 8) * (T / 8) + g / 8;
+}
+__device__ __forceinline__ uint32_t wg_of(const GemmArgs& a) {
+  return a.swz ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+}
 
 // Static schedule: units (a chain of TPC consecutive k-tiles of one strip for
 // the fused path) are numbered strip-major; workgroup b takes units
@@ -252,7 +265,7 @@ __device__ __forceinline__ void reduce_range(const GemmArgs& a,
                                              uint32_t u1, uint32_t C, uint32_t t) {
   const uint32_t lane = t & 63, wave = t >> 6;
   const uint32_t M = a.m, TN = FN * 16, RC = a.red_cols;
-  const uint32_t wg = blockIdx.x;
+  const uint32_t wg = wg_of(a);
   const uint32_t nw = waves_covering(min(u1 - u0, a.cpw), a.n2);  // active waves
   const uint32_t sA = u0 / a.cps, sB = (u1 - 1) / a.cps;
   const uint32_t split =                                         // waves in strip A
@@ -347,7 +360,7 @@ template <int FN, int MT>
 __device__ __forceinline__ void reduce_and_store(const GemmArgs& a,
                                                  floatx4 (&acc)[acc_bands(FN, MT)][acc_blocks(MT)],
                                                  float* red, float out_scale) {
-  const uint32_t u0 = blockIdx.x * a.cpw;
+  const uint32_t u0 = wg_of(a) * a.cpw;
   reduce_range<FN, MT>(a, acc, red, out_scale, u0, min(u0 + a.cpw, a.chains), a.cpw, threadIdx.x);
 }
 
@@ -600,7 +613,7 @@ __global__ __launch_bounds__(fused_max_threads(R, FN, MT, MIX ? 2 : 1)) void k_f
 
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t u0 = blockIdx.x * a.cpw, u1 = min(u0 + a.cpw, a.chains);
+  const uint32_t u0 = wg_of(a) * a.cpw, u1 = min(u0 + a.cpw, a.chains);
   const uint32_t cw = wave_first_unit(wave, a.n2);
   // chains of this wave: 2 for the first n2 waves, else 1; none past the range
   uint32_t nch = (MIX && wave < a.n2) ? 2u : 1u;
@@ -724,7 +737,7 @@ __device__ __forceinline__ void fused_rounds(const GemmArgs& a, uint8_t* smem, u
   uint32_t* cum = reinterpret_cast<uint32_t*>(smem + kLutBytes);
   float* red = reinterpret_cast<float*>(smem + a.red_off);
   const uint32_t C = a.cpw, CW = a.cpw * a.rounds;
-  const uint32_t U0 = blockIdx.x * CW, U1 = min(U0 + CW, a.chains);
+  const uint32_t U0 = wg_of(a) * CW, U1 = min(U0 + CW, a.chains);
   floatx4 acc[acc_bands(FN, MT)][acc_blocks(MT)];
   for (uint32_t u0 = U0; u0 < U1; u0 += C) {
     const uint32_t lane = lane_id();
@@ -850,7 +863,7 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
   constexpr uint32_t kSlotPairs = NW * MTW * FN * 2 * 64;  // float pairs per slot
   const GemmArgs& a = x.g;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t M = a.m, TN = FN * 16, wg = blockIdx.x;
+  const uint32_t M = a.m, TN = FN * 16, wg = wg_of(a);
   const uint32_t f = strip_first_wg(strip, x.bps, x.bpw), l = strip_last_wg(strip, x.bps, x.bpw);
   // waves whose rows all lie at or past M hold nothing to hand over
   const bool rows = wave * MTW * 16 < M;
@@ -955,7 +968,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   if constexpr (FMT == FP8)
     out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
   const uint32_t fq = table_issue<FMT>(L);
-  const uint32_t b0 = blockIdx.x * x.bpw, b1 = min(b0 + x.bpw, x.batches);
+  const uint32_t b0 = wg_of(a) * x.bpw, b1 = min(b0 + x.bpw, x.batches);
   floatx4 acc[FN][MTW];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn)
@@ -1366,6 +1379,244 @@ __global__ __launch_bounds__(dense_max_threads(FN, MT)) void k_dense(DenseArgs d
   if constexpr (FMT == FP8)
     out_scale = __hip_atomic_load(a.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * a.w_scale;
   reduce_and_store<FN, MT>(a, acc, reinterpret_cast<float*>(smem), out_scale);
+}
+
+// ------------------------------------------- dense GEMM, LDS-tiled (large M)
+// The uncompressed baseline at larger M: a plain tiled GEMM that reads each
+// BN x 64 block of W once per 128 rows of X.  Workgroups of 4 waves compute
+// 128 x BN blocks of Y (each wave a 64 x BN/2 quarter of 16 x 16 MFMA tiles);
+// k advances 64 at a time through two LDS stages of X and W (bf16, rows
+// padded to 144 bytes so the 16 rows an operand read touches fall in distinct
+// banks), the next stage's global loads in flight while the current one is
+// multiplied.  Byte formats are widened to bf16 as they enter LDS, with the
+// fused path's own conversion (the same values).  Blocks are numbered
+// XCD-major (xcd_tile), so the row blocks that read one W block share an L2.
+struct DenseTiledArgs {
+  const uint8_t* w;
+  const uint8_t* x;          // bf16 rows of x_row_bytes (fp8: the quantised X)
+  const uint16_t* scales;    // INT4: bf16 [N, K / 128]
+  const float* xscale;       // FP8: activation scale on the device
+  float w_scale;
+  float* y;                  // fp32 [M, N]
+  uint32_t m, n, k, x_row_bytes;
+  uint32_t nmb, nnb;         // 128-row blocks of M, BN-row blocks of N
+};
+constexpr uint32_t kDtRows = 128, kDtPitch = 144;
+__host__ __device__ constexpr uint32_t dense_tiled_lds(int BN) {
+  return 2 * (kDtRows + BN) * kDtPitch;  // two stages of X block then W block
+}
+
+template <int FMT, int BN>
+__global__ __launch_bounds__(256) void k_dense_tiled(DenseTiledArgs d) {
+  constexpr int NB = BN / 32;  // W chunks per thread and 16-column blocks per wave
+  constexpr uint32_t kStage = (kDtRows + BN) * kDtPitch;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t wave = uniform(tid >> 6), wm = wave & 1u, wn = wave >> 1;
+  const uint32_t tile = xcd_tile(blockIdx.x, d.nmb * d.nnb);
+  const uint32_t m0 = (tile % d.nmb) * kDtRows, n0 = (tile / d.nmb) * BN;
+  const uint32_t kgroups = d.k / 128, kt_end = d.k / 64;
+  // global chunks of this thread: c = tid + 256 i -> row c / 8, elements 8 (c % 8) ..
+  constexpr bool WIDE = FMT == BF16;
+  u32x4 ra[4], rb[NB];
+  u32x2 rbb[NB];
+  float sc[NB];
+  auto gload = [&](uint32_t kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = tid + 256u * i, row = c >> 3, kk = kt * 64u + (c & 7u) * 8u;
+      ra[i] = u32x4{0u, 0u, 0u, 0u};
+      if (m0 + row < d.m)
+        ra[i] = *reinterpret_cast<const u32x4*>(d.x + (size_t)(m0 + row) * d.x_row_bytes + kk * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const uint32_t c = tid + 256u * i, row = c >> 3, kk = kt * 64u + (c & 7u) * 8u;
+      const size_t wr = (size_t)(n0 + row) * d.k + kk;
+      if constexpr (WIDE) {
+        rb[i] = *reinterpret_cast<const u32x4*>(d.w + wr * 2);
+      } else {
+        rbb[i] = *reinterpret_cast<const u32x2*>(d.w + wr);
+        sc[i] = 0.f;
+        if constexpr (FMT == INT4)
+          sc[i] = __uint_as_float((uint32_t)d.scales[(size_t)(n0 + row) * kgroups + kk / 128] << 16);
+      }
+    }
+  };
+  auto lstore = [&](uint32_t stage) __attribute__((always_inline)) {
+    uint8_t* xs = smem + stage * kStage;
+    uint8_t* ws = xs + kDtRows * kDtPitch;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = tid + 256u * i;
+      *reinterpret_cast<u32x4*>(xs + (c >> 3) * kDtPitch + (c & 7u) * 16u) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const uint32_t c = tid + 256u * i, off = (c >> 3) * kDtPitch + (c & 7u) * 16u;
+      if constexpr (WIDE) {
+        *reinterpret_cast<u32x4*>(ws + off) = rb[i];
+      } else {
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[j] = rbb[i].x << (24 - 8 * j);
+          e[4 + j] = rbb[i].y << (24 - 8 * j);
+        }
+        *reinterpret_cast<u32x4*>(ws + off) = make_b<FMT>(e, u32x2{0u, 0u}, sc[i], -8.f * sc[i]).v;
+      }
+    }
+  };
+  floatx4 acc[NB][4];
+#pragma unroll
+  for (int fn = 0; fn < NB; ++fn)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t lrow = (lane & 15u) * kDtPitch, lk = (lane >> 4) * 16u;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (uint32_t kt = 0; kt < kt_end; ++kt) {
+    const bool more = kt + 1 < kt_end;
+    if (more) gload(kt + 1);
+    const uint8_t* xs = smem + (kt & 1u) * kStage;
+    const uint8_t* ws = xs + kDtRows * kDtPitch;
+#pragma unroll
+    for (uint32_t ks = 0; ks < 2; ++ks) {
+      u32x4 A[4];
+      BOp B[NB];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        A[mt] = *reinterpret_cast<const u32x4*>(xs + (wm * 64u + mt * 16u) * kDtPitch + lrow +
+                                                ks * 64u + lk);
+#pragma unroll
+      for (int fn = 0; fn < NB; ++fn)
+        B[fn].v = *reinterpret_cast<const u32x4*>(ws + (wn * (BN / 2) + fn * 16u) * kDtPitch +
+                                                  lrow + ks * 64u + lk);
+#pragma unroll
+      for (int fn = 0; fn < NB; ++fn)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[fn][mt] = mfma<FMT>(A[mt], B[fn], acc[fn][mt]);
+    }
+    // the other stage was last read before the previous barrier
+    if (more) lstore((kt + 1) & 1u);
+    __syncthreads();
+  }
+  float out_scale = 1.f;
+  if constexpr (FMT == FP8)
+    out_scale = __hip_atomic_load(d.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * d.w_scale;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t row = m0 + wm * 64u + mt * 16u + 4u * (lane >> 4) + r;
+      if (row < d.m) {
+#pragma unroll
+        for (int fn = 0; fn < NB; ++fn)
+          d.y[(size_t)row * d.n + n0 + wn * (BN / 2) + fn * 16u + (lane & 15u)] =
+              acc[fn][mt][r] * out_scale;
+      }
+    }
+}
+
+// ------------------------------------------------- dense GEMV (M = 1)
+// One row of X against W streamed once: X in LDS, each wave takes kGvRows
+// rows of W, every lane 8 consecutive k per load (16 bytes of bf16, 8 of the
+// byte formats), the next loads in flight while the current ones are summed
+// in fp32; one wave reduction per row.  Byte formats are widened to bf16
+// with the fused path's conversion, then to fp32.
+struct GemvArgs {
+  const uint8_t* w;
+  const uint16_t* x;
+  const uint16_t* scales;
+  const float* xscale;
+  float w_scale;
+  float* y;
+  uint32_t n, k;
+};
+constexpr uint32_t kGvRows = 4, kGvWaves = 8;
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kGvWaves) void k_gemv(GemvArgs g) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = uniform(tid >> 6);
+  for (uint32_t i = tid; i < g.k / 8; i += blockDim.x)
+    reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(g.x)[i];
+  __syncthreads();
+  const uint32_t r0 = (blockIdx.x * kGvWaves + wave) * kGvRows;
+  if (r0 >= g.n) return;
+  const uint32_t kgroups = g.k / 128;
+  constexpr bool WIDE = FMT == BF16;
+  float sum[kGvRows];
+#pragma unroll
+  for (uint32_t r = 0; r < kGvRows; ++r) sum[r] = 0.f;
+  auto widen = [&](uint32_t row, uint32_t kk, u32x4 wv, u32x2 wb) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (WIDE) {
+      return wv;
+    } else {
+      float s = 0.f;
+      if constexpr (FMT == INT4)
+        s = __uint_as_float((uint32_t)g.scales[(size_t)row * kgroups + kk / 128] << 16);
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = wb.x << (24 - 8 * j);
+        e[4 + j] = wb.y << (24 - 8 * j);
+      }
+      return make_b<FMT>(e, u32x2{0u, 0u}, s, -8.f * s).v;
+    }
+  };
+  auto dot8 = [&](u32x4 wv, u32x4 xv, float acc) __attribute__((always_inline)) -> float {
+    const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w}, xq[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = __builtin_fmaf(__uint_as_float(wq[j] << 16), __uint_as_float(xq[j] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(wq[j] & 0xFFFF0000u), __uint_as_float(xq[j] & 0xFFFF0000u), acc);
+    }
+    return acc;
+  };
+  // 4 chunks of 512 k per row in flight
+  constexpr uint32_t U = 4;
+  for (uint32_t k0 = 0; k0 < g.k; k0 += 512u * U) {
+    u32x4 wv[kGvRows][U];
+    u32x2 wb[kGvRows][U];
+#pragma unroll
+    for (uint32_t r = 0; r < kGvRows; ++r)
+#pragma unroll
+      for (uint32_t u = 0; u < U; ++u) {
+        const uint32_t kk = k0 + u * 512u + lane * 8u;
+        const uint32_t row = min(r0 + r, g.n - 1u);
+        wv[r][u] = u32x4{0u, 0u, 0u, 0u};
+        wb[r][u] = u32x2{0u, 0u};
+        if (kk < g.k) {
+          if constexpr (WIDE)
+            wv[r][u] = *reinterpret_cast<const u32x4*>(g.w + ((size_t)row * g.k + kk) * 2);
+          else
+            wb[r][u] = *reinterpret_cast<const u32x2*>(g.w + (size_t)row * g.k + kk);
+        }
+      }
+#pragma unroll
+    for (uint32_t u = 0; u < U; ++u) {
+      const uint32_t kk = k0 + u * 512u + lane * 8u;
+      if (kk < g.k) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + kk);
+#pragma unroll
+        for (uint32_t r = 0; r < kGvRows; ++r)
+          sum[r] = dot8(widen(min(r0 + r, g.n - 1u), kk, wv[r][u], wb[r][u]), xv, sum[r]);
+      }
+    }
+  }
+  float out_scale = 1.f;
+  if constexpr (FMT == FP8)
+    out_scale = __hip_atomic_load(g.xscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * g.w_scale;
+#pragma unroll
+  for (uint32_t r = 0; r < kGvRows; ++r) {
+    float v = sum[r];
+#pragma unroll
+    for (uint32_t o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0 && r0 + r < g.n) g.y[r0 + r] = v * out_scale;
+  }
 }
 
 }  // namespace dev

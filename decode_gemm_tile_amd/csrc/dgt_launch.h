@@ -26,6 +26,10 @@ int launch_decode(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bool ring, 
 template <int FMT>
 int launch_dense(const DenseArgs& d, uint32_t fn, uint32_t mt, uint32_t grid, uint32_t threads,
                  uint32_t lds, hipStream_t st);
+template <int FMT>
+int launch_dense_tiled(const DenseTiledArgs& d, uint32_t bn, hipStream_t st);
+template <int FMT>
+int launch_gemv(const GemvArgs& g, hipStream_t st);
 
 }  // namespace dev
 }  // namespace dgt

@@ -213,10 +213,13 @@ int dgt_fused_decode_gemm_noalloc(const void* d_blob, const dgt_info* info, cons
                                   uint32_t m, const uint16_t* d_scales, float w_scale,
                                   float* d_y, int32_t* d_status, void* stream);
 
-/* Uncompressed baseline with the same tiling and epilogue, reading W from
- * global memory: d_w is [N, K] in the same element layout dgt_decode_tiles
- * writes (INT4_PAIR is read as INT4, BF16_EXP as BF16_SPLIT).  Workspace from dgt_dense_workspace
- * (zero-filled before first use). */
+/* Uncompressed baseline: Y = X W^T with W read from global memory, d_w is
+ * [N, K] in the same element layout dgt_decode_tiles writes (INT4_PAIR is
+ * read as INT4, BF16_EXP, BF16_PAIR and BF16_WORD as BF16_SPLIT), same weight
+ * values and epilogue as the fused call.  M = 1 runs a streaming GEMV (K <=
+ * 32768), M >= 32 an LDS-tiled MFMA GEMM reading each W block once per 128
+ * rows, the rows between in the fused call's strip decomposition.  Workspace
+ * from dgt_dense_workspace (zero-filled before first use); M <= 256. */
 size_t dgt_dense_workspace(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n,
                            uint32_t m);
 int dgt_dense_gemm(uint32_t fmt, uint32_t n, uint32_t k, uint32_t tile_n, const void* d_w,

@@ -354,14 +354,33 @@ def test_exact_integer_case():
 
 @pytest.mark.parametrize("fmt,tn", [(F8, 128), (F4, 128), (FE, 256), (FB, 128), (FB, 256),
                                     (FP, 128), (FX, 128), (FH, 128)])
-@pytest.mark.parametrize("m", [1, 16, 64])
+@pytest.mark.parametrize("m", [1, 16, 33, 64, 200])
 def test_dense_baseline_matches_oracle(fmt, tn, m):
+    """The uncompressed baseline (GEMV at M = 1, strip kernel below 32 rows,
+    LDS-tiled GEMM from 32 rows, ragged row blocks) against the oracle."""
     import torch
     n, k = 512, 1024
     d = workloads.random_small(fmt, n, k, seed=40 + fmt, m=m)
     w = to_dev(codes_as_u8_or_u16(fmt, d["codes"]))
     scales = to_dev(d["scales"]) if d["scales"] is not None else None
     y = dgt.dgt_dense_gemm(fmt, w, x_dev(d["x"]), tile_n=tn, scales=scales,
+                           w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [FB, F4, FE, F8])
+@pytest.mark.parametrize("n,k,m", [(2048, 4096, 1), (2048, 4096, 256), (32768, 256, 129),
+                                   (32768, 256, 256)])
+def test_dense_baseline_several_blocks_match_oracle(fmt, n, k, m):
+    """Several blocks per XCD and a K of 64 stages (tiled GEMM with 64-row W
+    blocks), 512 blocks and more (128-row W blocks, ragged last row block),
+    and a GEMV over 2048 rows: every output against the fp64 oracle."""
+    import torch
+    d = workloads.random_small(fmt, n, k, seed=60 + fmt, m=m)
+    w = to_dev(codes_as_u8_or_u16(fmt, d["codes"]))
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    y = dgt.dgt_dense_gemm(fmt, w, x_dev(d["x"]), tile_n=128, scales=scales,
                            w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert rel_err(y.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
