@@ -226,7 +226,8 @@ bool xcd_order_from_env() {
 }
 
 // One fragment buffer instead of two in the large-M kernel (the ablation rung
-// without ping-pong), asked for by DGT_XM_SINGLE_BUFFER=1; results are identical.
+// without ping-pong, 64-lane layers), asked for by DGT_XM_SINGLE_BUFFER=1;
+// results are identical.
 bool xm_single_buffer_from_env() {
   const char* v = std::getenv("DGT_XM_SINGLE_BUFFER");
   return v && std::strcmp(v, "1") == 0;
@@ -521,7 +522,8 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
   Layer L = L0;
   L.region_words = p.region_words;
   if (p.xm) {
-    const bool pp = !xm_single_buffer_from_env();
+    // (the one-buffer rung exists for 64-lane layers)
+    const bool pp = !(xm_single_buffer_from_env() && info->lanes == 64);
     XmArgs x;
     GemmArgs& a = x.g;
     a.L = L;

@@ -948,6 +948,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
   constexpr int FPB = xm_fpb(R, FN, FMT);
   static_assert(FNH % FPB == 0 && (NO * FPB) % 4 == 0, "fragment groups");
+  static_assert(FNH % 2 == 0, "fragment parity slots");
   constexpr uint32_t FW = 32, TK = 64, FK = TK / FW, G = FK * FNH;
   constexpr int SPF = steps_per_frag<FMT>();
   constexpr int ADV = ring_group_steps(R);
@@ -1027,6 +1028,23 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
       const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
       return __uint_as_float((uint32_t)sb << 16);
     };
+    // raw bytes and scales of a fragment are loaded one fragment ahead (a
+    // fragment's 8 steps then cover their latency), in the slot of the
+    // fragment's parity (FNH is even, so the parity of g is that of fn)
+    u32x2 rawq[2][ILP][NS];
+    float scq[2][ILP][NS];
+    auto prefetch = [&](uint32_t g, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int h = 0; h < NS; ++h) {
+          rawq[slot][c][h] = u32x2{0u, 0u};
+          scq[slot][c][h] = 0.f;
+          if constexpr (has_raw_bytes<FMT>()) rawq[slot][c][h] = load_raw(c, g, h);
+          if constexpr (FMT == INT4 || FMT == INT4P) scq[slot][c][h] = load_scale(c, g, h);
+        }
+    };
+    prefetch(0, 0);
     // X rows of this wave; rows >= M repeat row M - 1 (their sums are never stored)
     const uint8_t* xp[MTW];
 #pragma unroll
@@ -1057,25 +1075,12 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
         const int fn = f0 + d;
         const uint32_t g = fk * FNH + fn;
         const uint32_t s0 = g * SPF;
-        // this fragment's raw bytes and scales: a fragment's decode (8
-        // dependent steps) outlasts their load, so they are not fetched a
-        // fragment ahead (registers are the budget here); the loads go after
-        // the fragment's last ring advance (a chunk written to the ring waits
-        // for the loads issued before it)
-        u32x2 raw[ILP][NS];
-        float sc[ILP][NS];
-        auto prefetch = [&]() __attribute__((always_inline)) {
-#pragma unroll
-          for (int c = 0; c < ILP; ++c)
-#pragma unroll
-            for (int h = 0; h < NS; ++h) {
-              raw[c][h] = u32x2{0u, 0u};
-              sc[c][h] = 0.f;
-              if constexpr (has_raw_bytes<FMT>()) raw[c][h] = load_raw(c, g, h);
-              if constexpr (FMT == INT4 || FMT == INT4P) sc[c][h] = load_scale(c, g, h);
-            }
-        };
+        // the next fragment's raw bytes and scales: issued after this
+        // fragment's last ring advance (a chunk written to the ring waits for
+        // the loads issued before it)
         constexpr int kPrefetchStep = RING ? ((SPF - 1) / ADV) * ADV : 0;
+        const int cur = fn & 1;  // compile-time once the loops are unrolled
+        const bool has_next = g + 1 < FK * FNH;
         FragAcc<FMT> e[ILP][NS];
         auto steps = [&](auto careful) __attribute__((always_inline)) {
 #pragma unroll
@@ -1087,7 +1092,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
                   ring_advance(rg[c], smem, ch[c].s0, ch[c].p0, lane);
               }
             }
-            if (i == kPrefetchStep) prefetch();
+            if (i == kPrefetchStep && has_next) prefetch(g + 1, cur ^ 1);
             uint32_t sy[ILP][NS];
             step_all<R, decltype(careful)::value, ILP, RING, sym_mode<FMT>()>(ch, lut, smem, s0 + i, false, sy);
 #pragma unroll
@@ -1106,7 +1111,8 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
         for (int c = 0; c < ILP; ++c)
 #pragma unroll
           for (int h = 0; h < NS; ++h) {
-            const BOp bop = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], -8.f * sc[c][h]);
+            const BOp bop = finish_b<FMT>(e[c][h].q, rawq[cur][c][h], scq[cur][c][h],
+                                          -8.f * scq[cur][c][h]);
             *reinterpret_cast<u32x4*>(buf + (d * NO + (c * NW + wave) * NS + h) * 1024 +
                                       lane * 16) = bop.v;
           }
