@@ -68,6 +68,7 @@ def source_hash() -> str:
 VALU_SIMDS = 1024            # 256 CUs x 4 SIMDs
 CLOCK_HZ = 2.4e9
 VALU_CYCLES = 4              # a wave64 VALU instruction occupies a SIMD16 for 4 cycles
+XCDS = 8
 
 
 def valu_from_profiles(workload: str, m: int, kernel_us: float):
@@ -80,11 +81,16 @@ def valu_from_profiles(workload: str, m: int, kernel_us: float):
     text = open(path).read()
     m_hash = re.search(r"source hash:\s*`?([0-9a-f]{16})", text)
     m_val = re.search(r"\| SQ_INSTS_VALU \| ([0-9.eE+]+) \|", text)
+    m_clk = re.search(r"\| GRBM_GUI_ACTIVE \| ([0-9.eE+]+) \|", text)
     if not m_hash or not m_val or m_hash.group(1) != source_hash():
         return None
-    busy_s = float(m_val.group(1)) * VALU_CYCLES / VALU_SIMDS / CLOCK_HZ
-    return {"valu_instructions": float(m_val.group(1)),
-            "valu_issue_frac": round(busy_s / (kernel_us * 1e-6), 4)}
+    busy_cycles = float(m_val.group(1)) * VALU_CYCLES / VALU_SIMDS
+    out = {"valu_instructions": float(m_val.group(1)),
+           "valu_issue_frac_at_2p4ghz": round(busy_cycles / CLOCK_HZ / (kernel_us * 1e-6), 4)}
+    if m_clk:
+        # busy cycles of the GPU during the dispatch, summed over the 8 XCDs
+        out["valu_issue_frac"] = round(busy_cycles / (float(m_clk.group(1)) / XCDS), 4)
+    return out
 
 
 def traffic_from_profiles(workload: str, m: int):
