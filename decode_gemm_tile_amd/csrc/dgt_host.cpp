@@ -367,7 +367,7 @@ int dgt_compress_layer(const dgt_params* p, const void* w, void* out, size_t cap
     uint8_t* dst = o + streams_off + 4 * (size_t)off[t];
     std::memcpy(dst, enc[t].states.data(), 4 * (size_t)R);
     const size_t nw_ = enc[t].words.size();
-    std::memcpy(dst + 4 * R, enc[t].words.data(), 2 * nw_);
+    if (nw_) std::memcpy(dst + 4 * R, enc[t].words.data(), 2 * nw_);  // (a constant layer has none)
     if (nw_ & 1) put<uint16_t>(dst, 4 * (size_t)R + 2 * nw_, 0);
   }
   if (raw_off) {

@@ -116,7 +116,7 @@ for _base, _tn, _tk, _r, _suffix in (("bf16_mlp", 128, 64, 64, "_t128"),
     WORKLOADS[_base + _suffix] = Workload(
         _base + _suffix, _w.fmt, _w.n, _w.k, _tn, _tk, _r, _w.seed, _w.m_values,
         w_sigma=_w.w_sigma, w_mean=_w.w_mean, prob_bits=_w.prob_bits,
-        note=_w.note + ", tiles %dx%d, R = %d" % (_tn, _tk, _r))
+        note=_w.note + ", the other tile geometry")
 # the bf16 layers (same draws) coded as whole 16-bit words at 16-bit precision
 for _base in ("bf16_mlp", "bf16_ffn405"):
     _w = WORKLOADS[_base]
