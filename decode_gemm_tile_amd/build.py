@@ -11,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdgt.so")
+PROBES = os.path.join(HERE, "..", "tests", "probes")
+PROBE_LIB = os.path.join(PROBES, "libmfma_probe.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -77,6 +79,11 @@ def build(verbose: bool = False, jobs: int = None, incremental: bool = False) ->
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"])
     os.replace(tmp, LIB)
+    # the matrix-instruction precision probe the GPU tests load (not part of libdgt)
+    probe_src = os.path.join(PROBES, "mfma_precision.hip")
+    if os.path.exists(probe_src) and (not incremental or _stale(PROBE_LIB, probe_src)):
+        _run([hipcc] + HIP_FLAGS + ["-shared", probe_src, "-o", PROBE_LIB + ".tmp"])
+        os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 
