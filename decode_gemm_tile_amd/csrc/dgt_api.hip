@@ -218,6 +218,13 @@ uint32_t pick_waves(uint32_t units, uint32_t ups, uint32_t cap) {
   return std::min(w, ups);
 }
 
+// Packed accumulators for 2..8 rows (default); DGT_PACKED=0 plans the 16-row
+// block kernels instead (the same products in the same order).
+bool packed_from_env() {
+  const char* v = std::getenv("DGT_PACKED");
+  return !(v && std::strcmp(v, "0") == 0);
+}
+
 // Workgroups of the fused kernels take their work in XCD-major order
 // (xcd_tile) when DGT_XCD_ORDER=1; results are identical.
 bool xcd_order_from_env() {
@@ -321,8 +328,14 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_e
   if (kt % tpc) return false;
   // Tn = 256 keeps 16 row bands of accumulators: 16-row chunks of X only
   p->m_chunk = std::min<uint32_t>(m, in->tile_n == 256 ? 16 : 64);
-  // one row: the single-row mode (row bands packed into one accumulator)
-  p->mt = p->m_chunk == 1 ? 0 : p->m_chunk <= 16 ? 1 : 4;
+  // one row: the single-row mode (row bands packed into one accumulator);
+  // up to 4 or 8 rows at 64 lanes: 4 or 2 bands per accumulator
+  // (DGT_PACKED=0 takes the 16-row block instead)
+  const bool pk = R == 64 && packed_from_env();
+  p->mt = p->m_chunk == 1 ? 0u
+          : (pk && p->m_chunk <= 4) ? (uint32_t)kPacked4
+          : (pk && p->m_chunk <= 8) ? (uint32_t)kPacked8
+          : p->m_chunk <= 16 ? 1u : 4u;
   p->strips = in->n / in->tile_n;
   p->chains = in->tiles / tpc;
   p->cps = kt / tpc;
@@ -378,7 +391,7 @@ bool plan_fused_reg(const dgt_info* in, uint32_t m, bool ring, uint32_t rounds_e
   // partial sums leave the workgroup once.  Ring staging, 16-row blocks of X,
   // full rounds inside one strip (cpw divides the units per strip).  The
   // reduction buffer then sits after the tables, over the rings.
-  if (ring && p->mt <= 1 && R != 32 && p->cps % c == 0) {
+  if (ring && (p->mt <= 1 || mt_packed((int)p->mt)) && R != 32 && p->cps % c == 0) {
     uint32_t rc2 = in->tile_n;
     while (rc2 > 16 && (uint64_t)p->waves * p->m_chunk * rc2 * 4 > c * chain_lds) rc2 /= 2;
     const uint32_t lds2 = tab + std::max<uint32_t>(c * chain_lds, p->waves * p->m_chunk * rc2 * 4);

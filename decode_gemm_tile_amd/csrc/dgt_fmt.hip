@@ -34,6 +34,12 @@ int fused_r(const GemmArgs& a, uint32_t mt, bool mix, uint32_t grid, uint32_t th
   if (mt == 0 && mix) return fused_t<R, FN, 0, true, RING>(a, grid, threads, lds, st);
   if (mt == 1 && !mix) return fused_t<R, FN, 1, false, RING>(a, grid, threads, lds, st);
   if (mt == 1 && mix) return fused_t<R, FN, 1, true, RING>(a, grid, threads, lds, st);
+  if constexpr (R == 64) {  // up to 4 or 8 rows packed: 64 lanes
+    if (mt == kPacked4 && !mix) return fused_t<R, FN, kPacked4, false, RING>(a, grid, threads, lds, st);
+    if (mt == kPacked4 && mix) return fused_t<R, FN, kPacked4, true, RING>(a, grid, threads, lds, st);
+    if (mt == kPacked8 && !mix) return fused_t<R, FN, kPacked8, false, RING>(a, grid, threads, lds, st);
+    if (mt == kPacked8 && mix) return fused_t<R, FN, kPacked8, true, RING>(a, grid, threads, lds, st);
+  }
   if constexpr (FN <= 8) {
     if (mt == 4 && !mix) return fused_t<R, FN, 4, false, RING>(a, grid, threads, lds, st);
     if (mt == 4 && mix) return fused_t<R, FN, 4, true, RING>(a, grid, threads, lds, st);
@@ -98,6 +104,16 @@ int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn,
                : rounds_t<RR, FNV, 1, false>(a, grid, threads, lds, st, blocks_per_cu);
   DGT_ROUNDS_CASE(64, 8)
   DGT_ROUNDS_CASE(64, 16)
+  // up to 4 or 8 rows packed (64 lanes)
+#define DGT_PACKED_CASE(FNV, MTV)                                                             \
+  if (lanes == 64 && fn == FNV && mt == MTV)                                                  \
+    return mix ? rounds_t<64, FNV, MTV, true>(a, grid, threads, lds, st, blocks_per_cu)       \
+               : rounds_t<64, FNV, MTV, false>(a, grid, threads, lds, st, blocks_per_cu);
+  DGT_PACKED_CASE(8, kPacked4)
+  DGT_PACKED_CASE(16, kPacked4)
+  DGT_PACKED_CASE(8, kPacked8)
+  DGT_PACKED_CASE(16, kPacked8)
+#undef DGT_PACKED_CASE
   if constexpr (DGT_FMT != BF16W) {
     DGT_ROUNDS_CASE(128, 8)
     DGT_ROUNDS_CASE(128, 16)

@@ -255,8 +255,20 @@ __device__ __forceinline__ u32x4 load_a(const GemmArgs& a, uint32_t m, uint32_t 
 // band, row band b of the tile is multiplied with an A operand holding X in
 // row b only, so accumulator row b collects band b and one 16x16 accumulator
 // holds all <= 16 bands (4 VGPRs instead of 4 per band).
-__host__ __device__ constexpr int acc_bands(int FN, int MT) { return MT == 0 ? 1 : FN; }
-__host__ __device__ constexpr int acc_blocks(int MT) { return MT == 0 ? 1 : MT; }
+// The same packing holds up to PR = 4 or 8 rows of X (MT = packed_mt(PR)):
+// an accumulator then takes 16 / PR bands, its row PR * (b % (16 / PR)) + m
+// collecting row m of band b, so PR rows cost 4 VGPRs per 16 / PR bands
+// instead of 4 per band.  MT codes: 0 and 16 + PR packed, 1 and 4 the number
+// of 16-row blocks of X.
+__host__ __device__ constexpr int packed_mt(int rows) { return 16 + rows; }
+constexpr int kPacked4 = packed_mt(4), kPacked8 = packed_mt(8);
+__host__ __device__ constexpr bool mt_packed(int MT) { return MT == 0 || MT > 16; }
+__host__ __device__ constexpr int packed_rows(int MT) { return MT > 16 ? MT - 16 : 1; }
+__host__ __device__ constexpr int packed_bands(int MT) { return 16 / packed_rows(MT); }
+__host__ __device__ constexpr int acc_bands(int FN, int MT) {
+  return mt_packed(MT) ? (FN + packed_bands(MT) - 1) / packed_bands(MT) : FN;
+}
+__host__ __device__ constexpr int acc_blocks(int MT) { return mt_packed(MT) ? 1 : MT; }
 
 template <int FN, int MT>
 __device__ __forceinline__ void reduce_range(const GemmArgs& a,
@@ -273,15 +285,19 @@ __device__ __forceinline__ void reduce_range(const GemmArgs& a,
   const uint32_t nstrips = (sA == sB) ? 1u : 2u;
   __syncthreads();  // LUT / staged streams are no longer needed
   for (uint32_t c0 = 0; c0 < TN; c0 += RC) {
-    if (MT == 0 && wave < nw) {
-      // accumulator row 4 * (lane / 16) + i holds band 4 * (lane / 16) + i
+    if (mt_packed(MT) && wave < nw) {
+      // accumulator j, row s = 4 * (lane / 16) + i: row s % PR of band
+      // j * PB + s / PR
+      constexpr uint32_t PR = packed_rows(MT), PB = packed_bands(MT);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t band = 4 * (lane >> 4) + i;
-        const uint32_t col = band * 16 + (lane & 15);
-        if (band < (uint32_t)FN && col >= c0 && col < c0 + RC)
-          red[(size_t)wave * M * RC + (col - c0)] = acc[0][0][i];
-      }
+      for (int j = 0; j < acc_bands(FN, MT); ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t s = 4 * (lane >> 4) + i, band = j * PB + s / PR, m = s % PR;
+          const uint32_t col = band * 16 + (lane & 15);
+          if (band < (uint32_t)FN && m < M && col >= c0 && col < c0 + RC)
+            red[((size_t)wave * M + m) * RC + (col - c0)] = acc[j][0][i];
+        }
     } else if (wave < nw) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
@@ -387,7 +403,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __host__ __device__ constexpr uint32_t fused_max_threads(int R, int FN, int MT, int ILP) {
-  return ((MT == 0 || (MT == 1 && FN <= 8)) && (R != 32 || ILP == 1)) ? 1024u : 512u;
+  // (the two-chain packed kernels fit 128 VGPRs with at most 4 accumulators)
+  return mt_packed(MT) ? (((R != 32 || ILP == 1) && (ILP == 1 || acc_bands(FN, MT) <= 4)) ? 1024u : 512u)
+                       : ((MT == 1 && FN <= 8 && (R != 32 || ILP == 1)) ? 1024u : 512u);
 }
 __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
   return (MT == 1 && FN <= 8) ? 1024u : 512u;
@@ -468,10 +486,10 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
       if constexpr (has_raw_bytes<FMT>()) raw_n[c][h] = load_raw(c, 0, h);
       if constexpr (FMT == INT4 || FMT == INT4P) sc_n[c][h] = load_scale(c, 0, h);
     }
-  constexpr bool kPrefetchA = (MT <= 1);
+  constexpr bool kPrefetchA = mt_packed(MT) || MT == 1;
   constexpr int MB = acc_blocks(MT);
-  // the X row of this lane (single-row mode: row 0 in every lane)
-  const uint32_t xrow = MT == 0 ? 0u : (lane & 15);
+  // the X row of this lane (packed modes: the row its accumulator slot collects)
+  const uint32_t xrow = mt_packed(MT) ? (lane & 15) % packed_rows(MT) : (lane & 15);
   u32x4 A_n[ILP][MB];
   if constexpr (kPrefetchA) {
 #pragma unroll
@@ -480,7 +498,8 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
       for (int mt = 0; mt < MB; ++mt)
         A_n[c][mt] = load_a<FMT>(a, mt * 16 + xrow, kb[c] + koff);
   }
-  // A operands of column block fk (X is fetched one block ahead when MT <= 1)
+  // A operands of column block fk (X is fetched one block ahead in the packed
+  // modes and at MT = 1)
   u32x4 A[ILP][MB];
   auto take_a = [&](uint32_t fk) __attribute__((always_inline)) {
 #pragma unroll
@@ -563,15 +582,17 @@ __device__ __forceinline__ void fused_chains(const GemmArgs& a, const u32x2* lut
 #pragma unroll
       for (int h = 0; h < NS; ++h) {
         const BOp b = finish_b<FMT>(e[c][h].q, raw[c][h], sc[c][h], nsc8[c][h]);
-        if constexpr (MT == 0) {
-          // band h * FNH + fn: X in that row of the A operand only
-          const bool row = (lane & 15) == (uint32_t)(h * FNH + fn);
+        if constexpr (mt_packed(MT)) {
+          // band h * FNH + fn: X in that band's rows of the A operand only
+          constexpr int PR = packed_rows(MT), PB = packed_bands(MT);
+          const int band = h * FNH + fn;
+          const bool row = (lane & 15) / PR == (uint32_t)(band % PB);
           u32x4 ap;
           ap.x = row ? A[c][0].x : 0u;
           ap.y = row ? A[c][0].y : 0u;
           ap.z = row ? A[c][0].z : 0u;
           ap.w = row ? A[c][0].w : 0u;
-          acc[0][0] = mfma<FMT>(ap, b, acc[0][0]);
+          acc[band / PB][0] = mfma<FMT>(ap, b, acc[band / PB][0]);
         } else {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)

@@ -103,7 +103,7 @@ def test_decode_tile_subset(fmt, n, k, tn, tk, R, seed):
 
 
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", CASES)
-@pytest.mark.parametrize("m", [1, 5, 16, 33, 64, 100])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 33, 64, 100])
 def test_fused_gemm_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     import torch
     if fmt in (F4, FP) and k % 128:
@@ -283,6 +283,34 @@ def test_rounds_per_workgroup_match_oracle(fmt, n, k, tn, tk, R, seed, rounds, s
         torch.cuda.synchronize()
         assert rel_err(y.cpu().numpy(), reference(fmt, d, xb)) <= TOL, m
         assert (status.cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,seed", [(FB, 2048, 4096, 256, 94), (F4, 1024, 4096, 128, 95),
+                                              (FE, 1024, 2048, 256, 96), (FW, 1024, 2048, 256, 97)])
+@pytest.mark.parametrize("rounds", ["0", "3"])
+def test_packed_rows_match_row_blocks(fmt, n, k, tn, seed, rounds, monkeypatch):
+    """2..8 rows with the tile's bands packed four (M <= 4) or two (M <= 8) per
+    accumulator give the 16-row block kernels' output bit for bit (the same
+    products in the same order) and the oracle's within the bound, in one
+    round and forced into three rounds per workgroup."""
+    import torch
+    monkeypatch.setenv("DGT_STAGING", "ring")
+    monkeypatch.setenv("DGT_ROUNDS", rounds)
+    d, blob = _layer(fmt, n, k, tn, 64, 64, seed, m=8)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    for m in (2, 3, 4, 5, 8):
+        out = {}
+        for packed in ("1", "0"):
+            monkeypatch.setenv("DGT_PACKED", packed)
+            status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+            y = dgt.dgt_fused_decode_gemm(layer, x_dev(d["x"][:m]), scales=scales,
+                                          w_scale=d["w_scale"], status=status)
+            torch.cuda.synchronize()
+            assert (status.cpu().numpy() == 0).all()
+            out[packed] = y.cpu()
+        assert torch.equal(out["1"], out["0"]), m
+        assert rel_err(out["1"].numpy(), reference(fmt, d, d["x"][:m])) <= TOL, m
 
 
 @pytest.mark.parametrize("fmt,seed", [(F4, 86), (FB, 87)])
