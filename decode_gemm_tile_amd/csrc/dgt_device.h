@@ -409,6 +409,9 @@ __device__ __forceinline__ void step_all(Chain (&c)[ILP], const u32x2* __restric
       if (R != 32 && RING) {
         addr = 2 * rank + (c[i].s0 + (pos & (2 * kRingWords - 1)));
         pos += 2 * (uint32_t)__builtin_popcountll(m);
+        // keep the byte pointer itself in its scalar register (not a word
+        // count the address is rebuilt from at every step)
+        asm volatile("" : "+s"(pos));
       } else if (R != 32) {
         addr = 2 * rank + min(pos, c[i].e0);
         pos += 2 * (uint32_t)__builtin_popcountll(m);
