@@ -73,6 +73,7 @@ VALU_SIMDS = 1024            # 256 CUs x 4 SIMDs
 CLOCK_HZ = 2.4e9
 VALU_CYCLES = 4              # a wave64 VALU instruction occupies a SIMD16 for 4 cycles
 XCDS = 8
+SEC_WARMUP = 10             # untimed launches before each secondary figure (clocks settle)
 
 
 def valu_from_profiles(workload: str, m: int, kernel_us: float):
@@ -299,7 +300,7 @@ def summary_line(dgt, name, dev, stream, reps, ms_list=(1, 256)):
     for m in ms_list:
         if m > d["x"].shape[0]:
             continue
-        ms = timed(r.call(m, stream), reps, 3, stream)
+        ms = timed(r.call(m, stream), reps, SEC_WARMUP, stream)
         out["fused_m%d_ms" % m] = round(ms, 4)
         if m == 1:
             out["decoded_gbs_m1"] = round(nk * STORAGE_BYTES[wl.fmt] / (ms * 1e-3) / 1e9, 3)
@@ -380,7 +381,7 @@ def main():
     if not args.no_secondary:
         reps = max(5, args.steps // 10)
         m2 = min(256, d["x"].shape[0])
-        ms2 = timed(res.call(m2, stream), reps, 3, stream)
+        ms2 = timed(res.call(m2, stream), reps, SEC_WARMUP, stream)
         flops = 2.0 * m2 * nk
         secondary["fused_m%d_ms" % m2] = round(ms2, 4)
         secondary["fused_m%d_tflops" % m2] = round(flops / (ms2 * 1e-3) / 1e12, 3)
@@ -402,9 +403,9 @@ def main():
             msd = timed(lambda i: dgt.dgt_dense_gemm(wl.fmt, wd[i % dcopies], xm,
                                                      tile_n=wl.tile_n, scales=res.scales,
                                                      w_scale=d["w_scale"], y=yd, ws=wsd,
-                                                     stream=stream), reps, 3, stream)
+                                                     stream=stream), reps, SEC_WARMUP, stream)
             ms_fused = ms if mm == m else secondary["fused_m%d_ms" % mm] if mm == m2 else \
-                timed(res.call(mm, stream), reps, 3, stream)
+                timed(res.call(mm, stream), reps, SEC_WARMUP, stream)
             secondary["dense_m%d_ms" % mm] = round(msd, 4)
             if mm == 1:
                 secondary["dense_m1_weight_gbs"] = round(nk * 2 / (msd * 1e-3) / 1e9, 3)
@@ -414,13 +415,13 @@ def main():
             # ablation: layer-level decode to HBM, then the dense GEMM on the
             # decoded copy (two launches per step) against the fused kernel
             ms_dec = timed(lambda i: dgt.dgt_decode_tiles(res.layers[i % copies], out=dec,
-                                                          stream=stream), reps, 3, stream)
+                                                          stream=stream), reps, SEC_WARMUP, stream)
 
             def two_stage(i, xm=xm, yd=yd, wsd=wsd):
                 dgt.dgt_decode_tiles(res.layers[i % copies], out=dec, stream=stream)
                 dgt.dgt_dense_gemm(wl.fmt, dec, xm, tile_n=wl.tile_n, scales=res.scales,
                                    w_scale=d["w_scale"], y=yd, ws=wsd, stream=stream)
-            ms_two = timed(two_stage, reps, 3, stream)
+            ms_two = timed(two_stage, reps, SEC_WARMUP, stream)
             ablation["m%d" % mm] = {"decode_to_hbm_ms": round(ms_dec, 4),
                                     "two_stage_ms": round(ms_two, 4),
                                     "fused_ms": round(ms_fused, 4),
@@ -430,7 +431,7 @@ def main():
                 # large-M kernel (the library reads the switch at every call)
                 os.environ["DGT_XM_SINGLE_BUFFER"] = "1"
                 try:
-                    ms_one = timed(res.call(mm, stream), reps, 3, stream)
+                    ms_one = timed(res.call(mm, stream), reps, SEC_WARMUP, stream)
                 finally:
                     del os.environ["DGT_XM_SINGLE_BUFFER"]
                 ablation["m%d" % mm]["fused_single_buffer_ms"] = round(ms_one, 4)
@@ -439,7 +440,7 @@ def main():
                 # vendor GEMM on the uncompressed bf16 weight (reference point
                 # only), alone and after the layer-level decode
                 wts = [w.view(torch.bfloat16).t().contiguous() for w in wd]
-                ms_lib = timed(lambda i: torch.matmul(xm, wts[i % len(wts)]), reps, 3, stream)
+                ms_lib = timed(lambda i: torch.matmul(xm, wts[i % len(wts)]), reps, SEC_WARMUP, stream)
                 secondary["torch_matmul_bf16_m%d_ms" % mm] = round(ms_lib, 4)
                 del wts
                 decb = dec.view(torch.bfloat16)
@@ -447,7 +448,7 @@ def main():
                 def two_stage_vendor(i, xm=xm):
                     dgt.dgt_decode_tiles(res.layers[i % copies], out=dec, stream=stream)
                     torch.nn.functional.linear(xm, decb)  # x @ W^T, W [N, K] as decoded
-                ms_tv = timed(two_stage_vendor, reps, 3, stream)
+                ms_tv = timed(two_stage_vendor, reps, SEC_WARMUP, stream)
                 ablation["m%d" % mm]["two_stage_vendor_gemm_ms"] = round(ms_tv, 4)
                 ablation["m%d" % mm]["fused_speedup_vs_two_stage_vendor"] = round(
                     ms_tv / ms_fused, 3)
@@ -468,7 +469,7 @@ def main():
             r2 = Resident(dgt, args.workload, dv, blob2, dev)
             var = {"fmt": vfmt, "lanes": vlanes, "bits_per_weight": round(r2.info.bits_per_weight, 4)}
             for mm in (1, m2):
-                var["fused_m%d_ms" % mm] = round(timed(r2.call(mm, stream), reps, 3, stream), 4)
+                var["fused_m%d_ms" % mm] = round(timed(r2.call(mm, stream), reps, SEC_WARMUP, stream), 4)
             var["decoded_gbs_m1"] = round(decoded_bytes / (var["fused_m1_ms"] * 1e-3) / 1e9, 3)
             secondary[vname] = var
             del r2
