@@ -403,8 +403,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __host__ __device__ constexpr uint32_t fused_max_threads(int R, int FN, int MT, int ILP) {
-  // (the two-chain packed kernels fit 128 VGPRs with at most 4 accumulators)
-  return mt_packed(MT) ? (((R != 32 || ILP == 1) && (ILP == 1 || acc_bands(FN, MT) <= 4)) ? 1024u : 512u)
+  // (the packed kernels are held to 128 VGPRs: 16 waves per CU)
+  return mt_packed(MT) ? ((R != 32 || ILP == 1) ? 1024u : 512u)
                        : ((MT == 1 && FN <= 8 && (R != 32 || ILP == 1)) ? 1024u : 512u);
 }
 __host__ __device__ constexpr uint32_t dense_max_threads(int FN, int MT) {
