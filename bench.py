@@ -388,8 +388,9 @@ def main():
         secondary["fused_m%d_mfma_frac" % m2] = round(
             flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         # small batches (packed accumulators up to 8 rows, 16-row blocks to 16)
-        for mm in (2, 4, 8, 16):
-            if mm <= d["x"].shape[0]:
+        # and medium ones (the large-M kernel's 16-wave subset form to 128 rows)
+        for mm in (2, 4, 8, 16, 64, 128):
+            if mm <= d["x"].shape[0] and mm != m2:
                 secondary["fused_m%d_ms" % mm] = round(
                     timed(res.call(mm, stream), reps, SEC_WARMUP, stream), 4)
         wide = wl.fmt in (4, 6, 7, 8)

@@ -204,8 +204,9 @@ struct FusedPlan {
   uint32_t rounds, red_off;
   uint32_t m_chunk;
   size_t part_off, part_bytes, quant_off, ws_bytes;
-  // large-M variant (fragments shared through LDS): used when xm != 0
-  uint32_t xm, bps, bpw, batches, xbuf_off;
+  // large-M variant (fragments shared through LDS): used when xm != 0;
+  // xs > 1: its 16-wave subset form
+  uint32_t xm, bps, bpw, batches, xbuf_off, xs;
 };
 
 constexpr uint32_t kCUs = 256;
@@ -240,19 +241,48 @@ bool xm_single_buffer_from_env() {
   return v && std::strcmp(v, "1") == 0;
 }
 
+// The 16-wave subset form of the large-M kernel for 256-row tiles at M <= 128
+// (DGT_XM_SUBSETS=0 keeps the 8-wave kernel; results agree within rounding).
+bool xm_subsets_from_env() {
+  const char* v = std::getenv("DGT_XM_SUBSETS");
+  return !(v && std::strcmp(v, "0") == 0);
+}
+
 // Large M: one launch in which every tile is decoded once and shared through
 // LDS by waves that own disjoint row blocks, instead of one launch per chunk
 // of rows that each decode the whole layer.  Needs R = 64 or 128 and k-tiles
-// per strip divisible by the workgroup's wave count.
+// per strip divisible by the workgroup's wave count.  With 256-row tiles at
+// 64 lanes and M <= 128 the subset form runs 16 decode chains per CU: 4
+// subsets of 4 row groups (M <= 64) or 2 of 8 (M <= 128).
+bool plan_fused_xm_xs(const dgt_info* in, uint32_t m, bool ring, uint32_t xs, FusedPlan* p);
+
+// The subset form, where the layer and M allow it and it fits (k-tiles per
+// strip, LDS) with the given staging.  Not for int4 codes: with 16 chains per
+// CU their per-fragment scale loads make it slower than the 8-wave form
+// (405B-scale FFN, M = 64: 891 against 865 us; pairs 774 against 700 us).
+// allow: the subset form may be used (DGT_XM_SUBSETS at a call).
+bool plan_fused_xm_sub(const dgt_info* in, uint32_t m, bool ring, bool allow, FusedPlan* p) {
+  const bool sub = allow && in->tile_n == 256 && in->lanes == 64 && m <= 128 &&
+                   in->fmt != DGT_FMT_INT4 && in->fmt != DGT_FMT_INT4_PAIR &&
+                   !xm_single_buffer_from_env();
+  return sub && plan_fused_xm_xs(in, m, ring, m <= 64 ? 4u : 2u, p);
+}
+
+// The 8-wave (or, for 128-row tiles, 16-wave) form.
 bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
+  return plan_fused_xm_xs(in, m, ring, 1u, p);
+}
+
+bool plan_fused_xm_xs(const dgt_info* in, uint32_t m, bool ring, uint32_t xs, FusedPlan* p) {
   p->rounds = 1;
   p->red_off = 0;
   const uint32_t fn = in->tile_n / 16;
   if (in->lanes == 32 || in->tile_k != 64 || (fn != 8 && fn != 16)) return false;
   const uint32_t ns = in->lanes == 128 ? 2 : 1;  // operands per wave and fragment
   if (m <= 16) return false;  // one register-resident pass (one 16-row block) covers M
-  const uint32_t nw = xm_waves(fn), mtw = xm_row_blocks(fn), nt = xm_tiles(fn);
-  if (m > nw * mtw * 16) return false;
+  const uint32_t nw = xm_waves(fn, xs), mtw = xm_row_blocks(fn, xs), nt = xm_tiles(fn, xs);
+  const uint32_t rows = xm_rows(fn, xs);
+  if (m > rows) return false;
   const uint32_t kt = in->k / in->tile_k;
   if (kt % nt) return false;
   p->ring = ring ? 1 : 0;
@@ -260,10 +290,11 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   const uint32_t region_bytes = p->region_words * 2;
   const uint32_t xbuf_off =
       (uint32_t)dgt::align_up((size_t)tab_bytes_layer((int)in->fmt, in->alphabet) + nt * region_bytes + 16, 16);
-  const uint32_t fpb = xm_fpb(in->lanes == 128 ? 128 : 64, fn, (int)in->fmt);
+  const uint32_t fpb = xm_fpb(in->lanes == 128 ? 128 : 64, fn, (int)in->fmt, xs);
   const uint32_t lds = xbuf_off + 2 * fpb * nt * ns * 1024;
   if (lds > kMaxLds) return false;
   p->xm = 1;
+  p->xs = xs;
   p->xbuf_off = xbuf_off;
   p->lds = lds;
   p->strips = in->n / in->tile_n;
@@ -285,7 +316,7 @@ bool plan_fused_xm(const dgt_info* in, uint32_t m, bool ring, FusedPlan* p) {
   size_t off = dgt::align_up((size_t)p->strips * 4, 256);
   p->part_off = off;
   // partial slots hold every row block of the workgroup (register layout)
-  p->part_bytes = (size_t)p->strips * p->slots * (nw * mtw * 16) * in->tile_n * 4;
+  p->part_bytes = (size_t)p->strips * p->slots * rows * in->tile_n * 4;
   off = dgt::align_up(off + p->part_bytes, 256);
   p->quant_off = off;
   if (in->fmt == DGT_FMT_FP8_E4M3) off += dgt::align_up((size_t)m * in->k * 2, 256) + 256;
@@ -438,17 +469,22 @@ Staging staging_from_env() {
 // A forced staging that cannot serve the layer falls back to the choice.
 // rounds: 0 = chosen per layer, else forced rounds per workgroup of the
 // register path (where cpw divides the units per strip).
-bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg, uint32_t rounds) {
+bool plan_fused(const dgt_info* in, uint32_t m, FusedPlan* p, Staging sg, uint32_t rounds,
+                bool sub) {
   const bool r64 = in->lanes != 32;
   bool unused = false;
   if (sg == kRing && r64) {
-    if (plan_fused_xm(in, m, true, p)) return true;
+    if (plan_fused_xm_sub(in, m, true, sub, p) || plan_fused_xm(in, m, true, p)) return true;
     if (plan_fused_reg(in, m, true, rounds, p, &unused)) return true;
   }
   if (sg == kWhole) {
-    if (plan_fused_xm(in, m, false, p)) return true;
+    if (plan_fused_xm_sub(in, m, false, sub, p) || plan_fused_xm(in, m, false, p)) return true;
     if (plan_fused_reg(in, m, false, rounds, p, &unused)) return true;
   }
+  // large M: the subset form (16 decode chains per CU) with either staging
+  // before the 8-wave form
+  if (plan_fused_xm_sub(in, m, false, sub, p)) return true;
+  if (r64 && plan_fused_xm_sub(in, m, true, sub, p)) return true;
   if (plan_fused_xm(in, m, false, p)) return true;
   if (r64 && plan_fused_xm(in, m, true, p)) return true;
   bool lds_bound = false;
@@ -508,16 +544,17 @@ struct CallPlan {
   size_t quant_off, ws_bytes;
 };
 
-bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c, Staging sg, uint32_t rounds) {
+bool plan_call(const dgt_info* in, uint32_t m, CallPlan* c, Staging sg, uint32_t rounds,
+               bool sub) {
   c->n_full = m / kPassRows;
   c->rest_rows = m % kPassRows;
   size_t q = 0;
   if (c->n_full) {
-    if (!plan_fused(in, kPassRows, &c->full, sg, rounds)) return false;
+    if (!plan_fused(in, kPassRows, &c->full, sg, rounds, sub)) return false;
     q = std::max(q, c->full.quant_off);
   }
   if (c->rest_rows) {
-    if (!plan_fused(in, c->rest_rows, &c->rest, sg, rounds)) return false;
+    if (!plan_fused(in, c->rest_rows, &c->rest, sg, rounds, sub)) return false;
     q = std::max(q, c->rest.quant_off);
   }
   c->quant_off = q;
@@ -567,14 +604,14 @@ int launch_pass(const FusedPlan& p, const dgt_info* info, const Layer& L0, const
     x.batches = p.batches;
     x.xbuf_off = p.xbuf_off;
     switch (info->fmt) {
-      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
-      case DGT_FMT_BF16_WORD: return launch_fused_xm<BF16W>(x, info->lanes, fn, rg, pp, p.wgs, p.lds, st);
+      case DGT_FMT_INT8: return launch_fused_xm<INT8>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_INT4: return launch_fused_xm<INT4>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_INT4_PAIR: return launch_fused_xm<INT4P>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_EXP: return launch_fused_xm<BF16E>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_PAIR: return launch_fused_xm<BF16P>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_FP8_E4M3: return launch_fused_xm<FP8>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_SPLIT: return launch_fused_xm<BF16>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
+      case DGT_FMT_BF16_WORD: return launch_fused_xm<BF16W>(x, info->lanes, fn, rg, pp, p.xs, p.wgs, p.lds, st);
       default: return DGT_E_ARG;
     }
   }
@@ -660,15 +697,17 @@ extern "C" {
 
 size_t dgt_gemm_workspace(const dgt_info* info, uint32_t m) {
   if (!info || m == 0 || m > kMaxRows) return 0;
-  // enough for every staging and for one round per workgroup (the most
-  // partial slots), so the environment may change between calls
+  // enough for every staging, for one round per workgroup (the most partial
+  // slots) and for either large-M form, so the environment may change
+  // between calls
   size_t ws = 0;
   for (Staging sg : {kAuto, kWhole, kRing})
-    for (uint32_t rounds : {0u, 1u}) {
-      CallPlan c;
-      if (!plan_call(info, m, &c, sg, rounds)) return 0;
-      ws = std::max(ws, c.ws_bytes);
-    }
+    for (uint32_t rounds : {0u, 1u})
+      for (bool sub : {false, true}) {
+        CallPlan c;
+        if (!plan_call(info, m, &c, sg, rounds, sub)) return 0;
+        ws = std::max(ws, c.ws_bytes);
+      }
   return ws;
 }
 
@@ -689,7 +728,8 @@ int fused_prepare(const void* d_blob, const dgt_info* info, const uint16_t* d_x,
   const uint32_t fn = info->tile_n / 16;
   if (fn != 8 && fn != 16) return DGT_E_UNSUPPORTED;
   if (info->lanes == 32 && (info->k / info->tile_k) % 2) return DGT_E_UNSUPPORTED;
-  if (!plan_call(info, m, c, staging_from_env(), rounds_from_env())) return DGT_E_UNSUPPORTED;
+  if (!plan_call(info, m, c, staging_from_env(), rounds_from_env(), xm_subsets_from_env()))
+    return DGT_E_UNSUPPORTED;
   return DGT_OK;
 }
 

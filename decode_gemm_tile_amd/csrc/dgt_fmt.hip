@@ -123,16 +123,32 @@ int launch_fused_rounds<DGT_FMT>(const GemmArgs& a, uint32_t lanes, uint32_t fn,
 }
 
 // pingpong = false: one fragment buffer (ablation; 64 lanes only).
+// xs > 1: the 16-wave subset kernel (256-row tiles, 64 lanes, M <= 256 / xs).
 template <>
 int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring,
-                             bool pingpong, uint32_t grid, uint32_t lds, hipStream_t st) {
+                             bool pingpong, uint32_t xs, uint32_t grid, uint32_t lds,
+                             hipStream_t st) {
 #define DGT_XM_CASE(RR, FNV, RG, PPV)                                           \
-  if (lanes == RR && fn == FNV && ring == RG && pingpong == PPV) {              \
+  if (lanes == RR && fn == FNV && ring == RG && pingpong == PPV && xs == 1) {   \
     auto k = k_fused_xm<DGT_FMT, RR, FNV, RG, PPV>;                             \
     if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(FNV)), lds, st, x);    \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
   }
+#define DGT_XS_CASE(RG, XSV)                                                    \
+  if (lanes == 64 && fn == 16 && ring == RG && pingpong && xs == XSV) {         \
+    auto k = k_fused_xm<DGT_FMT, 64, 16, RG, true, XSV>;                        \
+    if (!set_lds(k, lds)) return DGT_E_HIP;                                     \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(16, XSV)), lds, st, x); \
+    return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
+  }
+  if constexpr (DGT_FMT != INT4 && DGT_FMT != INT4P) {  // int4 codes keep the 8-wave form
+    DGT_XS_CASE(false, 2)
+    DGT_XS_CASE(true, 2)
+    DGT_XS_CASE(false, 4)
+    DGT_XS_CASE(true, 4)
+  }
+#undef DGT_XS_CASE
   DGT_XM_CASE(64, 8, false, true)
   DGT_XM_CASE(64, 8, true, true)
   DGT_XM_CASE(64, 16, false, true)

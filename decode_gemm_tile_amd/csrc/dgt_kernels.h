@@ -860,34 +860,53 @@ struct XmArgs {
   uint32_t xbuf_off;   // byte offset of the fragment buffers in LDS (16-aligned)
 };
 
-__host__ __device__ constexpr int xm_waves(int FN) { return FN == 8 ? 16 : 8; }
-__host__ __device__ constexpr int xm_row_blocks(int FN) { return FN == 8 ? 1 : 2; }
+// XS = 1: every wave multiplies every tile of the batch into its own row
+// blocks (8 waves x 32 rows for 256-row tiles, 16 x 16 for 128-row tiles).
+// XS > 1 (256-row tiles, M <= 256 / XS): 16 waves in XS subsets of 16 / XS
+// row groups; a wave multiplies only its subset's tiles, so its accumulators
+// and A operands fit 128 VGPRs and a CU runs 16 decode chains instead of 8;
+// the subsets' partial sums are added through LDS before the hand-off.
+__host__ __device__ constexpr int xm_waves(int FN, int XS = 1) {
+  return (FN == 8 || XS > 1) ? 16 : 8;
+}
+__host__ __device__ constexpr int xm_row_blocks(int FN, int XS = 1) {
+  return (FN == 8 || XS > 1) ? 1 : 2;
+}
 __host__ __device__ constexpr int xm_ilp(int FN) { return 1; }
-__host__ __device__ constexpr int xm_tiles(int FN) { return xm_waves(FN) * xm_ilp(FN); }
+__host__ __device__ constexpr int xm_tiles(int FN, int XS = 1) {
+  return xm_waves(FN, XS) * xm_ilp(FN);
+}
+// rows a workgroup holds
+__host__ __device__ constexpr int xm_rows(int FN, int XS = 1) {
+  return xm_waves(FN, XS) / XS * xm_row_blocks(FN, XS) * 16;
+}
 // fragments published per barrier: the most (4, 2 or 1) whose doubled buffers
 // stay within 64 KiB of LDS (operands of 1 KiB: tiles x states per lane per
 // fragment), 32 KiB beside the larger table of whole bf16 words
-__host__ __device__ constexpr int xm_fpb(int R, int FN, int fmt) {
+__host__ __device__ constexpr int xm_fpb(int R, int FN, int fmt, int XS = 1) {
   const int budget = (fmt == BF16W ? 32 : 64) * 1024;
-  return 2 * 4 * xm_tiles(FN) * states_per_lane(R) * 1024 <= budget   ? 4
-         : 2 * 2 * xm_tiles(FN) * states_per_lane(R) * 1024 <= budget ? 2
-                                                                       : 1;
+  return 2 * 4 * xm_tiles(FN, XS) * states_per_lane(R) * 1024 <= budget   ? 4
+         : 2 * 2 * xm_tiles(FN, XS) * states_per_lane(R) * 1024 <= budget ? 2
+                                                                           : 1;
 }
 
 // Partials of a strip shared by several workgroups are kept in the
 // accumulators' register layout (slot, wave, row block, fragment, float pair,
 // lane), so every 8-byte store and load of a wave covers 512 contiguous bytes.
 // A slot holds the full NW * MTW * 16 rows.
+// owner = false: a wave whose sums another wave holds (XS > 1); it takes part
+// in the barriers only.  NW: the waves that own row blocks (waves 0..NW-1).
 template <int FN, int MTW, int NW = xm_waves(FN)>
 __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW],
-                                         uint32_t strip, uint32_t* flag, float out_scale) {
+                                         uint32_t strip, uint32_t* flag, float out_scale,
+                                         bool owner = true) {
   constexpr uint32_t kSlotPairs = NW * MTW * FN * 2 * 64;  // float pairs per slot
   const GemmArgs& a = x.g;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t M = a.m, TN = FN * 16, wg = wg_of(a);
   const uint32_t f = strip_first_wg(strip, x.bps, x.bpw), l = strip_last_wg(strip, x.bps, x.bpw);
   // waves whose rows all lie at or past M hold nothing to hand over
-  const bool rows = wave * MTW * 16 < M;
+  const bool rows = owner && wave * MTW * 16 < M;
   auto store_y = [&](int fn, int mt, floatx4 v) __attribute__((always_inline)) {
     const uint32_t col = strip * TN + fn * 16 + (lane & 15);
     const uint32_t m0 = (wave * MTW + mt) * 16 + 4 * (lane >> 4);
@@ -904,7 +923,7 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
-        store_y(fn, mt, acc[fn][mt]);
+        if (rows) store_y(fn, mt, acc[fn][mt]);
         acc[fn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     return;
@@ -958,17 +977,65 @@ __device__ __forceinline__ void xm_flush(const XmArgs& x, floatx4 (&acc)[FN][MTW
     __hip_atomic_store(&a.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// XS > 1: the waves of subsets 1..XS-1 hand their sums to the wave of subset
+// 0 that owns the same row group, through the (idle) fragment buffers, BP
+// row bands at a time; fixed order, so the result is deterministic.  Every
+// wave ends with zeroed accumulators except the owners.
+template <int FN, int XS, int G, int BP>
+__device__ __forceinline__ void xm_subset_reduce(floatx4 (&acc)[FN][1], uint8_t* xbuf,
+                                                 uint32_t wave, bool has_rows) {
+  const uint32_t lane = lane_id(), sub = wave / G, rg = wave % G;
+#pragma unroll
+  for (int f0 = 0; f0 < FN; f0 += BP) {
+    __syncthreads();  // the buffers' previous readers are done
+    if (sub > 0 && has_rows) {
+      floatx4* slot = reinterpret_cast<floatx4*>(xbuf) + ((sub - 1) * G + rg) * BP * 64 + lane;
+#pragma unroll
+      for (int b = 0; b < BP; ++b) slot[b * 64] = acc[f0 + b][0];
+    }
+    __syncthreads();
+    if (sub == 0 && has_rows) {
+#pragma unroll
+      for (int s2 = 1; s2 < XS; ++s2) {
+        const floatx4* slot =
+            reinterpret_cast<const floatx4*>(xbuf) + ((s2 - 1) * G + rg) * BP * 64 + lane;
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          const floatx4 v = slot[b * 64];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f0 + b][0][i] += v[i];
+        }
+      }
+    }
+  }
+  __syncthreads();  // the buffers are free for the next batch
+  if (sub > 0) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // R = 64 or 128 (one tile per chain) and tile_k = 64 only.  With two states
 // per lane a wave publishes two operands per fragment (the tile's two row
 // halves at the same k), multiplied into the two halves' accumulators.
 // PP = false keeps one fragment buffer (a barrier after the products, before
 // the next group is published): the rung without ping-pong of the ablation.
-template <int FMT, int R, int FN, bool RING, bool PP = true>
-__global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
-  constexpr int NW = xm_waves(FN), MTW = xm_row_blocks(FN), ILP = xm_ilp(FN), NT = NW * ILP;
+template <int FMT, int R, int FN, bool RING, bool PP = true, int XS = 1>
+__global__ __launch_bounds__(64 * xm_waves(FN, XS)) void k_fused_xm(XmArgs x) {
+  constexpr int NW = xm_waves(FN, XS), MTW = xm_row_blocks(FN, XS), ILP = xm_ilp(FN);
+  constexpr int NT = NW * ILP;
+  constexpr int NG = NW / XS;  // row groups (waves of one subset)
+  constexpr int TJ = NT / XS;  // tiles a wave multiplies
   constexpr int NS = states_per_lane(R), FNH = FN / NS, NO = NT * NS;  // operands per fragment
-  constexpr int FPB = xm_fpb(R, FN, FMT);
+  constexpr int NOW = TJ * NS;                                         // ... a wave multiplies
+  constexpr int FPB = xm_fpb(R, FN, FMT, XS);
   static_assert(FNH % FPB == 0 && (NO * FPB) % 4 == 0, "fragment groups");
+  static_assert(XS == 1 || (MTW == 1 && NS == 1 && ILP == 1 && NOW % (4 / FPB) == 0),
+                "subsets: one row block per wave, one state per lane");
+  // row bands per pass of the subset reduction: its slots fit the fragment buffers
+  constexpr int BP = (XS - 1) * NG * 4 * 1024 <= 2 * FPB * NO * 1024   ? 4
+                     : (XS - 1) * NG * 2 * 1024 <= 2 * FPB * NO * 1024 ? 2
+                                                                      : 1;
   static_assert(FNH % 2 == 0, "fragment parity slots");
   constexpr uint32_t FW = 32, TK = 64, FK = TK / FW, G = FK * FNH;
   constexpr int SPF = steps_per_frag<FMT>();
@@ -983,7 +1050,8 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + x.xbuf_off - 16);
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x >> 6);
-  const uint32_t row0 = wave * MTW * 16;
+  const uint32_t sub = wave / NG;  // subset: tiles [sub * TJ, (sub + 1) * TJ) of a batch
+  const uint32_t row0 = (wave % NG) * MTW * 16;
   const bool has_rows = row0 < a.m;
   const uint32_t kgroups = L.k / 128;
   float out_scale = 1.f;
@@ -1075,14 +1143,15 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
                ((size_t)kt0 * TK + 8 * (lane >> 4)) * 2;
     }
     for (uint32_t fk = 0; fk < FK; ++fk) {
-      // X for this wave's rows and the NT k-ranges of fragment column block fk
-      u32x4 A[NT][MTW];
+      // X for this wave's rows and the k-ranges of its TJ tiles, column block fk
+      u32x4 A[TJ][MTW];
       if (has_rows) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int mt = 0; mt < MTW; ++mt)
-            A[j][mt] = *reinterpret_cast<const u32x4*>(xp[mt] + fk * FW * 2 + j * TK * 2);
+            A[j][mt] = *reinterpret_cast<const u32x4*>(xp[mt] + fk * FW * 2 +
+                                                       (sub * TJ + j) * TK * 2);
       }
       // FPB fragments per barrier: each wave decodes and publishes them, then
       // every wave multiplies all of them (alternating accumulators, so
@@ -1140,15 +1209,17 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
         }
         __syncthreads();
         if (has_rows) {
-          // operands are read kXB at a time so their LDS latencies overlap
+          // operands are read kXB at a time so their LDS latencies overlap;
+          // this wave's operands are o = sub * NOW + (0 .. NOW - 1)
           constexpr int kXB = 4;
+          const uint8_t* bufw = buf + sub * NOW * 1024 + lane * 16;
 #pragma unroll
-          for (int o0 = 0; o0 < NO; o0 += kXB / FPB) {
+          for (int o0 = 0; o0 < NOW; o0 += kXB / FPB) {
             BOp bq[kXB];
 #pragma unroll
             for (int q = 0; q < kXB; ++q) {
               const int d = q % FPB, o = o0 + q / FPB;
-              bq[q].v = *reinterpret_cast<const u32x4*>(buf + (d * NO + o) * 1024 + lane * 16);
+              bq[q].v = *reinterpret_cast<const u32x4*>(bufw + (d * NO + o) * 1024);
             }
 #pragma unroll
             for (int q = 0; q < kXB; ++q) {
@@ -1160,7 +1231,7 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
           }
           // keep each group of reads ahead of its products
 #pragma unroll
-          for (int o0 = 0; o0 < NO; o0 += kXB / FPB) {
+          for (int o0 = 0; o0 < NOW; o0 += kXB / FPB) {
             __builtin_amdgcn_sched_group_barrier(0x100, kXB, 0);        // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, kXB * MTW, 0);  // MFMA
           }
@@ -1175,7 +1246,14 @@ __global__ __launch_bounds__(64 * xm_waves(FN)) void k_fused_xm(XmArgs x) {
         if (lane == 0) a.status[tj[c]] = (int32_t)fl;
       }
     }
-    if (b + 1 == b1 || (b + 1) / x.bps != strip) xm_flush<FN, MTW>(x, acc, strip, flag, out_scale);
+    if (b + 1 == b1 || (b + 1) / x.bps != strip) {
+      if constexpr (XS > 1) {
+        xm_subset_reduce<FN, XS, NG, BP>(acc, xbuf, wave, has_rows);
+        xm_flush<FN, MTW, NG>(x, acc, strip, flag, out_scale, sub == 0);
+      } else {
+        xm_flush<FN, MTW>(x, acc, strip, flag, out_scale);
+      }
+    }
   }
 }
 

@@ -19,7 +19,7 @@ int launch_fused_rounds(const GemmArgs& a, uint32_t lanes, uint32_t fn, uint32_t
                         int* blocks_per_cu);
 template <int FMT>
 int launch_fused_xm(const XmArgs& x, uint32_t lanes, uint32_t fn, bool ring, bool pingpong,
-                    uint32_t grid, uint32_t lds, hipStream_t st);
+                    uint32_t xs, uint32_t grid, uint32_t lds, hipStream_t st);
 template <int FMT>
 int launch_decode(const DecodeArgs& a, uint32_t lanes, uint32_t ilp, bool ring, uint32_t grid,
                   uint32_t threads, uint32_t lds, hipStream_t st);

@@ -35,7 +35,10 @@
  *     choice (1 = one round); DGT_XM_SINGLE_BUFFER=1 makes the large-M fused
  *     kernel (17 <= M <= 256 per pass, 64 lanes) keep one fragment buffer
  *     instead of two (a comparison point; an error where no such kernel
- *     exists).  Results are identical.  Read at every call;
+ *     exists).  Results are identical.  DGT_XM_SUBSETS=0 keeps the 8-wave
+ *     large-M kernel where the 16-wave subset form would run (256-row tiles,
+ *     64 lanes, 17 <= M <= 128, not int4 codes); results agree within
+ *     rounding (another order of additions).  Read at every call;
  *     dgt_gemm_workspace covers every choice.
  *
  * Compressed layer ("blob") format, version 1 (all offsets in bytes):
@@ -203,7 +206,8 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
  * runs on holds from the library's load until the process ends.  A call whose
  * workspace (dgt_gemm_workspace) would exceed it returns DGT_E_BUFSIZE and
  * enqueues nothing; M <= 16 fits every layer up to 53248 x 16384 (55 MiB at
- * most), and so does M <= 256 up to 14336 x 4096 (42 MiB).  Each call
+ * most), M <= 64 a 53248 x 16384 bf16 layer (39 MiB), and M <= 256 one up
+ * to 14336 x 4096 (42 MiB).  Each call
  * first zeroes the array's counters with a small kernel on `stream`.  All
  * calls on one device share the array: calls that overlap in time on one
  * device (other streams, other threads) race and give wrong results.  Calls

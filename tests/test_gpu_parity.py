@@ -152,7 +152,7 @@ XM_CASES = [
 
 
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", XM_CASES)
-@pytest.mark.parametrize("m", [17, 65, 100, 256])
+@pytest.mark.parametrize("m", [17, 64, 65, 100, 128, 256])
 def test_fused_gemm_large_m_matches_fp64_oracle(fmt, n, k, tn, tk, R, seed, m):
     import torch
     d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
@@ -178,6 +178,7 @@ def test_large_m_single_buffer_matches_oracle(fmt, n, k, tn, tk, R, seed, stagin
     and the same values as the two-buffer kernel."""
     import torch
     monkeypatch.setenv("DGT_STAGING", staging)
+    monkeypatch.setenv("DGT_XM_SUBSETS", "0")  # the 8-wave form, which has the one-buffer rung
     d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=100)
     layer = dgt.DeviceLayer(blob)
     scales = to_dev(d["scales"]) if d["scales"] is not None else None
@@ -192,6 +193,62 @@ def test_large_m_single_buffer_matches_oracle(fmt, n, k, tn, tk, R, seed, stagin
     assert rel_err(y1.cpu().numpy(), reference(fmt, d, d["x"])) <= TOL
     assert torch.equal(y1, y2)
     assert (status.cpu().numpy() == 0).all()
+
+
+# The 16-wave subset form of the large-M kernel (256-row tiles, 64 lanes,
+# M <= 128): each wave multiplies a quarter (M <= 64) or half (M <= 128) of a
+# batch's 16 tiles and the subsets' sums are added through LDS.
+@pytest.mark.parametrize("staging", ["ring", "whole"])
+@pytest.mark.parametrize("k", [1024, 4096])
+@pytest.mark.parametrize("m", [17, 64, 65, 128])
+def test_large_m_subsets_exact_integer_case(m, k, staging, monkeypatch):
+    """int8 W at 256x64 tiles and integer X in [-4, 4]: every fp32 partial sum
+    is an integer below 2^24, so the subset kernel and the 8-wave kernel must
+    both give the fp64 product exactly (one strip per workgroup at K = 1024,
+    four workgroups per strip at K = 4096)."""
+    import torch
+    monkeypatch.setenv("DGT_STAGING", staging)
+    rng = np.random.default_rng(900 + m + k)
+    d = workloads.random_small(F8, 512, k, seed=910 + m)
+    xi = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    xb = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    blob = dgt.dgt_compress_layer(F8, d["codes"], 256, 64, 64)
+    layer = dgt.DeviceLayer(blob)
+    status = torch.full((layer.info.tiles,), -1, dtype=torch.int32, device="cuda")
+    ws = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, m))
+    y = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), status=status, ws=ws).clone()
+    monkeypatch.setenv("DGT_XM_SUBSETS", "0")   # (its workspace holds 256-row slots)
+    ws8 = dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, m))
+    y8 = dgt.dgt_fused_decode_gemm(layer, x_dev(xb), ws=ws8)
+    torch.cuda.synchronize()
+    ref = ogemm.gemm_fp64(xi.astype(np.float64), d["codes"].astype(np.float64))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    assert np.array_equal(y8.cpu().numpy().astype(np.float64), ref)
+    assert (status.cpu().numpy() == 0).all()
+    assert int(ws[:4 * 2].sum().item()) == 0   # strip counters returned to zero
+
+
+@pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", [c for c in XM_CASES
+                                                   if c[3] == 256 and c[5] == 64])
+@pytest.mark.parametrize("m", [33, 100])
+def test_large_m_subsets_match_eight_wave_kernel(fmt, n, k, tn, tk, R, seed, m, monkeypatch):
+    """Subset form and 8-wave form: both within the bound of the fp64 oracle,
+    each deterministic run to run (they add in different orders)."""
+    import torch
+    d, blob = _layer(fmt, n, k, tn, tk, R, seed, m=m)
+    layer = dgt.DeviceLayer(blob)
+    scales = to_dev(d["scales"]) if d["scales"] is not None else None
+    run = lambda: dgt.dgt_fused_decode_gemm(
+        layer, x_dev(d["x"]), scales=scales, w_scale=d["w_scale"],
+        ws=dgt.alloc_workspace(dgt.dgt_gemm_workspace(layer, m))).clone()
+    ys, ys2 = run(), run()
+    monkeypatch.setenv("DGT_XM_SUBSETS", "0")
+    y8 = run()
+    torch.cuda.synchronize()
+    ref = reference(fmt, d, d["x"])
+    assert rel_err(ys.cpu().numpy(), ref) <= TOL
+    assert rel_err(y8.cpu().numpy(), ref) <= TOL
+    assert torch.equal(ys, ys2)
 
 
 @pytest.mark.parametrize("fmt,n,k,tn,tk,R,seed", [

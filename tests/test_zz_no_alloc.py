@@ -45,13 +45,13 @@ def test_noalloc_matches_workspace_entry_point_twice(layer):
 
 
 def test_noalloc_refuses_oversize_workspace():
-    """fp8 8192 x 8192 at M = 64 needs 73 MiB of workspace: refused, nothing run."""
+    """fp8 8192 x 8192 at M = 256 needs 77 MiB of workspace: refused, nothing run."""
     import torch
     fmt, n, k = dgt.DGT_FMT_FP8_E4M3, 8192, 8192
     d = workloads.random_small(fmt, 1024, 1024, seed=95, m=1)
     codes = np.tile(d["codes"], (n // 1024, k // 1024))
     layer = dgt.DeviceLayer(dgt.dgt_compress_layer(fmt, codes, 256, 64, 64))
-    m = 64
+    m = 256
     assert dgt.dgt_gemm_workspace(layer, m) > dgt.dgt_noalloc_scratch_bytes()
     x = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
     y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
