@@ -257,15 +257,13 @@ bool xm_subsets_from_env() {
 bool plan_fused_xm_xs(const dgt_info* in, uint32_t m, bool ring, uint32_t xs, FusedPlan* p);
 
 // The subset form, where the layer and M allow it and it fits (k-tiles per
-// strip, LDS) with the given staging.  Not for int4 codes: their dequantisation
-// needs enough registers that the 128-VGPR subset kernel keeps accumulators in
-// scratch inside the decode loop (278 spilled VGPRs, 107 for the bf16 split),
-// which makes it slower than the 8-wave form (405B-scale FFN, M = 64: 891
-// against 865 us; pairs 774 against 700 us).
+// strip, LDS) with the given staging.  int4 code pairs take it up to M = 64
+// only: at M = 128 the 8-wave form measured faster (718 against 746 us on the
+// 405B-scale FFN).
 // allow: the subset form may be used (DGT_XM_SUBSETS at a call).
 bool plan_fused_xm_sub(const dgt_info* in, uint32_t m, bool ring, bool allow, FusedPlan* p) {
-  const bool sub = allow && in->tile_n == 256 && in->lanes == 64 && m <= 128 &&
-                   in->fmt != DGT_FMT_INT4 && in->fmt != DGT_FMT_INT4_PAIR &&
+  const uint32_t mmax = in->fmt == DGT_FMT_INT4_PAIR ? 64u : 128u;
+  const bool sub = allow && in->tile_n == 256 && in->lanes == 64 && m <= mmax &&
                    !xm_single_buffer_from_env();
   return sub && plan_fused_xm_xs(in, m, ring, m <= 64 ? 4u : 2u, p);
 }

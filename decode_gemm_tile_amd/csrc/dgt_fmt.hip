@@ -142,12 +142,10 @@ int launch_fused_xm<DGT_FMT>(const XmArgs& x, uint32_t lanes, uint32_t fn, bool 
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * xm_waves(16, XSV)), lds, st, x); \
     return hipGetLastError() == hipSuccess ? DGT_OK : DGT_E_HIP;                \
   }
-  if constexpr (DGT_FMT != INT4 && DGT_FMT != INT4P) {  // int4 codes keep the 8-wave form
-    DGT_XS_CASE(false, 2)
-    DGT_XS_CASE(true, 2)
-    DGT_XS_CASE(false, 4)
-    DGT_XS_CASE(true, 4)
-  }
+  DGT_XS_CASE(false, 2)
+  DGT_XS_CASE(true, 2)
+  DGT_XS_CASE(false, 4)
+  DGT_XS_CASE(true, 4)
 #undef DGT_XS_CASE
   DGT_XM_CASE(64, 8, false, true)
   DGT_XM_CASE(64, 8, true, true)

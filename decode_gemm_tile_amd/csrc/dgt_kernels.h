@@ -1110,12 +1110,31 @@ __global__ __launch_bounds__(64 * xm_waves(FN, XS)) void k_fused_xm(XmArgs x) {
                           (64 * h + lane) * 8;
       return *reinterpret_cast<const u32x2*>(rp);
     };
+    // the scale of the lane's row in band fng: a tile's 64 columns lie in one
+    // 128-column group, so it is the lane's first-band index plus a uniform
+    // band offset.  In the subset form the offset is added where the load is
+    // issued (the empty asm keeps the compiler from computing and loading
+    // every fragment's scale early and holding them all in registers, which
+    // spilled the accumulators inside the decode loop); the 8-wave form has
+    // the registers, and its early loads measured faster
+    size_t sidx[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+      sidx[c] = (size_t)(strip * L.tile_n + (lane & 15)) * kgroups +
+                (kt0 + c * NW + wave) * TK / 128;
     auto load_scale = [&](int c, uint32_t g, int h) __attribute__((always_inline)) -> float {
       const uint32_t fkg = g / FNH, fng = g % FNH;
-      const uint32_t row = strip * L.tile_n + (h * FNH + fng) * 16 + (lane & 15);
-      const uint32_t k0 = (kt0 + c * NW + wave) * TK + 8 * (lane >> 4) + fkg * FW;
-      const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
-      return __uint_as_float((uint32_t)sb << 16);
+      if constexpr (XS > 1) {
+        size_t i0 = sidx[c];
+        asm volatile("" : "+v"(i0));
+        const uint16_t sb = a.scales[i0 + (size_t)((h * FNH + fng) * 16) * kgroups];
+        return __uint_as_float((uint32_t)sb << 16);
+      } else {
+        const uint32_t row = strip * L.tile_n + (h * FNH + fng) * 16 + (lane & 15);
+        const uint32_t k0 = (kt0 + c * NW + wave) * TK + 8 * (lane >> 4) + fkg * FW;
+        const uint16_t sb = a.scales[(size_t)row * kgroups + k0 / 128];
+        return __uint_as_float((uint32_t)sb << 16);
+      }
     };
     // raw bytes and scales of a fragment are loaded one fragment ahead (a
     // fragment's 8 steps then cover their latency), in the slot of the

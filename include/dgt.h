@@ -37,7 +37,7 @@
  *     instead of two (a comparison point; an error where no such kernel
  *     exists).  Results are identical.  DGT_XM_SUBSETS=0 keeps the 8-wave
  *     large-M kernel where the 16-wave subset form would run (256-row tiles,
- *     64 lanes, 17 <= M <= 128, not int4 codes); results agree within
+ *     64 lanes, 17 <= M <= 128, int4 pairs to 64); results agree within
  *     rounding (another order of additions).  Read at every call;
  *     dgt_gemm_workspace covers every choice.
  *
