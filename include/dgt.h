@@ -206,8 +206,8 @@ int dgt_fused_decode_gemm(const void* d_blob, const dgt_info* info, const uint16
  * runs on holds from the library's load until the process ends.  A call whose
  * workspace (dgt_gemm_workspace) would exceed it returns DGT_E_BUFSIZE and
  * enqueues nothing; M <= 16 fits every layer up to 53248 x 16384 (55 MiB at
- * most), and so do M <= 64 (39 MiB at most) and M <= 256 up to 14336 x 4096
- * (42 MiB).  Each call
+ * most), and so does M <= 64 for 256 x 64 tiles at 64 lanes (39 MiB at most)
+ * and M <= 256 up to 14336 x 4096 (42 MiB).  Each call
  * first zeroes the array's counters with a small kernel on `stream`.  All
  * calls on one device share the array: calls that overlap in time on one
  * device (other streams, other threads) race and give wrong results.  Calls
